@@ -1,0 +1,94 @@
+"""Host-side checks of the seeded input generator (no GPU, no oracle arithmetic)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+
+def test_five_configs_shapes():
+    c = W.CONFIG_BY_NAME
+    assert [x.name for x in W.CONFIGS] == ["tiny_f32", "llama3_8b_b64", "llama3_8b_b256",
+                                          "long_split", "prefix_70b"]
+    assert c["tiny_f32"].dtype == "f32" and c["tiny_f32"].scale == 1 / 8
+    for x in W.CONFIGS[1:]:
+        assert x.dtype == "bf16" and x.head_size == 128 and x.num_kv_heads == 8
+    assert c["prefix_70b"].group == 8 and c["llama3_8b_b256"].group == 4
+    assert [x.seed for x in W.CONFIGS] == [0, 1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("cfg", W.CONFIGS, ids=lambda c: c.name)
+def test_context_length_ranges_and_pool_fit(cfg):
+    n = W.draw_context_lens(cfg)
+    assert n.shape == (cfg.num_seqs,) and n.dtype == np.int32
+    kind = cfg.ctx[0]
+    if kind == "uniform":
+        assert n.min() >= cfg.ctx[1] and n.max() <= cfg.ctx[2]
+    elif kind == "normal":
+        assert n.min() >= cfg.ctx[3] and n.max() <= cfg.ctx[4]
+        assert abs(n.mean() - cfg.ctx[1]) < 4 * cfg.ctx[2] / np.sqrt(cfg.num_seqs)
+    else:
+        assert n.min() >= cfg.ctx[1] + cfg.ctx[2] and n.max() <= cfg.ctx[1] + cfg.ctx[3]
+    nblk = (n + 15) // 16
+    shared = cfg.ctx[1] // 16 if kind == "prefix" else 0
+    assert shared + (nblk - shared).sum() <= cfg.num_blocks
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -1.00390625, 0.0, -0.0, 3e38], np.float32)])
+    ours = W.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_generator_deterministic_and_layout():
+    cfg = W.CONFIG_BY_NAME["tiny_f32"]
+    a = W.make_inputs(cfg)
+    b = W.make_inputs(cfg)
+    for k in ["context_lens", "block_tables", "query", "key_cache", "value_cache", "slot_mapping"]:
+        np.testing.assert_array_equal(getattr(a, k), getattr(b, k))
+    assert a.key_cache.shape == (64, 16, 2, 64) and a.query.shape == (4, 4, 64)
+    S = cfg.num_seqs
+    used = []
+    for i in range(S):
+        n = int(a.context_lens[i])
+        nb = (n + 15) // 16
+        row = a.block_tables[i]
+        assert (row[:nb] >= 0).all() and (row[nb:] == -1).all()
+        used.extend(row[:nb].tolist())
+        # New token = position n-1, through the table.
+        assert a.slot_mapping[i] == row[(n - 1) // 16] * 16 + (n - 1) % 16
+        np.testing.assert_array_equal(a.new_key[i], a.key_cache.reshape(-1, 2, 64)[a.slot_mapping[i]])
+        # Tail slots of the last block are poisoned, valid ones finite.
+        last = row[nb - 1]
+        k = n - (nb - 1) * 16
+        assert np.isfinite(a.key_cache[last, :k]).all()
+        assert np.isnan(a.key_cache[last, k:]).all() and np.isnan(a.value_cache[last, k:]).all()
+    assert len(used) == len(set(used))  # no sharing in this config
+    free = np.setdiff1d(np.arange(64), used)
+    assert np.isnan(a.key_cache[free]).all()
+    perf = W.make_inputs(cfg, mode="perf")
+    np.testing.assert_array_equal(perf.block_tables, a.block_tables)
+    assert (perf.key_cache[free] == 0).all()
+
+
+def test_prefix_sharing_layout_small():
+    cfg = W.PagedConfig(name="p", num_seqs=6, num_heads=8, num_kv_heads=2, head_size=64,
+                        block_size=16, num_blocks=128, dtype="bf16", ctx=("prefix", 64, 5, 40),
+                        seed=3)
+    a = W.make_inputs(cfg)
+    assert a.shared_prefix_blocks == 4
+    assert (a.block_tables[:, :4] == a.block_tables[0, :4]).all()
+    private = [set(a.block_tables[i, 4:(a.context_lens[i] + 15) // 16].tolist()) for i in range(6)]
+    for i in range(6):
+        for j in range(i + 1, 6):
+            assert not (private[i] & private[j])
+    assert W.unique_kv_bytes(a) < W.algorithmic_kv_bytes(cfg, a.context_lens)
+
+
+def test_algorithmic_bytes():
+    cfg = W.CONFIG_BY_NAME["llama3_8b_b256"]
+    n = np.array([1000, 10], np.int32)
+    assert W.algorithmic_kv_bytes(cfg, n) == 1010 * 4096

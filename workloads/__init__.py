@@ -1,0 +1,298 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only draws and lays out inputs: context lengths, block
+placement, query/key/value values, the new-token slot mapping. It holds no
+attention arithmetic, so both the fp64 oracle (``oracle/``) and the HIP path
+(``paged_kv_cache_150_amd``) can consume the same arrays without sharing any
+of the method's computation.
+
+Workload shapes follow the pages' statement of the problem:
+
+* the paged pool is ``[num_blocks, block_size, H_kv, d_h]`` per layer, blocks
+  of 16 tokens handed out from a shuffled free list
+  (llm-stack-book 7.3 "vLLM: Architecture, PagedAttention & Internals",
+  sections "PagedAttention in one paragraph" and "The free list and the block
+  table");
+* the new token of each sequence is written at
+  ``slot = block_table[pos // bs] * bs + pos % bs`` with ``pos = n - 1``
+  (same page, section "The forward step in detail");
+* model heads follow the Llama-3-8B shape, 32 layers x 8 KV heads x 128
+  (modernaiengineering.com lesson 13.15 "vLLM: High-Throughput Serving with
+  PagedAttention", listing "paged_kv.py") and a 70B-like 64-query-head variant
+  sharing one long prefix (same lesson, "How PagedAttention shares memory").
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+
+@dataclass(frozen=True)
+class PagedConfig:
+    """One synthetic decode workload (one layer, one decode step)."""
+
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    num_blocks: int
+    dtype: str  # "f32" or "bf16"
+    ctx: tuple  # ("uniform", lo, hi) | ("normal", mean, std, lo, hi) | ("prefix", prefix_tokens, lo, hi)
+    seed: int
+    partition_size: int = 512
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        # 1/sqrt(d_h), the scale the model contract passes to Attention(...)
+        # (llm-stack-book 7.3, "Serving a model vLLM has never seen").
+        return 1.0 / math.sqrt(self.head_size)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+
+CONFIGS: list[PagedConfig] = [
+    PagedConfig(
+        name="tiny_f32", num_seqs=4, num_heads=4, num_kv_heads=2, head_size=64,
+        block_size=16, num_blocks=64, dtype="f32", ctx=("uniform", 1, 100), seed=0,
+        partition_size=32,
+        description="Tiny fp32: 4 seqs, H_q=4, H_kv=2, d_h=64, ctx U{1..100}, 64-block pool"),
+    PagedConfig(
+        name="llama3_8b_b64", num_seqs=64, num_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, num_blocks=16384, dtype="bf16", ctx=("uniform", 512, 2048), seed=1,
+        partition_size=512,
+        description="Llama-3-8B-shaped decode layer: batch 64, ctx U{512..2048}, 16k-block pool"),
+    PagedConfig(
+        name="llama3_8b_b256", num_seqs=256, num_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, num_blocks=32768, dtype="bf16", ctx=("normal", 1000.0, 200.0, 16, 4096),
+        seed=2, partition_size=512,
+        description="Llama-3-8B-shaped decode: batch 256, ctx N(1000,200) clipped [16,4096], "
+                    "reshape_and_cache of 256 new tokens first"),
+    PagedConfig(
+        name="long_split", num_seqs=8, num_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, num_blocks=32768, dtype="bf16", ctx=("uniform", 16384, 32768), seed=3,
+        partition_size=512,
+        description="Long-context split-K: batch 8, ctx U{16k..32k}, 512-token partitions"),
+    PagedConfig(
+        name="prefix_70b", num_seqs=128, num_heads=64, num_kv_heads=8, head_size=128,
+        block_size=16, num_blocks=16384, dtype="bf16", ctx=("prefix", 1024, 64, 512), seed=4,
+        partition_size=512,
+        description="70B-shaped heads: 128 seqs share one 1024-token prefix + suffix U{64..512}"),
+]
+
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return the bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bits to float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw_context_lens(cfg: PagedConfig, rng: np.random.Generator) -> np.ndarray:
+    kind = cfg.ctx[0]
+    if kind == "uniform":
+        _, lo, hi = cfg.ctx
+        n = rng.integers(lo, hi + 1, size=cfg.num_seqs)
+    elif kind == "normal":
+        _, mean, std, lo, hi = cfg.ctx
+        n = np.clip(np.rint(rng.normal(mean, std, size=cfg.num_seqs)), lo, hi)
+    elif kind == "prefix":
+        _, prefix, lo, hi = cfg.ctx
+        n = prefix + rng.integers(lo, hi + 1, size=cfg.num_seqs)
+    else:
+        raise ValueError(kind)
+    return n.astype(np.int32)
+
+
+def draw_context_lens(cfg: PagedConfig, seed: int | None = None) -> np.ndarray:
+    """The context lengths make_inputs() would draw (its first draw), without the rest."""
+    return _draw_context_lens(cfg, np.random.default_rng(cfg.seed if seed is None else seed))
+
+
+def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def poison_value(dtype: str):
+    return np.float32(np.nan) if dtype == "f32" else BF16_NAN_BITS
+
+
+def storage_dtype(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+@dataclass
+class PagedInputs:
+    """Host arrays for one workload.
+
+    Caches are stored as float32 (``f32``) or as raw bfloat16 bits in uint16
+    (``bf16``). ``key_cache``/``value_cache`` hold the full context, including
+    the new token at position ``n-1``; ``new_key``/``new_value`` are that
+    token's rows and ``slot_mapping`` its flat slot, so the state *before*
+    reshape_and_cache is the pool with those slots overwritten by poison.
+    """
+
+    cfg: PagedConfig
+    context_lens: np.ndarray      # int32 [S]
+    block_tables: np.ndarray      # int32 [S, MB], padded with -1
+    query: np.ndarray             # [S, H_q, d_h]
+    key_cache: np.ndarray         # [NB, bs, H_kv, d_h]
+    value_cache: np.ndarray       # [NB, bs, H_kv, d_h]
+    new_key: np.ndarray           # [S, H_kv, d_h]
+    new_value: np.ndarray         # [S, H_kv, d_h]
+    slot_mapping: np.ndarray      # int64 [S]
+    referenced_blocks: np.ndarray  # int64 [n_ref], physical ids in allocation order
+    shared_prefix_blocks: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+
+def make_inputs(cfg: PagedConfig, mode: str = "parity", seed: int | None = None,
+                context_lens: np.ndarray | None = None) -> PagedInputs:
+    """Draw one workload.
+
+    Draw order from one PCG64 stream: context lengths, block placement (a
+    permutation of the free list handed out in logical order), query, K blocks,
+    V blocks. ``mode="parity"`` fills every slot that no sequence owns (tails of
+    last blocks, unreferenced blocks) with NaN so that a stray read shows up in
+    the output; ``mode="perf"`` leaves unreferenced blocks zero.
+    ``context_lens`` optionally overrides the drawn lengths (same draw order).
+    """
+    if mode not in ("parity", "perf"):
+        raise ValueError(mode)
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    S, bs = cfg.num_seqs, cfg.block_size
+    n = _draw_context_lens(cfg, rng)
+    if context_lens is not None:
+        n = np.asarray(context_lens, dtype=np.int32).copy()
+        S = n.shape[0]
+    nblk = (n.astype(np.int64) + bs - 1) // bs
+
+    prefix_blocks = 0
+    if cfg.ctx[0] == "prefix":
+        prefix_blocks = cfg.ctx[1] // bs
+    private = nblk - prefix_blocks
+    total = int(prefix_blocks + private.sum())
+    if total > cfg.num_blocks:
+        raise ValueError(f"{cfg.name}: needs {total} blocks, pool has {cfg.num_blocks}")
+
+    free = rng.permutation(cfg.num_blocks)
+    mb = int(max(1, nblk.max() if S else 1))
+    tables = np.full((S, mb), -1, dtype=np.int32)
+    cursor = 0
+    shared = free[cursor:cursor + prefix_blocks]
+    cursor += prefix_blocks
+    alloc_order = [shared]
+    for i in range(S):
+        own = free[cursor:cursor + int(private[i])]
+        cursor += int(private[i])
+        tables[i, :prefix_blocks] = shared
+        tables[i, prefix_blocks:nblk[i]] = own
+        alloc_order.append(own)
+    referenced = np.concatenate(alloc_order).astype(np.int64) if alloc_order else np.zeros(0, np.int64)
+
+    Hq, Hkv, d = cfg.num_heads, cfg.num_kv_heads, cfg.head_size
+    query = _values(rng, (S, Hq, d), cfg.dtype)
+
+    sdt = storage_dtype(cfg.dtype)
+    fill = poison_value(cfg.dtype) if mode == "parity" else sdt(0)
+    caches = []
+    for _ in range(2):  # K then V
+        pool = np.empty((cfg.num_blocks, bs, Hkv, d), dtype=sdt)
+        if mode == "parity":
+            pool[...] = fill
+        else:
+            pool[...] = 0
+        pool[referenced] = _values(rng, (referenced.size, bs, Hkv, d), cfg.dtype)
+        caches.append(pool)
+    key_cache, value_cache = caches
+
+    # Slots that no sequence owns (past n_i in its last block) are poisoned in
+    # parity mode. Shared blocks are full by construction, so a tail is only
+    # ever owned by one sequence.
+    if mode == "parity":
+        for i in range(S):
+            if n[i] % bs and nblk[i] > 0:
+                last = tables[i, nblk[i] - 1]
+                key_cache[last, n[i] % bs:] = fill
+                value_cache[last, n[i] % bs:] = fill
+
+    # New token of each sequence sits at position n-1.
+    pos = n.astype(np.int64) - 1
+    slot = np.full(S, -1, dtype=np.int64)
+    for i in range(S):
+        if n[i] > 0:
+            slot[i] = int(tables[i, pos[i] // bs]) * bs + int(pos[i] % bs)
+    flat_k = key_cache.reshape(cfg.num_blocks * bs, Hkv, d)
+    flat_v = value_cache.reshape(cfg.num_blocks * bs, Hkv, d)
+    ok = slot >= 0
+    new_key = np.zeros((S, Hkv, d), dtype=sdt)
+    new_value = np.zeros((S, Hkv, d), dtype=sdt)
+    new_key[ok] = flat_k[slot[ok]]
+    new_value[ok] = flat_v[slot[ok]]
+
+    return PagedInputs(cfg=cfg, context_lens=n, block_tables=tables, query=query,
+                       key_cache=key_cache, value_cache=value_cache, new_key=new_key,
+                       new_value=new_value, slot_mapping=slot, referenced_blocks=referenced,
+                       shared_prefix_blocks=prefix_blocks,
+                       meta={"mode": mode, "seed": cfg.seed if seed is None else seed})
+
+
+def algorithmic_kv_bytes(cfg: PagedConfig, context_lens: np.ndarray) -> int:
+    """K and V bytes one decode call must read: sum_i n_i * 2 * H_kv * d_h * b."""
+    return int(np.asarray(context_lens, dtype=np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_size * cfg.elem_bytes
+
+
+def unique_kv_bytes(inp: PagedInputs) -> int:
+    """K and V bytes of distinct physical slots read (shared prefix blocks counted once)."""
+    cfg = inp.cfg
+    bs = cfg.block_size
+    seen = set()
+    total_tokens = 0
+    for i in range(inp.context_lens.shape[0]):
+        n = int(inp.context_lens[i])
+        for j in range((n + bs - 1) // bs):
+            b = int(inp.block_tables[i, j])
+            used = min(bs, n - j * bs)
+            key = b
+            if key in seen:
+                continue
+            seen.add(key)
+            total_tokens += used
+    return total_tokens * 2 * cfg.num_kv_heads * cfg.head_size * cfg.elem_bytes
+
+
+def small_case(name: str, num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+               dtype: str, ctx: tuple, seed: int, num_blocks: int, partition_size: int = 64) -> PagedConfig:
+    """A small ad-hoc config for parity sweeps (same generator, different shape)."""
+    return PagedConfig(name=name, num_seqs=num_seqs, num_heads=num_heads,
+                       num_kv_heads=num_kv_heads, head_size=head_size, block_size=16,
+                       num_blocks=num_blocks, dtype=dtype, ctx=ctx, seed=seed,
+                       partition_size=partition_size, description="ad-hoc parity case")
