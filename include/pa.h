@@ -1,0 +1,189 @@
+/*
+ * pa.h - C ABI of libpa.so: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * The library holds the data-plane half of PagedAttention as the pages describe
+ * it: a per-layer KV pool carved into fixed-size blocks, a block table per
+ * sequence mapping logical blocks to physical ones, a slot mapping telling
+ * where each new token's K/V is written, and a decode kernel that follows the
+ * block table (llm-stack-book 7.3 "vLLM: Architecture, PagedAttention &
+ * Internals", sections "PagedAttention in one paragraph" and "The forward step
+ * in detail"; stanleyjacob.dev "vLLM", Part V "The attention backend dispatch
+ * layer": a backend runs attention given the query, the paged KV pool and the
+ * block tables).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers, row-major and contiguous, owned
+ *    by the caller. The library never allocates, frees or synchronises; every
+ *    launch goes on the caller's `stream` (a hipStream_t passed as void*, NULL
+ *    for the default stream) and returns immediately. Work on one stream is
+ *    ordered, so reshape_and_cache followed by a decode on the same stream sees
+ *    the new token.
+ *  - Base pointers of tensors must be 16-byte aligned.
+ *  - Element type (`dtype`): PA_DTYPE_F32 (IEEE float32) or PA_DTYPE_BF16
+ *    (bfloat16 stored as 16-bit words). Query, caches, new K/V and `out` share
+ *    it; accumulation is always float32.
+ *  - Layouts:
+ *        query, out        [num_seqs, num_heads, head_size]
+ *        key_cache,
+ *        value_cache       [num_blocks, block_size, num_kv_heads, head_size]
+ *        block_tables      int32 [num_seqs, max_blocks_per_seq]
+ *        context_lens      int32 [num_seqs]   (tokens stored, including the
+ *                                              token written this step)
+ *        key, value        [num_tokens, num_kv_heads, head_size]
+ *        slot_mapping      int64 [num_tokens]
+ *  - Supported shapes: block_size == 16; head_size in {64, 128};
+ *    num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16.
+ *  - Host-side checks (shapes, enums, null or misaligned pointers, workspace
+ *    size) return a non-zero pa_status before any GPU work is queued. Device
+ *    CONTENTS are the caller's contract: block ids in [0, num_blocks),
+ *    context_lens[i] <= max_blocks_per_seq * block_size, distinct slots. The
+ *    kernels clamp out-of-range block ids and lengths, and skip out-of-range
+ *    slots, so bad contents give unspecified numbers, never an out-of-bounds
+ *    access.
+ *  - Query head h reads kv head h / (num_heads / num_kv_heads) (contiguous GQA
+ *    groups).
+ *  - No entry point uses atomics; results are bit-identical run to run and do
+ *    not depend on where the physical blocks sit in the pool.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, negative size, bad enum   */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (block_size, head_size)   */
+  PA_ERR_WORKSPACE = 3,    /* workspace smaller than pa_decode_split_workspace_bytes */
+  PA_ERR_HIP = 4           /* the HIP runtime refused a launch                     */
+} pa_status;
+
+/*
+ * pa_reshape_and_cache - write each new token's K and V into its cache slot.
+ *
+ * The freshly computed K and V of every token are scattered into the paged
+ * pool at slot_mapping (llm-stack-book 7.3, "The forward step in detail"),
+ * where a slot is physical_block * block_size + offset.
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_size], read.
+ *   key_cache,
+ *   value_cache       [num_blocks, block_size, num_kv_heads, head_size], written
+ *                     at rows slot_mapping[t] only; every other row is untouched.
+ *   slot_mapping      int64 [num_tokens]. slot < 0 marks a padding token and is
+ *                     skipped; slot >= num_blocks*block_size is skipped too.
+ *                     Two tokens with the same slot is a caller error.
+ *   num_tokens        may be 0 (nothing is launched).
+ *
+ * The copy is bitwise: no conversion, no rounding.
+ * Returns PA_OK or an error status (see conventions).
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                         int32_t dtype, void* stream);
+
+/*
+ * pa_decode - one decode step of paged attention, one pass over each context.
+ *
+ * For every sequence i and query head h, with n = context_lens[i] and
+ * kvh = h / (num_heads / num_kv_heads):
+ *     K_t = key_cache[block_tables[i][t / block_size]][t % block_size][kvh]
+ *     s_t = scale * <query[i][h], K_t>            for t in [0, n)
+ *     out[i][h] = sum_t softmax(s)_t * V_t
+ * The arithmetic is ordinary attention; only the addressing goes through the
+ * block table (llm-stack-book 7.3, "PagedAttention in one paragraph"). The
+ * softmax is evaluated online over the streamed blocks (stanleyjacob.dev
+ * "vLLM", Part IV "Stage 6: The forward pass").
+ *
+ *   out               [num_seqs, num_heads, head_size], written (dtype).
+ *   lse_out           optional float32 [num_seqs, num_heads]: ln sum_t exp(s_t).
+ *                     NULL to skip.
+ *   n = 0             gives out = 0 and lse = -inf.
+ *   Table entries at index >= ceil(n / block_size) are never read.
+ * Returns PA_OK or an error status.
+ */
+int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+              int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
+              float scale, int32_t dtype, float* lse_out, void* stream);
+
+/*
+ * pa_decode_split_workspace_bytes - workspace pa_decode_split needs.
+ *
+ * num_parts = ceil(max_context_len / partition_size); the workspace holds
+ * float32 partials o_p [num_seqs, num_heads, num_parts, head_size] followed (at
+ * a 256-byte aligned offset) by float32 lse_p [num_seqs, num_heads, num_parts].
+ * Returns 0 for invalid arguments.
+ */
+size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode_split - the same result as pa_decode, computed over context
+ * partitions and merged exactly.
+ *
+ * Partition p covers positions [p*P, min((p+1)*P, n)), P = partition_size.
+ * A first kernel writes each partition's normalised output o_p and its
+ * log-sum-exp lse_p into `workspace` (empty partitions: lse_p = -inf); then
+ * pa_merge_partitions' kernel combines them on the same stream. The merge
+ * follows from the softmax normaliser identity the pages lean on for
+ * streaming (stanleyjacob.dev "vLLM", Part V "The attention backend dispatch
+ * layer": tiling plus online softmax); the partitioned form itself is this
+ * library's reading.
+ *
+ *   max_context_len   host-side upper bound of context_lens (sizes the grid
+ *                     without reading the lengths back). Positions past
+ *                     num_parts*P are ignored, so it must be >= every length.
+ *   partition_size    multiple of block_size, > 0.
+ *   workspace         device memory of at least
+ *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
+ *                     aligned, owned by the caller; overwritten.
+ *   lse_out           optional float32 [num_seqs, num_heads]; NULL to skip.
+ * Other arguments as pa_decode. Returns PA_OK or an error status.
+ */
+int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                    int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    float* lse_out, void* stream);
+
+/*
+ * pa_merge_partitions - exact log-sum-exp merge of partial attention results.
+ *
+ * For each (sequence, head): M = max_p lse_p, w_p = exp(lse_p - M),
+ *     out = sum_p w_p o_p / sum_p w_p,   lse = M + ln sum_p w_p.
+ * Partitions with lse_p = -inf carry no weight and their o_p is never used
+ * (it may hold anything). If all are -inf: out = 0, lse = -inf.
+ *
+ *   o_parts           float32 [num_seqs, num_heads, num_parts, head_size]
+ *   lse_parts         float32 [num_seqs, num_heads, num_parts]
+ *   out               [num_seqs, num_heads, head_size] in dtype, written.
+ *   lse_out           optional float32 [num_seqs, num_heads]; NULL to skip.
+ * Returns PA_OK or an error status.
+ */
+int pa_merge_partitions(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_parts,
+                        int32_t head_size, int32_t dtype, void* stream);
+
+/* pa_status_string - static, NUL-terminated description of a status code. */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,227 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Thin Python binding over ``libpa.so`` (declared in ``include/pa.h``). Each
+function has the name of the C entry point it calls and only marshals
+arguments: it checks that tensors live on the GPU, are contiguous and agree in
+shape (the C side receives raw pointers and cannot), then passes device
+pointers and the current HIP stream. Every step of the computation runs in the
+library's HIP kernels; there is no fallback. If ``libpa.so`` has not been built
+the first call raises.
+
+PyTorch is used only for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library",
+    "pa_reshape_and_cache", "pa_decode", "pa_decode_split_workspace_bytes", "pa_decode_split",
+    "pa_merge_partitions", "pa_status_string",
+]
+
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+BLOCK_SIZE = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pa_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpa.so")
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_150_amd.build` "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    c_int, c_i32, c_i64, c_f, c_p, c_sz = (ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                          ctypes.c_void_p, ctypes.c_size_t)
+    lib.pa_reshape_and_cache.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
+    lib.pa_reshape_and_cache.restype = c_int
+    lib.pa_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
+                              c_f, c_i32, c_p, c_p]
+    lib.pa_decode.restype = c_int
+    lib.pa_decode_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
+    lib.pa_decode_split_workspace_bytes.restype = c_sz
+    lib.pa_decode_split.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                    c_i32, c_f, c_i32, c_i32, c_i32, c_p, c_sz, c_p, c_p]
+    lib.pa_decode_split.restype = c_int
+    lib.pa_merge_partitions.argtypes = [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p]
+    lib.pa_merge_partitions.restype = c_int
+    lib.pa_status_string.argtypes = [c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PaError(status, where)
+
+
+def _cache_dims(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("key_cache and value_cache must have the same shape and dtype")
+    if key_cache.dim() != 4:
+        raise ValueError("caches must be [num_blocks, block_size, num_kv_heads, head_size]")
+    return tuple(int(x) for x in key_cache.shape)
+
+
+# ------------------------------------------------------------------ entry points
+def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write key[t], value[t] into cache slot slot_mapping[t] (negative slot: skipped)."""
+    NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (Hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_size] matching the cache")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise TypeError("key/value dtype must match the cache dtype")
+    T = int(key.shape[0])
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    lib = load_library()
+    st = lib.pa_reshape_and_cache(_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+                                  _dev(value_cache, "value_cache"),
+                                  _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d,
+                                  _dtype_code(key_cache), _stream(stream))
+    _check(st, "pa_reshape_and_cache")
+
+
+def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens, lse_out):
+    NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
+    if query.dim() != 3 or int(query.shape[2]) != d:
+        raise ValueError("query must be [num_seqs, num_heads, head_size]")
+    S, Hq = int(query.shape[0]), int(query.shape[1])
+    if out.shape != query.shape or out.dtype != query.dtype or query.dtype != key_cache.dtype:
+        raise ValueError("out must match query's shape; query, out and caches share one dtype")
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if context_lens.shape != (S,):
+        raise ValueError("context_lens must be [num_seqs]")
+    lse_ptr = None
+    if lse_out is not None:
+        if lse_out.shape != (S, Hq):
+            raise ValueError("lse_out must be [num_seqs, num_heads]")
+        lse_ptr = _dev(lse_out, "lse_out", torch.float32)
+    ptrs = dict(out=_dev(out, "out"), query=_dev(query, "query"), kc=_dev(key_cache, "key_cache"),
+                vc=_dev(value_cache, "value_cache"),
+                bt=_dev(block_tables, "block_tables", torch.int32, 2),
+                cl=_dev(context_lens, "context_lens", torch.int32, 1), lse=lse_ptr)
+    return ptrs, (S, Hq, Hkv, d, NB, bs, int(block_tables.shape[1]))
+
+
+def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+              lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """One-pass paged decode attention into ``out`` (optionally ln-sum-exp into ``lse_out``)."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out)
+    lib = load_library()
+    st = lib.pa_decode(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
+                       float(scale), _dtype_code(query), p["lse"], _stream(stream))
+    _check(st, "pa_decode")
+
+
+def pa_decode_split_workspace_bytes(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,
+                                    partition_size: int) -> int:
+    return int(load_library().pa_decode_split_workspace_bytes(num_seqs, num_heads, head_size,
+                                                              max_context_len, partition_size))
+
+
+def pa_decode_split(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                    value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                    scale: float, max_context_len: int, partition_size: int, workspace: torch.Tensor,
+                    lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """Partitioned paged decode + log-sum-exp merge; ``workspace`` is a uint8 GPU tensor."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out)
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    st = lib.pa_decode_split(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
+                             float(scale), _dtype_code(query), int(max_context_len), int(partition_size), ws,
+                             nbytes, p["lse"], _stream(stream))
+    _check(st, "pa_decode_split")
+
+
+def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head_size: int,
+                    max_context_len: int, partition_size: int):
+    """(o_parts, lse_parts) float32 views into a pa_decode_split workspace."""
+    num_parts = max(1, -(-max_context_len // partition_size))
+    rows = num_seqs * num_heads * num_parts
+    o_bytes = (rows * head_size * 4 + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    o_parts = f[:rows * head_size * 4].view(torch.float32).view(num_seqs, num_heads, num_parts, head_size)
+    lse_parts = f[o_bytes:o_bytes + rows * 4].view(torch.float32).view(num_seqs, num_heads, num_parts)
+    return o_parts, lse_parts
+
+
+def pa_merge_partitions(out: torch.Tensor, o_parts: torch.Tensor, lse_parts: torch.Tensor,
+                        lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """Log-sum-exp merge of float32 partials [S, H, P, d] / [S, H, P] into ``out`` [S, H, d]."""
+    if o_parts.dim() != 4 or lse_parts.shape != o_parts.shape[:3]:
+        raise ValueError("o_parts must be [S, H, P, d] and lse_parts [S, H, P]")
+    S, H, P, d = (int(x) for x in o_parts.shape)
+    if out.shape != (S, H, d):
+        raise ValueError("out must be [S, H, d]")
+    lse_ptr = None
+    if lse_out is not None:
+        if lse_out.shape != (S, H):
+            raise ValueError("lse_out must be [S, H]")
+        lse_ptr = _dev(lse_out, "lse_out", torch.float32)
+    lib = load_library()
+    st = lib.pa_merge_partitions(_dev(out, "out"), lse_ptr, _dev(o_parts, "o_parts", torch.float32),
+                                 _dev(lse_parts, "lse_parts", torch.float32), S, H, P, d, _dtype_code(out),
+                                 _stream(stream))
+    _check(st, "pa_merge_partitions")

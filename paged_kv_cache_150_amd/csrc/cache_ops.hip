@@ -1,0 +1,79 @@
+// pa_reshape_and_cache for gfx950: scatter new K/V rows into their cache slots.
+//
+// Each token's K and V row ([H_kv, d_h], contiguous) is copied to row `slot` of
+// the flattened pool [num_blocks * block_size, H_kv, d_h], where the slot is
+// physical_block * block_size + offset (llm-stack-book 7.3 "vLLM: Architecture,
+// PagedAttention & Internals", section "The forward step in detail"). One
+// thread moves one 16-byte piece of K and the matching piece of V, so a wave
+// copies 1 KiB of each with fully coalesced loads and stores. The copy is
+// bitwise.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_device.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(const u32x4_t* __restrict__ key,
+                                                                const u32x4_t* __restrict__ value,
+                                                                u32x4_t* __restrict__ key_cache,
+                                                                u32x4_t* __restrict__ value_cache,
+                                                                const int64_t* __restrict__ slot_mapping,
+                                                                int64_t num_tokens, int64_t num_slots,
+                                                                int row_pieces) {
+  const int64_t total = num_tokens * row_pieces;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t t = i / row_pieces;
+    const int64_t piece = i - t * row_pieces;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;  // padding token, or a slot outside the pool
+    key_cache[slot * row_pieces + piece] = key[i];
+    value_cache[slot * row_pieces + piece] = value[i];
+  }
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                                    const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                    int32_t block_size, int32_t num_kv_heads, int32_t head_size, int32_t dtype,
+                                    void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
+                        reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache);
+  if (mis & 15u) return PA_ERR_INVALID_ARG;
+  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_size * (dtype == PA_DTYPE_F32 ? 4 : 2);
+  const int64_t row_pieces = row_bytes / 16;  // head_size in {64,128} makes rows whole 16-byte pieces
+  if (row_pieces > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int64_t total = num_tokens * row_pieces;
+  constexpr int kThreads = 256;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;  // grid-stride loop covers the rest
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4_t*>(key),
+                     static_cast<const u32x4_t*>(value), static_cast<u32x4_t*>(key_cache),
+                     static_cast<u32x4_t*>(value_cache), slot_mapping, num_tokens,
+                     num_blocks * kBlockTokens, static_cast<int>(row_pieces));
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or dtype)";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape (block_size must be 16, head_size 64 or 128, "
+                                    "num_heads/num_kv_heads at most 16)";
+    case PA_ERR_WORKSPACE: return "workspace smaller than pa_decode_split_workspace_bytes()";
+    case PA_ERR_HIP: return "HIP runtime refused the launch";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,82 @@
+// Device-side helpers shared by the paged-attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace pa {
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;  // MFMA bf16 operand
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+constexpr int kWave = 64;
+constexpr int kBlockTokens = 16;  // tokens per KV block; also the MFMA M dimension
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// Lane H of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(H >= 0 && H < 16, "row lane");
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + H, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(T* p, float x);
+template <>
+__device__ __forceinline__ void store_elem<float>(float* p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+
+// Load `NDW` dwords (8, 16 or 32 bytes) that are 16-byte (or 8-byte) aligned.
+template <int NDW>
+__device__ __forceinline__ void load_dwords(uint32_t (&dst)[NDW], const void* src) {
+  if constexpr (NDW == 2) {
+    u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
+    dst[0] = v[0];
+    dst[1] = v[1];
+  } else {
+    static_assert(NDW % 4 == 0, "16-byte granules");
+#pragma unroll
+    for (int i = 0; i < NDW / 4; ++i) {
+      u32x4_t v = reinterpret_cast<const u32x4_t*>(src)[i];
+      dst[4 * i + 0] = v[0];
+      dst[4 * i + 1] = v[1];
+      dst[4 * i + 2] = v[2];
+      dst[4 * i + 3] = v[3];
+    }
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,620 @@
+// Paged decode attention for gfx950: pa_decode, pa_decode_split, pa_merge_partitions.
+//
+// What is computed (llm-stack-book 7.3 "vLLM: Architecture, PagedAttention &
+// Internals", sections "PagedAttention in one paragraph" and "The forward step
+// in detail"): for each sequence and query head, ordinary attention of the one
+// new query over the sequence's whole context, with K/V rows found through the
+// block table instead of in one contiguous tensor. The softmax runs online over
+// streamed blocks (stanleyjacob.dev "vLLM", Part IV "Stage 6: The forward
+// pass"); a context split into partitions is recombined exactly with
+// log-sum-exp weights.
+//
+// Work decomposition (one workgroup per (sequence, kv head, context
+// partition), W waves per workgroup):
+//  * A wave handles "chunks" of CB consecutive 16-token blocks; chunk c goes to
+//    wave c % W. All g = H_q/H_kv query heads of the kv head share every K/V
+//    tile the wave loads.
+//  * Scores: one 16x16 MFMA tile per block, A = K rows (M = the block's 16
+//    tokens), B = the group's query rows (N = up to 16 heads), contracted over
+//    head_size. Each lane loads its K operand straight from HBM: token
+//    (lane % 16), 16-byte pieces at byte offset s*64 + (lane/16)*16 of the row,
+//    so every load instruction reads one aligned 64-byte segment of each of the
+//    16 rows of the tile. The query fragment uses the same d ordering.
+//  * The MFMA result leaves lane l with the scores of tokens 4*(l/16)+r,
+//    r = 0..3, for head l % 16. The V load uses exactly those tokens: lane l
+//    reads head_size/16 contiguous elements (d = (l%16)*head_size/16 ...) of
+//    the 4 rows, so each load instruction covers 4 whole rows, and the
+//    probabilities a lane needs come from its own 16-lane row by DPP broadcast.
+//  * P*V runs on the VALU in fp32 (the V tile would need a transpose for MFMA).
+//  * Online softmax per chunk with base-2 exponentials (scale*log2(e) folded
+//    into the scores); the chunk maximum is reduced across the 4 row groups.
+//  * At the end each wave reduces its partial sums across row groups and the W
+//    waves merge through LDS with log-sum-exp weights.
+// Reduction order depends only on logical token positions, W and CB, never on
+// physical block ids, so results do not change when blocks move or are shared.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "pa.h"
+#include "pa_device.h"
+
+namespace pa {
+
+template <typename T, int D, int G, int CB>
+struct DecodeShape {
+  static constexpr int kElemBytes = static_cast<int>(sizeof(T));
+  static constexpr int kKSeg = D * kElemBytes / 64;  // 16-byte K loads per lane per block
+  static constexpr int kVec = D / 16;                // V elements per lane per token
+  static constexpr int kVDw = kVec * kElemBytes / 4; // ... as dwords
+  static_assert(kKSeg >= 1 && kVDw >= 2, "shape");
+  static_assert(G >= 1 && G <= 16, "group");
+};
+
+template <typename T, int D, int G, int CB>
+struct Chunk {
+  using S = DecodeShape<T, D, G, CB>;
+  u32x4_t k[CB][S::kKSeg];
+  uint32_t v[CB][4][S::kVDw];
+};
+
+struct DecodeArgs {
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;           // final output (num_parts == 1)
+  float* lse_out;      // optional, final lse (num_parts == 1)
+  float* o_parts;      // partials (num_parts > 1)
+  float* lse_parts;    // partials (num_parts > 1)
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // H_q / H_kv
+  int32_t part_tokens;  // tokens per partition (multiple of 16)
+  int32_t num_parts;
+  float scale_log2;     // scale * log2(e)
+};
+
+template <typename T, int D, int G, int CB>
+__device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB>& f, const char* kc, const char* vc,
+                                           const int32_t* bt_row, int blk0, int blk_last,
+                                           int64_t num_blocks, int64_t tok_stride_bytes,
+                                           int64_t blk_stride_bytes, int64_t head_off_bytes,
+                                           int lane) {
+  using S = DecodeShape<T, D, G, CB>;
+  const int tok = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int b = min(blk0 + i, blk_last);
+    // Out-of-range ids (negative included) are clamped so a bad table never
+    // leads to an out-of-bounds access.
+    uint64_t phys = static_cast<uint32_t>(bt_row[b]);
+    phys = phys < static_cast<uint64_t>(num_blocks) ? phys : static_cast<uint64_t>(num_blocks - 1);
+    const int64_t base = static_cast<int64_t>(phys) * blk_stride_bytes + head_off_bytes;
+    const char* krow = kc + base + tok * tok_stride_bytes + j * 16;
+#pragma unroll
+    for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = *reinterpret_cast<const u32x4_t*>(krow + s * 64);
+    const char* vrow = vc + base + (4 * j) * tok_stride_bytes + tok * (S::kVDw * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_dwords<S::kVDw>(f.v[i][r], vrow + r * tok_stride_bytes);
+  }
+}
+
+template <typename T, int D, int G, int CB>
+struct WaveState {
+  using S = DecodeShape<T, D, G, CB>;
+  float m;                  // running max (base-2 scaled) for head lane%16
+  float l;                  // partial sum of weights, this lane's tokens
+  float acc[G][S::kVec];    // partial P*V, this lane's tokens and d range
+};
+
+template <typename T, int D, int G, int CB>
+__device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB>& f,
+                                              const u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg],
+                                              float scale_log2, int tok0, int t_end, bool mask,
+                                              int lane) {
+  using S = DecodeShape<T, D, G, CB>;
+  const int rg = lane >> 4;
+  float s[CB][4];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sg = 0; sg < S::kKSeg; ++sg) {
+      if constexpr (sizeof(T) == 2) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[i][sg]),
+                                                    __builtin_bit_cast(bf16x8_t, q[sg]), c, 0, 0, 0);
+      } else {
+        // Vector elements are read into scalars first: bit-casting a vector
+        // element in place is not reliable.
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(as_float(f.k[i][sg][e]), as_float(q[sg][e]), c, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[i][r] = c[r] * scale_log2;
+  }
+  // The chunk that straddles the end of the context: positions >= t_end get
+  // weight exactly 0 and their V rows (stale or poisoned) are replaced by 0.
+  uint32_t vz[CB][4][S::kVDw];
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int w = 0; w < S::kVDw; ++w) vz[i][r][w] = f.v[i][r][w];
+  if (mask) {
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = tok0 + i * 16 + 4 * rg + r < t_end;
+        s[i][r] = valid ? s[i][r] : -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < S::kVDw; ++w) vz[i][r][w] = valid ? vz[i][r][w] : 0u;
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[i][r]);
+  mx = fmaxf(mx, xor_shfl(mx, 16));
+  mx = fmaxf(mx, xor_shfl(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fast_exp2(st.m - m_new);
+  st.m = m_new;
+  float p[CB][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[i][r] = fast_exp2(s[i][r] - m_new);
+      psum += p[i][r];
+    }
+  st.l = st.l * alpha + psum;
+
+  static_for<G>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const float a = row_bcast<h>(alpha);
+#pragma unroll
+    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] *= a;
+  });
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float vf[S::kVec];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int w = 0; w < S::kVDw; ++w) {
+          vf[2 * w] = bf16_lo(vz[i][r][w]);
+          vf[2 * w + 1] = bf16_hi(vz[i][r][w]);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < S::kVDw; ++w) vf[w] = as_float(vz[i][r][w]);
+      }
+      const float pr = p[i][r];
+      static_for<G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float ph = row_bcast<h>(pr);
+#pragma unroll
+        for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = fmaf(ph, vf[e], st.acc[h][e]);
+      });
+    }
+}
+
+template <typename T, int D, int G, int CB, bool PF>
+__global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
+  using S = DecodeShape<T, D, G, CB>;
+  extern __shared__ float s_acc[];  // [W][G][D]
+  __shared__ float s_m[8][16];
+  __shared__ float s_l[8][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+
+  // kv head fastest: with 8 kv heads and 8 XCDs every XCD sees one kv head,
+  // so blocks shared between sequences stay in that XCD's L2.
+  const int id = blockIdx.x;
+  const int kvh = id % a.num_kv_heads;
+  const int rest = id / a.num_kv_heads;
+  const int part = rest % a.num_parts;
+  const int seq = rest / a.num_parts;
+
+  const int max_tokens = a.max_blocks * kBlockTokens;
+  int n = a.context_lens[seq];
+  n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+  const int t_begin = part * a.part_tokens;
+  const int t_end = min(n, t_begin + a.part_tokens);
+  const int g = a.group;
+  const int head0 = kvh * g;
+
+  const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * D * S::kElemBytes;
+  const int64_t blk_stride = tok_stride * kBlockTokens;
+  const int64_t head_off = static_cast<int64_t>(kvh) * D * S::kElemBytes;
+  const char* kc = static_cast<const char*>(a.key_cache);
+  const char* vc = static_cast<const char*>(a.value_cache);
+  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
+
+  WaveState<T, D, G, CB> st;
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
+
+  if (t_begin < t_end) {
+    // Query fragment (MFMA B operand): head lane%16 of the group, same d order as K.
+    u32x4_t q[S::kKSeg];
+    {
+      const int hq = lane & 15;
+      const int j = lane >> 4;
+      const char* qrow = static_cast<const char*>(a.query) +
+                         (static_cast<int64_t>(seq) * a.num_heads + head0 + (hq < g ? hq : 0)) * D *
+                             S::kElemBytes +
+                         j * 16;
+#pragma unroll
+      for (int sg = 0; sg < S::kKSeg; ++sg) {
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + sg * 64);
+        q[sg] = hq < g ? v : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    const int blk_begin = t_begin / kBlockTokens;
+    const int blk_end = (t_end + kBlockTokens - 1) / kBlockTokens;
+    const int blk_last = blk_end - 1;
+    const int nchunk = (blk_end - blk_begin + CB - 1) / CB;
+    // Only the final chunk can reach past t_end.
+    const int mask_chunk = ((blk_begin + nchunk * CB) * kBlockTokens > t_end) ? nchunk - 1 : -1;
+
+    Chunk<T, D, G, CB> fa;
+    int c = wave;
+    if constexpr (PF) {
+      // One chunk of lookahead: the next chunk's loads are in flight while
+      // this one is computed.
+      Chunk<T, D, G, CB> fb;
+      if (c < nchunk)
+        load_chunk<T, D, G, CB>(fa, kc, vc, bt_row, blk_begin + c * CB, blk_last, a.num_blocks,
+                                tok_stride, blk_stride, head_off, lane);
+      while (c < nchunk) {
+        int cn = c + nwaves;
+        if (cn < nchunk)
+          load_chunk<T, D, G, CB>(fb, kc, vc, bt_row, blk_begin + cn * CB, blk_last, a.num_blocks,
+                                  tok_stride, blk_stride, head_off, lane);
+        compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, (blk_begin + c * CB) * kBlockTokens, t_end,
+                                   c == mask_chunk, lane);
+        if (cn >= nchunk) break;
+        c = cn;
+        cn = c + nwaves;
+        if (cn < nchunk)
+          load_chunk<T, D, G, CB>(fa, kc, vc, bt_row, blk_begin + cn * CB, blk_last, a.num_blocks,
+                                  tok_stride, blk_stride, head_off, lane);
+        compute_chunk<T, D, G, CB>(st, fb, q, a.scale_log2, (blk_begin + c * CB) * kBlockTokens, t_end,
+                                   c == mask_chunk, lane);
+        c = cn;
+      }
+    } else {
+      for (; c < nchunk; c += nwaves) {
+        load_chunk<T, D, G, CB>(fa, kc, vc, bt_row, blk_begin + c * CB, blk_last, a.num_blocks,
+                                tok_stride, blk_stride, head_off, lane);
+        compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, (blk_begin + c * CB) * kBlockTokens, t_end,
+                                   c == mask_chunk, lane);
+      }
+    }
+  }
+
+  // Sum this wave's partials over the 4 row groups (lanes l, l^16, l^32, l^48).
+  st.l += xor_shfl(st.l, 16);
+  st.l += xor_shfl(st.l, 32);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < S::kVec; ++e) {
+      float x = st.acc[h][e];
+      x += xor_shfl(x, 16);
+      x += xor_shfl(x, 32);
+      st.acc[h][e] = x;
+    }
+  if (lane < 16) {
+    s_m[wave][lane] = st.m;
+    s_l[wave][lane] = st.l;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < S::kVec; ++e) s_acc[(wave * G + h) * D + lane * S::kVec + e] = st.acc[h][e];
+  }
+  __syncthreads();
+
+  // Merge the waves: weights 2^(m_w - M).
+  for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = -__builtin_inff();
+    for (int w = 0; w < nwaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float o = 0.f, L = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int w = 0; w < nwaves; ++w) {
+        const float wt = fast_exp2(s_m[w][h] - M);
+        L = fmaf(wt, s_l[w][h], L);
+        o = fmaf(wt, s_acc[(w * G + h) * D + d], o);
+      }
+      o = o / L;
+    }
+    const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
+    const int64_t row = static_cast<int64_t>(seq) * a.num_heads + head0 + h;
+    if (a.num_parts == 1) {
+      store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
+      if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
+    } else {
+      const int64_t prow = row * a.num_parts + part;
+      a.o_parts[prow * D + d] = o;
+      if (d == 0) a.lse_parts[prow] = lse;
+    }
+  }
+}
+
+// One wave per (sequence, head) row: out = sum_p w_p o_p / sum_p w_p with
+// w_p = exp(lse_p - max lse); partitions at -inf are skipped outright.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_partitions_kernel(T* __restrict__ out, float* __restrict__ lse_out,
+                                                               const float* __restrict__ o_parts,
+                                                               const float* __restrict__ lse_parts,
+                                                               int64_t num_rows, int num_parts) {
+  constexpr int kPer = D / kWave;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= num_rows) return;
+  const float* lp = lse_parts + row * num_parts;
+  float M = -__builtin_inff();
+  for (int p = lane; p < num_parts; p += kWave) M = fmaxf(M, lp[p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != -__builtin_inff()) {
+    const float* op = o_parts + row * num_parts * D + lane * kPer;
+    for (int p = 0; p < num_parts; ++p) {
+      const float lv = lp[p];
+      if (lv == -__builtin_inff()) continue;
+      const float w = fast_exp2((lv - M) * kLog2e);
+      L += w;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, op[p * D + e], acc[e]);
+    }
+  }
+  const bool empty = (M == -__builtin_inff());
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_elem<T>(out + row * D + lane * kPer + e, empty ? 0.f : acc[e] / L);
+  if (lse_out != nullptr && lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + fast_log2(L) * kLn2;
+}
+
+// ------------------------------------------------------------------ host side
+namespace {
+
+// Blocks per chunk (CB) and one-chunk register lookahead (PF), chosen per
+// shape so a wave fits in 256 VGPRs without spilling (2 waves per SIMD).
+template <typename T, int D, int G>
+struct Policy {
+  static constexpr int kRegsPerBlock = D * static_cast<int>(sizeof(T)) / 8;  // K + V dwords per lane
+  static constexpr int kAcc = G * D / 16;
+  static constexpr int CB = (kRegsPerBlock <= 32 && G <= 4) ? 2 : 1;
+  static constexpr bool PF = 2 * CB * kRegsPerBlock + kAcc <= 160;
+};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int next_pow2_group(int g) {
+  int G = 1;
+  while (G < g) G <<= 1;
+  return G;
+}
+
+int waves_per_group() {
+  static int w = [] {
+    const char* e = getenv("PA_DECODE_WAVES");
+    int v = e ? atoi(e) : 4;
+    return (v == 1 || v == 2 || v == 4) ? v : 4;
+  }();
+  return w;
+}
+
+typedef void (*DecodeKernel)(DecodeArgs);
+
+template <typename T, int D, int G>
+DecodeKernel kernel_for() {
+  using P = Policy<T, D, G>;
+  return paged_decode_kernel<T, D, G, P::CB, P::PF>;
+}
+
+template <typename T, int D>
+DecodeKernel pick_group(int G) {
+  switch (G) {
+    case 1: return kernel_for<T, D, 1>();
+    case 2: return kernel_for<T, D, 2>();
+    case 4: return kernel_for<T, D, 4>();
+    case 8: return kernel_for<T, D, 8>();
+    case 16: return kernel_for<T, D, 16>();
+    default: return nullptr;
+  }
+}
+
+DecodeKernel pick_decode(int dtype, int D, int G) {
+  if (dtype == PA_DTYPE_BF16) return D == 128 ? pick_group<bf16_t, 128>(G) : pick_group<bf16_t, 64>(G);
+  return D == 128 ? pick_group<float, 128>(G) : pick_group<float, 64>(G);
+}
+
+int check_common(const void* out, const void* query, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                 int64_t num_blocks, int32_t block_size, int32_t dtype) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+int launch_decode(const DecodeArgs& args, int num_seqs, int dtype, int head_size, hipStream_t stream) {
+  const int G = next_pow2_group(args.group);
+  DecodeKernel k = pick_decode(dtype, head_size, G);
+  if (!k) return PA_ERR_UNSUPPORTED;
+  const int64_t grid = static_cast<int64_t>(num_seqs) * args.num_kv_heads * args.num_parts;
+  if (grid <= 0) return PA_OK;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int W = waves_per_group();
+  const size_t lds = static_cast<size_t>(W) * G * head_size * sizeof(float);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), lds, stream, args);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int launch_merge(void* out, float* lse_out, const float* o_parts, const float* lse_parts, int64_t rows,
+                 int num_parts, int head_size, int dtype, hipStream_t stream) {
+  if (rows <= 0) return PA_OK;
+  constexpr int kRowsPerBlock = 4;
+  const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
+  if (dtype == PA_DTYPE_BF16) {
+    if (head_size == 128)
+      hipLaunchKernelGGL((merge_partitions_kernel<bf16_t, 128>), g, b, 0, stream, static_cast<bf16_t*>(out),
+                         lse_out, o_parts, lse_parts, rows, num_parts);
+    else
+      hipLaunchKernelGGL((merge_partitions_kernel<bf16_t, 64>), g, b, 0, stream, static_cast<bf16_t*>(out),
+                         lse_out, o_parts, lse_parts, rows, num_parts);
+  } else {
+    if (head_size == 128)
+      hipLaunchKernelGGL((merge_partitions_kernel<float, 128>), g, b, 0, stream, static_cast<float*>(out),
+                         lse_out, o_parts, lse_parts, rows, num_parts);
+    else
+      hipLaunchKernelGGL((merge_partitions_kernel<float, 64>), g, b, 0, stream, static_cast<float*>(out),
+                         lse_out, o_parts, lse_parts, rows, num_parts);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int64_t split_parts(int32_t max_context_len, int32_t partition_size) {
+  const int64_t np = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  return np < 1 ? 1 : np;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
+                         float scale, int32_t dtype, float* lse_out, void* stream) {
+  int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  DecodeArgs args{};
+  args.query = query;
+  args.key_cache = key_cache;
+  args.value_cache = value_cache;
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.out = out;
+  args.lse_out = lse_out;
+  args.num_blocks = num_blocks;
+  args.max_blocks = max_blocks_per_seq;
+  args.num_heads = num_heads;
+  args.num_kv_heads = num_kv_heads;
+  args.group = num_heads / num_kv_heads;
+  args.part_tokens = max_blocks_per_seq * kBlockTokens;
+  args.num_parts = 1;
+  args.scale_log2 = scale * kLog2e;
+  return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                                  int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0 || partition_size <= 0) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * split_parts(max_context_len, partition_size);
+  return align256(rows * head_size * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+extern "C" int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                               int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes,
+                               float* lse_out, void* stream) {
+  int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % kBlockTokens != 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  const size_t need = pa_decode_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
+                                                      partition_size);
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const int64_t np = split_parts(max_context_len, partition_size);
+  if (np > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * head_size * sizeof(float)));
+
+  DecodeArgs args{};
+  args.query = query;
+  args.key_cache = key_cache;
+  args.value_cache = value_cache;
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.num_blocks = num_blocks;
+  args.max_blocks = max_blocks_per_seq;
+  args.num_heads = num_heads;
+  args.num_kv_heads = num_kv_heads;
+  args.group = num_heads / num_kv_heads;
+  args.part_tokens = partition_size;
+  args.num_parts = static_cast<int32_t>(np);
+  args.scale_log2 = scale * kLog2e;
+  if (np == 1) {  // one partition: the partial is already the answer
+    args.out = out;
+    args.lse_out = lse_out;
+    return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
+  }
+  args.o_parts = o_parts;
+  args.lse_parts = lse_parts;
+  st = launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
+  return launch_merge(out, lse_out, o_parts, lse_parts, static_cast<int64_t>(num_seqs) * num_heads,
+                      static_cast<int>(np), head_size, dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pa_merge_partitions(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_parts, int32_t head_size,
+                                   int32_t dtype, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || num_parts <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !o_parts || !lse_parts) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(o_parts)) return PA_ERR_INVALID_ARG;
+  return launch_merge(out, lse_out, o_parts, lse_parts, static_cast<int64_t>(num_seqs) * num_heads, num_parts,
+                      head_size, dtype, static_cast<hipStream_t>(stream));
+}

@@ -1,0 +1,83 @@
+"""Plumbing shared by the GPU tests: upload host inputs, run entry points, read back."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+import workloads as W
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}        # max |out - oracle|
+LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}    # max |lse - oracle|
+PART_TOL = {"bf16": 1e-3, "f32": 1e-5}   # float32 partials from bf16 inputs
+
+
+def ensure_built():
+    import paged_kv_cache_150_amd as pa
+    if not os.path.exists(pa.library_path()):
+        from paged_kv_cache_150_amd.build import build_library
+        build_library()
+    pa.load_library()
+    return pa
+
+
+def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
+    """Host array -> GPU tensor. uint16 arrays are bfloat16 bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """GPU tensor -> raw bits on the host (uint16 for bf16, uint32 for f32)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy().view(np.uint32)
+    return t.numpy()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class Dev:
+    """Device copies of one workload."""
+
+    def __init__(self, inp: W.PagedInputs, key_cache=None, value_cache=None):
+        self.inp = inp
+        self.cfg = inp.cfg
+        self.kc = to_dev(inp.key_cache if key_cache is None else key_cache)
+        self.vc = to_dev(inp.value_cache if value_cache is None else value_cache)
+        self.q = to_dev(inp.query)
+        self.bt = to_dev(inp.block_tables)
+        self.cl = to_dev(inp.context_lens)
+
+    def decode(self, pa, lse=False):
+        out = torch.empty_like(self.q)
+        lse_t = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda") if lse else None
+        pa.pa_decode(out, self.q, self.kc, self.vc, self.bt, self.cl, self.cfg.scale, lse_out=lse_t)
+        return out, lse_t
+
+    def decode_split(self, pa, partition_size=None, lse=False, max_context_len=None):
+        P = partition_size or self.cfg.partition_size
+        mcl = self.inp.max_context_len if max_context_len is None else max_context_len
+        S, Hq, d = self.q.shape
+        nbytes = pa.pa_decode_split_workspace_bytes(S, Hq, d, mcl, P)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(self.q)
+        lse_t = torch.empty((S, Hq), dtype=torch.float32, device="cuda") if lse else None
+        pa.pa_decode_split(out, self.q, self.kc, self.vc, self.bt, self.cl, self.cfg.scale, mcl, P, ws,
+                           lse_out=lse_t)
+        return out, lse_t, ws
+
+
+def max_err(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    g = f64(gpu)
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(g - ref))
+    return float(np.nan_to_num(diff, nan=np.inf).max()) if diff.size else 0.0

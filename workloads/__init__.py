@@ -23,8 +23,10 @@ Workload shapes follow the pages' statement of the problem:
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 import math
+import os
 
 import numpy as np
 
@@ -128,9 +130,33 @@ def draw_context_lens(cfg: PagedConfig, seed: int | None = None) -> np.ndarray:
     return _draw_context_lens(cfg, np.random.default_rng(cfg.seed if seed is None else seed))
 
 
+_CHUNK = 1 << 22  # elements per independent sub-stream of a large draw
+
+
 def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    return x if dtype == "f32" else f32_to_bf16_bits(x)
+    """N(0,1) values of ``shape``: float32, or bfloat16 bits (RNE) for ``bf16``.
+
+    One seed is drawn from ``rng``; the array is then filled in fixed chunks of
+    2^22 elements, each from its own child stream of that seed
+    (numpy SeedSequence.spawn), so the result does not depend on how many
+    threads fill it.
+    """
+    n = int(np.prod(shape))
+    seed = int(rng.integers(0, 2 ** 63))
+    kids = np.random.SeedSequence(seed).spawn(max(1, -(-n // _CHUNK)))
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+
+    def fill(i):
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = np.random.default_rng(kids[i]).standard_normal(size=hi - lo, dtype=np.float32)
+        out[lo:hi] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    if len(kids) == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(len(kids))))
+    return out.reshape(shape)
 
 
 def poison_value(dtype: str):
@@ -263,6 +289,23 @@ def make_inputs(cfg: PagedConfig, mode: str = "parity", seed: int | None = None,
                        new_value=new_value, slot_mapping=slot, referenced_blocks=referenced,
                        shared_prefix_blocks=prefix_blocks,
                        meta={"mode": mode, "seed": cfg.seed if seed is None else seed})
+
+
+def caches_before_write(inp: PagedInputs):
+    """Copies of the caches as they are before this step's new tokens are written.
+
+    The new token of each sequence is the row at its slot; before the write that
+    row holds poison (NaN), so a missing write shows up in the decode output.
+    """
+    cfg = inp.cfg
+    rows = cfg.num_blocks * cfg.block_size
+    kc = inp.key_cache.copy()
+    vc = inp.value_cache.copy()
+    ok = (inp.slot_mapping >= 0) & (inp.slot_mapping < rows)
+    fill = poison_value(cfg.dtype)
+    kc.reshape(rows, cfg.num_kv_heads, cfg.head_size)[inp.slot_mapping[ok]] = fill
+    vc.reshape(rows, cfg.num_kv_heads, cfg.head_size)[inp.slot_mapping[ok]] = fill
+    return kc, vc
 
 
 def algorithmic_kv_bytes(cfg: PagedConfig, context_lens: np.ndarray) -> int:
