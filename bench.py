@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: reshape_and_cache writes
+each sequence's new-token K/V through slot_mapping, then paged decode reads
+every context through the block tables (one-pass kernel, or partition kernel
++ log-sum-exp merge with ``--decode split``). Inputs are synthetic, generated
+with the shapes of the Llama-3-8B-like batch-256 workload and copied to HBM
+before timing; two copies of the KV pool alternate between steps so no step
+finds the previous step's K/V in the caches.
+
+Prints ONE JSON line. ``value`` is the effective KV read bandwidth of the
+whole step (bytes of K and V the step must read, over step time).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+DEFAULT_WORKLOAD = "llama3_8b_b256"
+KERNEL_SOURCES = ["paged_kv_cache_150_amd/csrc/paged_decode.hip", "paged_kv_cache_150_amd/csrc/pa_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, decode: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{decode}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD, help="workload name (see workloads.CONFIGS)")
+    ap.add_argument("--decode", choices=["fused", "split"], default="fused",
+                    help="fused: pa_decode (one pass); split: pa_decode_split (partitions + LSE merge)")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB 20 times (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 20}))
+
+
+def cpu_baseline(cfg, inp, budget_s: float):
+    """The fp64 oracle on the host cores over the same batch, repeated to ~budget_s."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
+                            cfg.scale, cfg.dtype)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    kv = W.algorithmic_kv_bytes(cfg, inp.context_lens)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, pa_decode of the full {cfg.num_seqs}-sequence batch "
+                      f"({reps} passes, {dt:.2f} s each; decode only, no reshape)",
+            "seqs_per_s": cfg.num_seqs / dt, "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import paged_kv_cache_150_amd as pa
+    import workloads as W
+
+    if not os.path.exists(pa.library_path()):
+        from paged_kv_cache_150_amd.build import build_library
+        build_library()
+    pa.load_library()
+
+    cfg = W.CONFIG_BY_NAME[args.config]
+    P = args.partition_size or cfg.partition_size
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    inp = W.make_inputs(cfg, mode="perf")
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # Two resident copies of the pool (same contents), used on alternate steps.
+    pools = [(up(inp.key_cache), up(inp.value_cache)) for _ in range(2)]
+    q, bt, cl = up(inp.query), up(inp.block_tables), up(inp.context_lens)
+    new_k, new_v, slots = up(inp.new_key), up(inp.new_value), up(inp.slot_mapping)
+    out = torch.empty_like(q)
+    S, Hq, d = cfg.num_seqs, cfg.num_heads, cfg.head_size
+    mcl = inp.max_context_len
+    ws = torch.empty(max(256, pa.pa_decode_split_workspace_bytes(S, Hq, d, mcl, P)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def decode(kc, vc):
+        if args.decode == "fused":
+            pa.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, stream=stream)
+        else:
+            pa.pa_decode_split(out, q, kc, vc, bt, cl, cfg.scale, mcl, P, ws, stream=stream)
+
+    def step(i):
+        kc, vc = pools[i & 1]
+        pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+        decode(kc, vc)
+
+    print(f"[bench] warmup {args.warmup}, timed {args.steps} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Per-launch events around the decode call inside the timed region, on the
+    # stream the kernels run on.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        kc, vc = pools[i & 1]
+        pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+        ev[i][0].record(stream)
+        decode(kc, vc)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg = statistics.fmean(dec_ms)
+    dec_med = statistics.median(dec_ms)
+
+    kv_bytes = W.algorithmic_kv_bytes(cfg, inp.context_lens)
+    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
+    traffic = stored_traffic(cfg.name, args.decode)
+    rec = {
+        "metric": "paged decode attention effective KV GB/s (% of HBM peak) + seqs/sec, 1 GPU",
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "description": cfg.description, "num_seqs": S, "num_heads": Hq,
+                   "num_kv_heads": cfg.num_kv_heads, "head_size": d, "block_size": cfg.block_size,
+                   "num_blocks": cfg.num_blocks, "mean_context": float(inp.context_lens.mean()),
+                   "decode": args.decode, "partition_size": P if args.decode == "split" else None,
+                   "step": "pa_reshape_and_cache + " + ("pa_decode" if args.decode == "fused" else
+                                                        "pa_decode_split")},
+        "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "decode_ms_avg": round(dec_avg, 5),
+        "decode_ms_median": round(dec_med, 5),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "paged_decode_kernel" + ("" if args.decode == "fused" else
+                                                        " + merge_partitions_kernel"),
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "kernel_source_hash": kernel_source_hash()},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
