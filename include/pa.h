@@ -134,22 +134,30 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * pa_decode_split - the same result as pa_decode, computed over context
  * partitions and merged exactly.
  *
- * Partition p covers positions [p*P, min((p+1)*P, n)), P = partition_size.
- * A first kernel writes each partition's normalised output o_p and its
- * log-sum-exp lse_p into `workspace` (empty partitions: lse_p = -inf); then
- * pa_merge_partitions' kernel combines them on the same stream. The merge
- * follows from the softmax normaliser identity the pages lean on for
- * streaming (stanleyjacob.dev "vLLM", Part V "The attention backend dispatch
- * layer": tiling plus online softmax); the partitioned form itself is this
- * library's reading.
+ * Partition p of sequence i covers positions [p*P, min((p+1)*P, n_i)),
+ * P = partition_size, so sequence i has ceil(n_i / P) partitions. A first
+ * kernel computes each partition's normalised output o_p and log-sum-exp
+ * lse_p; the units (sequence, kv head, partition) are spread evenly over
+ * persistent workers, so long and short contexts share the GPU evenly. A
+ * second kernel on the same stream merges the partials of every sequence with
+ * more than one partition (the log-sum-exp merge of pa_merge_partitions);
+ * sequences with a single partition get their output from the first kernel
+ * directly. The merge rests on the softmax normaliser identity the pages lean
+ * on for streaming (stanleyjacob.dev "vLLM", Part V "The attention backend
+ * dispatch layer": tiling plus online softmax); the partitioned form itself is
+ * this library's reading.
  *
- *   max_context_len   host-side upper bound of context_lens (sizes the grid
- *                     without reading the lengths back). Positions past
- *                     num_parts*P are ignored, so it must be >= every length.
+ *   max_context_len   host-side upper bound of context_lens (sizes the
+ *                     partial buffers without reading the lengths back).
+ *                     Positions past ceil(max_context_len/P)*P are ignored,
+ *                     so it must be >= every length.
  *   partition_size    multiple of block_size, > 0.
  *   workspace         device memory of at least
  *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
- *                     aligned, owned by the caller; overwritten.
+ *                     aligned, owned by the caller. Only the slots of
+ *                     sequences with more than one partition are written
+ *                     (o_p at [i][h][p][:], lse_p at [i][h][p] for p <
+ *                     ceil(n_i/P)); the rest is left untouched.
  *   lse_out           optional float32 [num_seqs, num_heads]; NULL to skip.
  * Other arguments as pa_decode. Returns PA_OK or an error status.
  */

@@ -40,6 +40,23 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// A wave-uniform pointer passed through readfirstlane: the compiler keeps it in
+// scalar registers and does not fold per-lane offsets into it, so loads use the
+// scalar-base + 32-bit-lane-offset addressing form.
+typedef __attribute__((address_space(1))) const char gchar_t;  // global-memory byte
+
+__device__ __forceinline__ const gchar_t* uniform_ptr(const char* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const gchar_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Load of a 16-byte vector from global memory.
+__device__ __forceinline__ u32x4_t gload16(const gchar_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t*>(p);
+}
+
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
@@ -61,16 +78,16 @@ __device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, float x) { *p = f3
 
 // Load `NDW` dwords (8, 16 or 32 bytes) that are 16-byte (or 8-byte) aligned.
 template <int NDW>
-__device__ __forceinline__ void load_dwords(uint32_t (&dst)[NDW], const void* src) {
+__device__ __forceinline__ void load_dwords(uint32_t (&dst)[NDW], const gchar_t* src) {
   if constexpr (NDW == 2) {
-    u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
+    u32x2_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(src);
     dst[0] = v[0];
     dst[1] = v[1];
   } else {
     static_assert(NDW % 4 == 0, "16-byte granules");
 #pragma unroll
     for (int i = 0; i < NDW / 4; ++i) {
-      u32x4_t v = reinterpret_cast<const u32x4_t*>(src)[i];
+      u32x4_t v = gload16(src + 16 * i);
       dst[4 * i + 0] = v[0];
       dst[4 * i + 1] = v[1];
       dst[4 * i + 2] = v[2];

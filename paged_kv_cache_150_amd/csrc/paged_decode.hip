@@ -78,29 +78,34 @@ struct DecodeArgs {
   float scale_log2;     // scale * log2(e)
 };
 
+// Loads one chunk (CB blocks) of K and V for this wave's kv head. Block ids
+// are wave-uniform, so each load is a scalar base (block, head, row) plus a
+// 32-bit per-lane offset.
 template <typename T, int D, int G, int CB>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB>& f, const char* kc, const char* vc,
                                            const int32_t* bt_row, int blk0, int blk_last,
-                                           int64_t num_blocks, int64_t tok_stride_bytes,
+                                           int64_t num_blocks, uint32_t tok_stride_bytes,
                                            int64_t blk_stride_bytes, int64_t head_off_bytes,
                                            int lane) {
   using S = DecodeShape<T, D, G, CB>;
   const int tok = lane & 15;
   const int j = lane >> 4;
+  const uint32_t koff = tok * tok_stride_bytes + j * 16;                      // K: row tok, piece j
+  const uint32_t voff = (4 * j) * tok_stride_bytes + tok * (S::kVDw * 4);     // V: rows 4j.., piece tok
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int b = min(blk0 + i, blk_last);
     // Out-of-range ids (negative included) are clamped so a bad table never
     // leads to an out-of-bounds access.
-    uint64_t phys = static_cast<uint32_t>(bt_row[b]);
+    uint64_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bt_row[b]));
     phys = phys < static_cast<uint64_t>(num_blocks) ? phys : static_cast<uint64_t>(num_blocks - 1);
     const int64_t base = static_cast<int64_t>(phys) * blk_stride_bytes + head_off_bytes;
-    const char* krow = kc + base + tok * tok_stride_bytes + j * 16;
+    const gchar_t* kb = uniform_ptr(kc + base);
+    const gchar_t* vb = uniform_ptr(vc + base);
 #pragma unroll
-    for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = *reinterpret_cast<const u32x4_t*>(krow + s * 64);
-    const char* vrow = vc + base + (4 * j) * tok_stride_bytes + tok * (S::kVDw * 4);
+    for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + koff);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) load_dwords<S::kVDw>(f.v[i][r], vrow + r * tok_stride_bytes);
+    for (int r = 0; r < 4; ++r) load_dwords<S::kVDw>(f.v[i][r], vb + r * tok_stride_bytes + voff);
   }
 }
 
@@ -112,14 +117,12 @@ struct WaveState {
   float acc[G][S::kVec];    // partial P*V, this lane's tokens and d range
 };
 
+// Scores of one chunk: s[i][r] = scale*log2(e) * <q, K> for token 4*(lane/16)+r
+// of block i and head lane % 16.
 template <typename T, int D, int G, int CB>
-__device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB>& f,
-                                              const u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg],
-                                              float scale_log2, int tok0, int t_end, bool mask,
-                                              int lane) {
+__device__ __forceinline__ void qk_chunk(float (&s)[CB][4], const Chunk<T, D, G, CB>& f,
+                                         const u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg], float scale_log2) {
   using S = DecodeShape<T, D, G, CB>;
-  const int rg = lane >> 4;
-  float s[CB][4];
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -139,6 +142,14 @@ __device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const 
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[i][r] = c[r] * scale_log2;
   }
+}
+
+// Online-softmax update and P*V for one chunk whose scores are in s.
+template <typename T, int D, int G, int CB>
+__device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB>& f,
+                                                 float (&s)[CB][4], int tok0, int t_end, bool mask, int lane) {
+  using S = DecodeShape<T, D, G, CB>;
+  const int rg = lane >> 4;
   // The chunk that straddles the end of the context: positions >= t_end get
   // weight exactly 0 and their V rows (stale or poisoned) are replaced by 0.
   uint32_t vz[CB][4][S::kVDw];
@@ -211,6 +222,30 @@ __device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const 
     }
 }
 
+template <typename T, int D, int G, int CB>
+__device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB>& f,
+                                              const u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg],
+                                              float scale_log2, int tok0, int t_end, bool mask, int lane) {
+  float s[CB][4];
+  qk_chunk<T, D, G, CB>(s, f, q, scale_log2);
+  softmax_pv_chunk<T, D, G, CB>(st, f, s, tok0, t_end, mask, lane);
+}
+
+template <typename T, int D, int G, int CB>
+__device__ __forceinline__ void load_query(const void* query, int seq, int num_heads, int head0, int g, int lane,
+                                           u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg]) {
+  using S = DecodeShape<T, D, G, CB>;
+  const int hq = lane & 15;
+  const gchar_t* qb = uniform_ptr(static_cast<const char*>(query) +
+                                  (static_cast<int64_t>(seq) * num_heads + head0) * D * S::kElemBytes);
+  const uint32_t qoff = (hq < g ? hq : 0) * (D * S::kElemBytes) + (lane >> 4) * 16;
+#pragma unroll
+  for (int sg = 0; sg < S::kKSeg; ++sg) {
+    u32x4_t v = gload16(qb + sg * 64 + qoff);
+    q[sg] = hq < g ? v : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
 template <typename T, int D, int G, int CB, bool PF>
 __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D, G, CB>;
@@ -219,7 +254,9 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
   __shared__ float s_l[8][16];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep all
+  // per-wave indexing (units, block ids, base addresses) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
 
   // kv head fastest: with 8 kv heads and 8 XCDs every XCD sees one kv head,
@@ -238,8 +275,8 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
   const int g = a.group;
   const int head0 = kvh * g;
 
-  const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * D * S::kElemBytes;
-  const int64_t blk_stride = tok_stride * kBlockTokens;
+  const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
+  const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
   const int64_t head_off = static_cast<int64_t>(kvh) * D * S::kElemBytes;
   const char* kc = static_cast<const char*>(a.key_cache);
   const char* vc = static_cast<const char*>(a.value_cache);
@@ -256,19 +293,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
   if (t_begin < t_end) {
     // Query fragment (MFMA B operand): head lane%16 of the group, same d order as K.
     u32x4_t q[S::kKSeg];
-    {
-      const int hq = lane & 15;
-      const int j = lane >> 4;
-      const char* qrow = static_cast<const char*>(a.query) +
-                         (static_cast<int64_t>(seq) * a.num_heads + head0 + (hq < g ? hq : 0)) * D *
-                             S::kElemBytes +
-                         j * 16;
-#pragma unroll
-      for (int sg = 0; sg < S::kKSeg; ++sg) {
-        u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + sg * 64);
-        q[sg] = hq < g ? v : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+    load_query<T, D, G, CB>(a.query, seq, a.num_heads, head0, g, lane, q);
     const int blk_begin = t_begin / kBlockTokens;
     const int blk_end = (t_end + kBlockTokens - 1) / kBlockTokens;
     const int blk_last = blk_end - 1;
@@ -360,6 +385,292 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
       if (d == 0) a.lse_parts[prow] = lse;
     }
   }
+}
+
+// ------------------------------------------------------------------ partitioned path
+// Persistent wave workers. A unit of work is (sequence, kv head, partition of
+// part_tokens positions). The units of one kv head are numbered sequence by
+// sequence (sequence i owns ceil(n_i / P) units) and unit k goes to worker
+// k % workers, so every worker gets the same number of units, all but the
+// last of each sequence exactly P long. A worker is one wave: it streams the
+// chunks of its units back to back with the next chunk (possibly of the next
+// unit) in flight, and closes each unit by writing that partition's
+// normalised output and log-sum-exp (or the final output when the sequence has
+// a single partition). No LDS traffic or barriers inside the loop.
+struct UnitArgs {
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* lse_out;
+  float* o_parts;
+  float* lse_parts;
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t part_tokens;
+  int32_t num_parts;
+  int32_t prefix_in_lds;  // 1: per-sequence unit prefix sums in LDS; 0: fixed num_parts units per sequence
+  float scale_log2;
+};
+
+// Tokens of sequence `seq` that the partitioned path covers.
+__device__ __forceinline__ int covered_tokens(const int32_t* context_lens, int seq, int max_blocks,
+                                              int part_tokens, int num_parts) {
+  int n = context_lens[seq];
+  const int64_t cap = min(static_cast<int64_t>(max_blocks) * kBlockTokens,
+                          static_cast<int64_t>(part_tokens) * num_parts);
+  return n < 0 ? 0 : static_cast<int>(n > cap ? cap : n);
+}
+
+struct UnitCursor {
+  int k;         // unit index within this kv head, or -1 when the worker is done
+  int seq;
+  int part;
+  int nparts;    // partitions of this sequence
+  int t_end;     // exclusive end position of the unit
+  int blk0;      // first block of the unit
+  int blk_last;  // last block of the unit (inclusive)
+  int nchunk;
+  int c;         // chunk within the unit
+};
+
+template <int CB>
+__device__ __forceinline__ void cursor_set_unit(UnitCursor& u, const UnitArgs& a, const int* s_pre, int stride) {
+  // Find the next unit with work at or after u.k.
+  for (;;) {
+    if (a.prefix_in_lds) {
+      const int total = __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
+      if (u.k >= total) { u.k = -1; return; }
+      int lo = 0, hi = a.num_seqs;  // largest seq with s_pre[seq] <= k
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= u.k) lo = mid; else hi = mid;
+      }
+      u.seq = __builtin_amdgcn_readfirstlane(lo);
+      u.part = u.k - __builtin_amdgcn_readfirstlane(s_pre[u.seq]);
+      u.nparts = __builtin_amdgcn_readfirstlane(s_pre[u.seq + 1]) + u.part - u.k;
+    } else {
+      if (u.k >= a.num_seqs * a.num_parts) { u.k = -1; return; }
+      u.seq = u.k / a.num_parts;
+      u.part = u.k - u.seq * a.num_parts;
+    }
+    const int n = __builtin_amdgcn_readfirstlane(
+        covered_tokens(a.context_lens, u.seq, a.max_blocks, a.part_tokens, a.num_parts));
+    const int t0 = u.part * a.part_tokens;
+    if (t0 < n) {
+      if (!a.prefix_in_lds) u.nparts = (n + a.part_tokens - 1) / a.part_tokens;
+      u.t_end = min(n, t0 + a.part_tokens);
+      u.blk0 = t0 / kBlockTokens;
+      u.blk_last = (u.t_end + kBlockTokens - 1) / kBlockTokens - 1;
+      u.nchunk = (u.blk_last - u.blk0 + CB) / CB;
+      u.c = 0;
+      return;
+    }
+    u.k += stride;  // empty unit (only without LDS prefix sums)
+  }
+}
+
+template <int CB>
+__device__ __forceinline__ void cursor_advance(UnitCursor& u, const UnitArgs& a, const int* s_pre, int stride) {
+  if (++u.c < u.nchunk) return;
+  u.k += stride;
+  cursor_set_unit<CB>(u, a, s_pre, stride);
+}
+
+// Close a unit: sum over row groups, normalise, write the partial (or the final
+// output). After the xor reduction every row group holds the totals, so row
+// group rg writes heads h with h % 4 == rg.
+template <typename T, int D, int G, int CB>
+__device__ __forceinline__ void finish_unit(WaveState<T, D, G, CB>& st, const UnitArgs& a, const UnitCursor& u,
+                                            int head0, int lane) {
+  using S = DecodeShape<T, D, G, CB>;
+  float l = st.l;
+  l += xor_shfl(l, 16);
+  l += xor_shfl(l, 32);
+  const float lse_col = (st.m + fast_log2(l)) * kLn2;  // head lane % 16
+  const int rg = lane >> 4;
+  const int c = lane & 15;
+  static_for<G>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const float Lh = row_bcast<h>(l);
+    const float inv = 1.f / Lh;
+    float o[S::kVec];
+#pragma unroll
+    for (int e = 0; e < S::kVec; ++e) {
+      float x = st.acc[h][e];
+      x += xor_shfl(x, 16);
+      x += xor_shfl(x, 32);
+      o[e] = x * inv;
+    }
+    if ((h & 3) == rg && h < a.group) {
+      const int64_t row = static_cast<int64_t>(u.seq) * a.num_heads + head0 + h;
+      if (u.nparts == 1) {
+        T* dst = static_cast<T*>(a.out) + row * D + c * S::kVec;
+#pragma unroll
+        for (int e = 0; e < S::kVec; ++e) store_elem<T>(dst + e, o[e]);
+      } else {
+        float* dst = a.o_parts + (row * a.num_parts + u.part) * D + c * S::kVec;
+#pragma unroll
+        for (int e = 0; e < S::kVec; e += 4)
+          *reinterpret_cast<f32x4_t*>(dst + e) = f32x4_t{o[e], o[e + 1], o[e + 2], o[e + 3]};
+      }
+    }
+  });
+  if (rg == 0 && c < a.group) {
+    const int64_t row = static_cast<int64_t>(u.seq) * a.num_heads + head0 + c;
+    if (u.nparts == 1) {
+      if (a.lse_out != nullptr) a.lse_out[row] = lse_col;
+    } else {
+      a.lse_parts[row * a.num_parts + u.part] = lse_col;
+    }
+  }
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
+}
+
+template <typename T, int D, int G, int CB>
+__global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) {
+  using S = DecodeShape<T, D, G, CB>;
+  extern __shared__ int s_pre[];  // [num_seqs + 1] when a.prefix_in_lds
+  const int lane = threadIdx.x & 63;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep all
+  // per-wave indexing (units, block ids, base addresses) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int kvh = blockIdx.x % a.num_kv_heads;
+  const int stride = (gridDim.x / a.num_kv_heads) * nwaves;  // workers per kv head
+  const int worker = (blockIdx.x / a.num_kv_heads) * nwaves + wave;
+
+  if (a.prefix_in_lds) {
+    // Exclusive prefix sum of units per sequence: thread t sums a contiguous
+    // run of sequences, then the run totals are scanned in LDS.
+    const int per = (a.num_seqs + blockDim.x - 1) / blockDim.x;
+    const int s0 = threadIdx.x * per;
+    const int s1 = min(a.num_seqs, s0 + per);
+    int run = 0;
+    for (int i = s0; i < s1; ++i) {
+      const int n = covered_tokens(a.context_lens, i, a.max_blocks, a.part_tokens, a.num_parts);
+      run += (n + a.part_tokens - 1) / a.part_tokens;
+    }
+    __shared__ int s_run[256];
+    s_run[threadIdx.x] = run;
+    __syncthreads();
+    for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
+      const int v = threadIdx.x >= static_cast<unsigned>(off) ? s_run[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_run[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int base = s_run[threadIdx.x] - run;
+    for (int i = s0; i < s1; ++i) {
+      s_pre[i] = base;
+      const int n = covered_tokens(a.context_lens, i, a.max_blocks, a.part_tokens, a.num_parts);
+      base += (n + a.part_tokens - 1) / a.part_tokens;
+    }
+    if (threadIdx.x == blockDim.x - 1) s_pre[a.num_seqs] = s_run[threadIdx.x];
+    __syncthreads();
+  }
+
+  UnitCursor cur;
+  cur.k = worker;
+  cursor_set_unit<CB>(cur, a, s_pre, stride);
+  if (cur.k < 0) return;
+
+  const int g = a.group;
+  const int head0 = kvh * g;
+  const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
+  const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
+  const int64_t head_off = static_cast<int64_t>(kvh) * D * S::kElemBytes;
+  const char* kc = static_cast<const char*>(a.key_cache);
+  const char* vc = static_cast<const char*>(a.value_cache);
+  auto bt_row = [&](int seq) { return a.block_tables + static_cast<int64_t>(seq) * a.max_blocks; };
+
+  WaveState<T, D, G, CB> st;
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
+
+  u32x4_t q[S::kKSeg];
+  load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, head0, g, lane, q);
+  Chunk<T, D, G, CB> fa, fb;
+  load_chunk<T, D, G, CB>(fa, kc, vc, bt_row(cur.seq), cur.blk0, cur.blk_last, a.num_blocks, tok_stride,
+                          blk_stride, head_off, lane);
+  UnitCursor nx = cur;
+  cursor_advance<CB>(nx, a, s_pre, stride);
+
+  auto step = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
+    if (nx.k >= 0)
+      load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.blk0 + nx.c * CB, nx.blk_last, a.num_blocks,
+                              tok_stride, blk_stride, head_off, lane);
+    const int tok0 = (cur.blk0 + cur.c * CB) * kBlockTokens;
+    const bool last = cur.c == cur.nchunk - 1;
+    float sc[CB][4];
+    qk_chunk<T, D, G, CB>(sc, fcur, q, a.scale_log2);
+    // The query of the next unit is fetched as soon as this unit's last
+    // scores are out, so its latency hides behind the P*V work.
+    if (last && nx.k >= 0) load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, head0, g, lane, q);
+    softmax_pv_chunk<T, D, G, CB>(st, fcur, sc, tok0, cur.t_end, tok0 + CB * kBlockTokens > cur.t_end, lane);
+    if (last) finish_unit<T, D, G, CB>(st, a, cur, head0, lane);
+    if (nx.k < 0) return false;
+    cur = nx;
+    cursor_advance<CB>(nx, a, s_pre, stride);
+    return true;
+  };
+  while (step(fa, fb) && step(fb, fa)) {
+  }
+}
+
+// Merge for the partitioned path: row (sequence, head) combines the
+// ceil(n / P) partitions the unit kernel wrote. Sequences with one partition
+// were written directly by the unit kernel; an empty context gives 0 / -inf.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_units_kernel(T* __restrict__ out, float* __restrict__ lse_out,
+                                                          const float* __restrict__ o_parts,
+                                                          const float* __restrict__ lse_parts,
+                                                          const int32_t* __restrict__ context_lens, int num_seqs,
+                                                          int num_heads, int max_blocks, int part_tokens,
+                                                          int num_parts) {
+  constexpr int kPer = D / kWave;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= static_cast<int64_t>(num_seqs) * num_heads) return;
+  const int seq = static_cast<int>(row / num_heads);
+  const int n = covered_tokens(context_lens, seq, max_blocks, part_tokens, num_parts);
+  const int np = (n + part_tokens - 1) / part_tokens;
+  if (np == 1) return;
+  const float* lp = lse_parts + row * num_parts;
+  float M = -__builtin_inff();
+  for (int p = lane; p < np; p += kWave) M = fmaxf(M, lp[p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  const float* op = o_parts + row * num_parts * D + lane * kPer;
+  for (int p = 0; p < np; ++p) {
+    const float w = fast_exp2((lp[p] - M) * kLog2e);
+    L += w;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, op[p * D + e], acc[e]);
+  }
+  const bool empty = (np == 0);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_elem<T>(out + row * D + lane * kPer + e, empty ? 0.f : acc[e] / L);
+  if (lse_out != nullptr && lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + fast_log2(L) * kLn2;
 }
 
 // One wave per (sequence, head) row: out = sum_p w_p o_p / sum_p w_p with
@@ -486,6 +797,82 @@ int launch_decode(const DecodeArgs& args, int num_seqs, int dtype, int head_size
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+typedef void (*UnitKernel)(UnitArgs);
+
+template <typename T, int D, int G>
+UnitKernel unit_kernel_for() {
+  using P = Policy<T, D, G>;
+  return paged_decode_units_kernel<T, D, G, P::CB>;
+}
+
+template <typename T, int D>
+UnitKernel pick_unit_group(int G) {
+  switch (G) {
+    case 1: return unit_kernel_for<T, D, 1>();
+    case 2: return unit_kernel_for<T, D, 2>();
+    case 4: return unit_kernel_for<T, D, 4>();
+    case 8: return unit_kernel_for<T, D, 8>();
+    case 16: return unit_kernel_for<T, D, 16>();
+    default: return nullptr;
+  }
+}
+
+UnitKernel pick_unit(int dtype, int D, int G) {
+  if (dtype == PA_DTYPE_BF16) return D == 128 ? pick_unit_group<bf16_t, 128>(G) : pick_unit_group<bf16_t, 64>(G);
+  return D == 128 ? pick_unit_group<float, 128>(G) : pick_unit_group<float, 64>(G);
+}
+
+constexpr int kUnitThreads = 256;
+constexpr int kMaxLdsSeqs = 8192;
+
+// Workgroups that fit on the device at once for `kernel` (persistent grid size).
+int resident_groups(const void* kernel, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kUnitThreads, lds) != hipSuccess) return 0;
+  return cus * (per_cu > 0 ? per_cu : 1);
+}
+
+int launch_units(const UnitArgs& args, int dtype, int head_size, hipStream_t stream) {
+  const int G = next_pow2_group(args.group);
+  UnitKernel k = pick_unit(dtype, head_size, G);
+  if (!k) return PA_ERR_UNSUPPORTED;
+  const size_t lds = args.prefix_in_lds ? (static_cast<size_t>(args.num_seqs) + 1) * sizeof(int) : 0;
+  const int resident = resident_groups(reinterpret_cast<const void*>(k), lds);
+  if (resident <= 0) return PA_ERR_HIP;
+  const int64_t waves_needed = static_cast<int64_t>(args.num_seqs) * args.num_parts;  // per kv head, upper bound
+  const int64_t groups_per_head_needed = (waves_needed + kUnitThreads / kWave - 1) / (kUnitThreads / kWave);
+  int64_t per_head = resident / args.num_kv_heads;
+  if (per_head < 1) per_head = 1;
+  if (per_head > groups_per_head_needed) per_head = groups_per_head_needed;
+  const int64_t grid = per_head * args.num_kv_heads;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kUnitThreads), lds, stream, args);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int launch_merge_units(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
+                       const int32_t* context_lens, int num_seqs, int num_heads, int max_blocks, int part_tokens,
+                       int num_parts, int head_size, int dtype, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
+  if (rows <= 0) return PA_OK;
+  constexpr int kRowsPerBlock = 4;
+  const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
+#define PA_MERGE_UNITS(TT, DD)                                                                                    \
+  hipLaunchKernelGGL((merge_units_kernel<TT, DD>), g, b, 0, stream, static_cast<TT*>(out), lse_out, o_parts,     \
+                     lse_parts, context_lens, num_seqs, num_heads, max_blocks, part_tokens, num_parts)
+  if (dtype == PA_DTYPE_BF16) {
+    if (head_size == 128) PA_MERGE_UNITS(bf16_t, 128); else PA_MERGE_UNITS(bf16_t, 64);
+  } else {
+    if (head_size == 128) PA_MERGE_UNITS(float, 128); else PA_MERGE_UNITS(float, 64);
+  }
+#undef PA_MERGE_UNITS
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int launch_merge(void* out, float* lse_out, const float* o_parts, const float* lse_parts, int64_t rows,
                  int num_parts, int head_size, int dtype, hipStream_t stream) {
   if (rows <= 0) return PA_OK;
@@ -579,31 +966,30 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
   float* o_parts = static_cast<float*>(workspace);
   float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * head_size * sizeof(float)));
 
-  DecodeArgs args{};
+  UnitArgs args{};
   args.query = query;
   args.key_cache = key_cache;
   args.value_cache = value_cache;
   args.block_tables = block_tables;
   args.context_lens = context_lens;
+  args.out = out;
+  args.lse_out = lse_out;
+  args.o_parts = o_parts;
+  args.lse_parts = lse_parts;
   args.num_blocks = num_blocks;
   args.max_blocks = max_blocks_per_seq;
+  args.num_seqs = num_seqs;
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;
   args.group = num_heads / num_kv_heads;
   args.part_tokens = partition_size;
   args.num_parts = static_cast<int32_t>(np);
+  args.prefix_in_lds = num_seqs <= kMaxLdsSeqs ? 1 : 0;
   args.scale_log2 = scale * kLog2e;
-  if (np == 1) {  // one partition: the partial is already the answer
-    args.out = out;
-    args.lse_out = lse_out;
-    return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
-  }
-  args.o_parts = o_parts;
-  args.lse_parts = lse_parts;
-  st = launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
+  st = launch_units(args, dtype, head_size, static_cast<hipStream_t>(stream));
   if (st != PA_OK) return st;
-  return launch_merge(out, lse_out, o_parts, lse_parts, static_cast<int64_t>(num_seqs) * num_heads,
-                      static_cast<int>(np), head_size, dtype, static_cast<hipStream_t>(stream));
+  return launch_merge_units(out, lse_out, o_parts, lse_parts, context_lens, num_seqs, num_heads, max_blocks_per_seq,
+                            partition_size, static_cast<int>(np), head_size, dtype, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int pa_merge_partitions(void* out, float* lse_out, const float* o_parts, const float* lse_parts,

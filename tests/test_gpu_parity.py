@@ -53,21 +53,21 @@ def test_workload_reshape_then_decode(pa, cfg):
     assert e1 <= TOL[cfg.dtype] and e2 <= TOL[cfg.dtype]
     assert l1 <= LSE_TOL[cfg.dtype] and l2 <= LSE_TOL[cfg.dtype]
 
-    # The partials in the workspace are the per-partition attention results.
+    # The partials in the workspace are the per-partition attention results
+    # (written for sequences that span more than one partition).
     P = cfg.partition_size
     num_parts = max(1, -(-inp.max_context_len // P))
-    if num_parts > 1:
+    multi = [i for i in range(cfg.num_seqs) if -(-int(inp.context_lens[i]) // P) > 1][:8]
+    if multi:
         o_parts, lse_parts = pa.workspace_views(ws, cfg.num_seqs, cfg.num_heads, cfg.head_size,
                                                 inp.max_context_len, P)
-        seqs = list(range(min(cfg.num_seqs, 8)))
         ro, rl = oracle.paged_decode_partitions(inp.query, ref_k, ref_v, inp.block_tables, inp.context_lens,
-                                                cfg.scale, cfg.dtype, P, num_parts, seqs=seqs)
-        go, gl = f64(o_parts)[seqs], f64(lse_parts)[seqs]
-        ro, rl = ro[seqs], rl[seqs]
-        assert (np.isneginf(gl) == np.isneginf(rl)).all()
-        fin = np.isfinite(rl)
-        assert np.abs(gl[fin] - rl[fin]).max() <= LSE_TOL[cfg.dtype]
-        assert np.abs(go[fin] - ro[fin]).max() <= PART_TOL[cfg.dtype]
+                                                cfg.scale, cfg.dtype, P, num_parts, seqs=multi)
+        go, gl = f64(o_parts), f64(lse_parts)
+        for i in multi:
+            npi = -(-int(inp.context_lens[i]) // P)
+            assert np.abs(gl[i, :, :npi] - rl[i, :, :npi]).max() <= LSE_TOL[cfg.dtype]
+            assert np.abs(go[i, :, :npi] - ro[i, :, :npi]).max() <= PART_TOL[cfg.dtype]
 
 
 # --------------------------------------------------------------- shape sweep, ragged tails
