@@ -62,6 +62,8 @@ def parse_args():
     ap.add_argument("--decode", choices=["fused", "split"], default="fused",
                     help="fused: pa_decode (one pass); split: pa_decode_split (partitions + LSE merge)")
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--order", choices=["longest", "natural"], default="longest",
+                    help="seq_order schedule hint for pa_decode: longest context first (default) or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -152,6 +154,9 @@ def main():
     q, bt, cl = up(inp.query), up(inp.block_tables), up(inp.context_lens)
     new_k, new_v, slots = up(inp.new_key), up(inp.new_value), up(inp.slot_mapping)
     out = torch.empty_like(q)
+    # The schedule a serving loop would pass: it knows every context length on
+    # the host when it builds the block tables.
+    order = up(np.argsort(-inp.context_lens, kind="stable").astype(np.int32)) if args.order == "longest" else None
     S, Hq, d = cfg.num_seqs, cfg.num_heads, cfg.head_size
     mcl = inp.max_context_len
     ws = torch.empty(max(256, pa.pa_decode_split_workspace_bytes(S, Hq, d, mcl, P)), dtype=torch.uint8,
@@ -160,7 +165,7 @@ def main():
 
     def decode(kc, vc):
         if args.decode == "fused":
-            pa.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, stream=stream)
+            pa.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, seq_order=order, stream=stream)
         else:
             pa.pa_decode_split(out, q, kc, vc, bt, cl, cfg.scale, mcl, P, ws, stream=stream)
 
@@ -218,6 +223,7 @@ def main():
                    "num_kv_heads": cfg.num_kv_heads, "head_size": d, "block_size": cfg.block_size,
                    "num_blocks": cfg.num_blocks, "mean_context": float(inp.context_lens.mean()),
                    "decode": args.decode, "partition_size": P if args.decode == "split" else None,
+                   "seq_order": args.order if args.decode == "fused" else None,
                    "step": "pa_reshape_and_cache + " + ("pa_decode" if args.decode == "fused" else
                                                         "pa_decode_split")},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),

@@ -109,6 +109,13 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
  *   out               [num_seqs, num_heads, head_size], written (dtype).
  *   lse_out           optional float32 [num_seqs, num_heads]: ln sum_t exp(s_t).
  *                     NULL to skip.
+ *   seq_order         optional int32 [num_seqs], a permutation of the sequence
+ *                     indices: the order in which sequences are handed to the
+ *                     GPU (one workgroup per sequence and kv head, dispatched
+ *                     in order). Longest-first keeps the last wave of work
+ *                     short. It is a schedule only: every output is
+ *                     bit-identical to the NULL (natural order) result.
+ *                     Entries outside [0, num_seqs) are clamped.
  *   n = 0             gives out = 0 and lse = -inf.
  *   Table entries at index >= ceil(n / block_size) are never read.
  * Returns PA_OK or an error status.
@@ -117,7 +124,7 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               const int32_t* block_tables, int32_t max_blocks_per_seq,
               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
               int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
-              float scale, int32_t dtype, float* lse_out, void* stream);
+              float scale, int32_t dtype, float* lse_out, const int32_t* seq_order, void* stream);
 
 /*
  * pa_decode_split_workspace_bytes - workspace pa_decode_split needs.

@@ -55,7 +55,7 @@ def load_library() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
     lib.pa_reshape_and_cache.restype = c_int
     lib.pa_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
-                              c_f, c_i32, c_p, c_p]
+                              c_f, c_i32, c_p, c_p, c_p]
     lib.pa_decode.restype = c_int
     lib.pa_decode_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_split_workspace_bytes.restype = c_sz
@@ -163,13 +163,23 @@ def _decode_common(out, query, key_cache, value_cache, block_tables, context_len
 
 def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-              lse_out: torch.Tensor | None = None, stream=None) -> None:
-    """One-pass paged decode attention into ``out`` (optionally ln-sum-exp into ``lse_out``)."""
+              lse_out: torch.Tensor | None = None, seq_order: torch.Tensor | None = None,
+              stream=None) -> None:
+    """One-pass paged decode attention into ``out`` (optionally ln-sum-exp into ``lse_out``).
+
+    ``seq_order`` (int32 [num_seqs], a permutation) is a schedule hint: the order
+    in which sequences are dispatched, e.g. longest first. Results do not depend on it.
+    """
     p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
                                                    context_lens, lse_out)
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.shape != (S,):
+            raise ValueError("seq_order must be [num_seqs]")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
     lib = load_library()
     st = lib.pa_decode(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
-                       float(scale), _dtype_code(query), p["lse"], _stream(stream))
+                       float(scale), _dtype_code(query), p["lse"], order_ptr, _stream(stream))
     _check(st, "pa_decode")
 
 

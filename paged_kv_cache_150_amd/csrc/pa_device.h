@@ -37,6 +37,35 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 __device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, kWave); }
 
+// Combine each lane's value with lane l^16 (resp. l^32) on the VALU
+// (v_permlane16_swap / v_permlane32_swap give every lane both values of its
+// pair); unlike a shuffle through LDS this does not wait on the LDS/scalar
+// memory counter. Addition is commutative, so both lanes of a pair get the
+// same bits.
+__device__ __forceinline__ float pair16_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, static_cast<uint32_t>(r[0])), __builtin_bit_cast(float, static_cast<uint32_t>(r[1])));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, static_cast<uint32_t>(r[0])), __builtin_bit_cast(float, static_cast<uint32_t>(r[1])));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+// Sum / max over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_sum(float x) { return pair32_sum(pair16_sum(x)); }
+__device__ __forceinline__ float rows_max(float x) { return pair32_max(pair16_max(x)); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

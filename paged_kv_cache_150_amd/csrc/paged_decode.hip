@@ -64,19 +64,28 @@ struct DecodeArgs {
   const void* value_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  void* out;           // final output (num_parts == 1)
-  float* lse_out;      // optional, final lse (num_parts == 1)
-  float* o_parts;      // partials (num_parts > 1)
-  float* lse_parts;    // partials (num_parts > 1)
+  void* out;
+  float* lse_out;            // optional
+  const int32_t* seq_order;  // optional processing order of sequences
   int64_t num_blocks;
   int32_t max_blocks;
+  int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t group;        // H_q / H_kv
-  int32_t part_tokens;  // tokens per partition (multiple of 16)
-  int32_t num_parts;
   float scale_log2;     // scale * log2(e)
 };
+
+// Workgroup -> (sequence, kv head). Consecutive workgroups are dispatched to
+// the 8 XCDs in turn; the kv heads of one sequence are placed on the same XCD
+// (workgroups x, x+8, x+16, ...), so each XCD reads whole 2 KiB token rows and
+// all of its L2 channels, and consecutive XCDs take consecutive sequences.
+__device__ __forceinline__ void wg_to_seq_head(int id, int num_kv_heads, int& seq, int& kvh) {
+  const int xcd = id & 7;
+  const int k = id >> 3;
+  kvh = k % num_kv_heads;
+  seq = (k / num_kv_heads) * 8 + xcd;
+}
 
 // Loads one chunk (CB blocks) of K and V for this wave's kv head. Block ids
 // are wave-uniform, so each load is a scalar base (block, head, row) plus a
@@ -175,8 +184,7 @@ __device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, con
   for (int i = 0; i < CB; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[i][r]);
-  mx = fmaxf(mx, xor_shfl(mx, 16));
-  mx = fmaxf(mx, xor_shfl(mx, 32));
+  mx = rows_max(mx);
   const float m_new = fmaxf(st.m, mx);
   const float alpha = fast_exp2(st.m - m_new);
   st.m = m_new;
@@ -247,7 +255,7 @@ __device__ __forceinline__ void load_query(const void* query, int seq, int num_h
 }
 
 template <typename T, int D, int G, int CB, bool PF>
-__global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 1) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D, G, CB>;
   extern __shared__ float s_acc[];  // [W][G][D]
   __shared__ float s_m[8][16];
@@ -259,19 +267,21 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
 
-  // kv head fastest: with 8 kv heads and 8 XCDs every XCD sees one kv head,
-  // so blocks shared between sequences stay in that XCD's L2.
-  const int id = blockIdx.x;
-  const int kvh = id % a.num_kv_heads;
-  const int rest = id / a.num_kv_heads;
-  const int part = rest % a.num_parts;
-  const int seq = rest / a.num_parts;
+  int seq, kvh;
+  wg_to_seq_head(blockIdx.x, a.num_kv_heads, seq, kvh);
+  if (seq >= a.num_seqs) return;  // padding workgroups of the last XCD round
+  if (a.seq_order != nullptr) {
+    // Schedule hint: the j-th dispatched sequence is seq_order[j]. Out-of-range
+    // entries are clamped (wrong output for that caller, never a bad access).
+    const uint32_t o = static_cast<uint32_t>(a.seq_order[seq]);
+    seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
+  }
 
   const int max_tokens = a.max_blocks * kBlockTokens;
   int n = a.context_lens[seq];
   n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-  const int t_begin = part * a.part_tokens;
-  const int t_end = min(n, t_begin + a.part_tokens);
+  const int t_begin = 0;
+  const int t_end = n;
   const int g = a.group;
   const int head0 = kvh * g;
 
@@ -338,17 +348,11 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
   }
 
   // Sum this wave's partials over the 4 row groups (lanes l, l^16, l^32, l^48).
-  st.l += xor_shfl(st.l, 16);
-  st.l += xor_shfl(st.l, 32);
+  st.l = rows_sum(st.l);
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < S::kVec; ++e) {
-      float x = st.acc[h][e];
-      x += xor_shfl(x, 16);
-      x += xor_shfl(x, 32);
-      st.acc[h][e] = x;
-    }
+    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = rows_sum(st.acc[h][e]);
   if (lane < 16) {
     s_m[wave][lane] = st.m;
     s_l[wave][lane] = st.l;
@@ -376,27 +380,23 @@ __global__ __launch_bounds__(256, 2) void paged_decode_kernel(DecodeArgs a) {
     }
     const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
     const int64_t row = static_cast<int64_t>(seq) * a.num_heads + head0 + h;
-    if (a.num_parts == 1) {
-      store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
-      if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
-    } else {
-      const int64_t prow = row * a.num_parts + part;
-      a.o_parts[prow * D + d] = o;
-      if (d == 0) a.lse_parts[prow] = lse;
-    }
+    store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
+    if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
   }
 }
 
 // ------------------------------------------------------------------ partitioned path
-// Persistent wave workers. A unit of work is (sequence, kv head, partition of
-// part_tokens positions). The units of one kv head are numbered sequence by
-// sequence (sequence i owns ceil(n_i / P) units) and unit k goes to worker
-// k % workers, so every worker gets the same number of units, all but the
-// last of each sequence exactly P long. A worker is one wave: it streams the
-// chunks of its units back to back with the next chunk (possibly of the next
-// unit) in flight, and closes each unit by writing that partition's
-// normalised output and log-sum-exp (or the final output when the sequence has
-// a single partition). No LDS traffic or barriers inside the loop.
+// Persistent wave workers. A unit of work is (sequence, partition of
+// part_tokens positions, kv head). Units are numbered partition by partition
+// (sequence i owns ceil(n_i / P) partitions) with the kv head fastest, and
+// unit k goes to worker k % workers, so every worker gets the same number of
+// units, all but the last partition of each sequence exactly P long. Worker
+// ids are laid out so that the kv heads of one partition run on the same XCD
+// (whole 2 KiB token rows per L2). A worker is one wave: it streams the chunks
+// of its units back to back with the next chunk (possibly of the next unit)
+// in flight, and closes each unit by writing that partition's normalised
+// output and log-sum-exp (or the final output when the sequence has a single
+// partition). No LDS traffic or barriers inside the loop.
 struct UnitArgs {
   const void* query;
   const void* key_cache;
@@ -429,7 +429,8 @@ __device__ __forceinline__ int covered_tokens(const int32_t* context_lens, int s
 }
 
 struct UnitCursor {
-  int k;         // unit index within this kv head, or -1 when the worker is done
+  int k;         // unit index, or -1 when the worker is done
+  int kvh;
   int seq;
   int part;
   int nparts;    // partitions of this sequence
@@ -444,22 +445,24 @@ template <int CB>
 __device__ __forceinline__ void cursor_set_unit(UnitCursor& u, const UnitArgs& a, const int* s_pre, int stride) {
   // Find the next unit with work at or after u.k.
   for (;;) {
+    const int pu = u.k / a.num_kv_heads;  // partition-unit (sequence, partition)
     if (a.prefix_in_lds) {
       const int total = __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
-      if (u.k >= total) { u.k = -1; return; }
-      int lo = 0, hi = a.num_seqs;  // largest seq with s_pre[seq] <= k
+      if (pu >= total) { u.k = -1; return; }
+      int lo = 0, hi = a.num_seqs;  // largest seq with s_pre[seq] <= pu
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= u.k) lo = mid; else hi = mid;
+        if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= pu) lo = mid; else hi = mid;
       }
       u.seq = __builtin_amdgcn_readfirstlane(lo);
-      u.part = u.k - __builtin_amdgcn_readfirstlane(s_pre[u.seq]);
-      u.nparts = __builtin_amdgcn_readfirstlane(s_pre[u.seq + 1]) + u.part - u.k;
+      u.part = pu - __builtin_amdgcn_readfirstlane(s_pre[u.seq]);
+      u.nparts = __builtin_amdgcn_readfirstlane(s_pre[u.seq + 1]) + u.part - pu;
     } else {
-      if (u.k >= a.num_seqs * a.num_parts) { u.k = -1; return; }
-      u.seq = u.k / a.num_parts;
-      u.part = u.k - u.seq * a.num_parts;
+      if (pu >= a.num_seqs * a.num_parts) { u.k = -1; return; }
+      u.seq = pu / a.num_parts;
+      u.part = pu - u.seq * a.num_parts;
     }
+    u.kvh = u.k - pu * a.num_kv_heads;
     const int n = __builtin_amdgcn_readfirstlane(
         covered_tokens(a.context_lens, u.seq, a.max_blocks, a.part_tokens, a.num_parts));
     const int t0 = u.part * a.part_tokens;
@@ -488,11 +491,10 @@ __device__ __forceinline__ void cursor_advance(UnitCursor& u, const UnitArgs& a,
 // group rg writes heads h with h % 4 == rg.
 template <typename T, int D, int G, int CB>
 __device__ __forceinline__ void finish_unit(WaveState<T, D, G, CB>& st, const UnitArgs& a, const UnitCursor& u,
-                                            int head0, int lane) {
+                                            int lane) {
+  const int head0 = u.kvh * a.group;
   using S = DecodeShape<T, D, G, CB>;
-  float l = st.l;
-  l += xor_shfl(l, 16);
-  l += xor_shfl(l, 32);
+  const float l = rows_sum(st.l);
   const float lse_col = (st.m + fast_log2(l)) * kLn2;  // head lane % 16
   const int rg = lane >> 4;
   const int c = lane & 15;
@@ -502,12 +504,7 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, G, CB>& st, const Un
     const float inv = 1.f / Lh;
     float o[S::kVec];
 #pragma unroll
-    for (int e = 0; e < S::kVec; ++e) {
-      float x = st.acc[h][e];
-      x += xor_shfl(x, 16);
-      x += xor_shfl(x, 32);
-      o[e] = x * inv;
-    }
+    for (int e = 0; e < S::kVec; ++e) o[e] = rows_sum(st.acc[h][e]) * inv;
     if ((h & 3) == rg && h < a.group) {
       const int64_t row = static_cast<int64_t>(u.seq) * a.num_heads + head0 + h;
       if (u.nparts == 1) {
@@ -547,9 +544,11 @@ __global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) 
   // per-wave indexing (units, block ids, base addresses) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
-  const int kvh = blockIdx.x % a.num_kv_heads;
-  const int stride = (gridDim.x / a.num_kv_heads) * nwaves;  // workers per kv head
-  const int worker = (blockIdx.x / a.num_kv_heads) * nwaves + wave;
+  // gridDim.x is a multiple of 8; workgroup b runs on XCD b % 8. Workers of
+  // one XCD get consecutive ids, so consecutive units (the kv heads of one
+  // partition) share an XCD.
+  const int stride = gridDim.x * nwaves;
+  const int worker = (blockIdx.x & 7) * (gridDim.x >> 3) * nwaves + (blockIdx.x >> 3) * nwaves + wave;
 
   if (a.prefix_in_lds) {
     // Exclusive prefix sum of units per sequence: thread t sums a contiguous
@@ -587,13 +586,12 @@ __global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) 
   if (cur.k < 0) return;
 
   const int g = a.group;
-  const int head0 = kvh * g;
   const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
   const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
-  const int64_t head_off = static_cast<int64_t>(kvh) * D * S::kElemBytes;
   const char* kc = static_cast<const char*>(a.key_cache);
   const char* vc = static_cast<const char*>(a.value_cache);
   auto bt_row = [&](int seq) { return a.block_tables + static_cast<int64_t>(seq) * a.max_blocks; };
+  auto head_off = [&](int kvh) { return static_cast<int64_t>(kvh) * D * S::kElemBytes; };
 
   WaveState<T, D, G, CB> st;
   st.m = -__builtin_inff();
@@ -604,26 +602,26 @@ __global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) 
     for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
 
   u32x4_t q[S::kKSeg];
-  load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, head0, g, lane, q);
+  load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
   Chunk<T, D, G, CB> fa, fb;
   load_chunk<T, D, G, CB>(fa, kc, vc, bt_row(cur.seq), cur.blk0, cur.blk_last, a.num_blocks, tok_stride,
-                          blk_stride, head_off, lane);
+                          blk_stride, head_off(cur.kvh), lane);
   UnitCursor nx = cur;
   cursor_advance<CB>(nx, a, s_pre, stride);
 
   auto step = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
     if (nx.k >= 0)
       load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.blk0 + nx.c * CB, nx.blk_last, a.num_blocks,
-                              tok_stride, blk_stride, head_off, lane);
+                              tok_stride, blk_stride, head_off(nx.kvh), lane);
     const int tok0 = (cur.blk0 + cur.c * CB) * kBlockTokens;
     const bool last = cur.c == cur.nchunk - 1;
     float sc[CB][4];
     qk_chunk<T, D, G, CB>(sc, fcur, q, a.scale_log2);
     // The query of the next unit is fetched as soon as this unit's last
     // scores are out, so its latency hides behind the P*V work.
-    if (last && nx.k >= 0) load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, head0, g, lane, q);
+    if (last && nx.k >= 0) load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, nx.kvh * g, g, lane, q);
     softmax_pv_chunk<T, D, G, CB>(st, fcur, sc, tok0, cur.t_end, tok0 + CB * kBlockTokens > cur.t_end, lane);
-    if (last) finish_unit<T, D, G, CB>(st, a, cur, head0, lane);
+    if (last) finish_unit<T, D, G, CB>(st, a, cur, lane);
     if (nx.k < 0) return false;
     cur = nx;
     cursor_advance<CB>(nx, a, s_pre, stride);
@@ -788,7 +786,7 @@ int launch_decode(const DecodeArgs& args, int num_seqs, int dtype, int head_size
   const int G = next_pow2_group(args.group);
   DecodeKernel k = pick_decode(dtype, head_size, G);
   if (!k) return PA_ERR_UNSUPPORTED;
-  const int64_t grid = static_cast<int64_t>(num_seqs) * args.num_kv_heads * args.num_parts;
+  const int64_t grid = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * args.num_kv_heads;
   if (grid <= 0) return PA_OK;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const int W = waves_per_group();
@@ -841,12 +839,13 @@ int launch_units(const UnitArgs& args, int dtype, int head_size, hipStream_t str
   const size_t lds = args.prefix_in_lds ? (static_cast<size_t>(args.num_seqs) + 1) * sizeof(int) : 0;
   const int resident = resident_groups(reinterpret_cast<const void*>(k), lds);
   if (resident <= 0) return PA_ERR_HIP;
-  const int64_t waves_needed = static_cast<int64_t>(args.num_seqs) * args.num_parts;  // per kv head, upper bound
-  const int64_t groups_per_head_needed = (waves_needed + kUnitThreads / kWave - 1) / (kUnitThreads / kWave);
-  int64_t per_head = resident / args.num_kv_heads;
-  if (per_head < 1) per_head = 1;
-  if (per_head > groups_per_head_needed) per_head = groups_per_head_needed;
-  const int64_t grid = per_head * args.num_kv_heads;
+  // Persistent grid: as many workgroups as fit at once, a multiple of 8 (one
+  // per XCD in turn), and no more than the units can use.
+  const int64_t units = static_cast<int64_t>(args.num_seqs) * args.num_parts * args.num_kv_heads;  // upper bound
+  const int64_t useful = (units + kUnitThreads / kWave - 1) / (kUnitThreads / kWave);
+  int64_t grid = resident / 8 * 8;
+  if (grid > (useful + 7) / 8 * 8) grid = (useful + 7) / 8 * 8;
+  if (grid < 8) grid = 8;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kUnitThreads), lds, stream, args);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -914,7 +913,7 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                          int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
-                         float scale, int32_t dtype, float* lse_out, void* stream) {
+                         float scale, int32_t dtype, float* lse_out, const int32_t* seq_order, void* stream) {
   int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                         num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
   if (st != PA_OK || num_seqs == 0) return st;
@@ -926,13 +925,13 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   args.context_lens = context_lens;
   args.out = out;
   args.lse_out = lse_out;
+  args.seq_order = seq_order;
   args.num_blocks = num_blocks;
   args.max_blocks = max_blocks_per_seq;
+  args.num_seqs = num_seqs;
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;
   args.group = num_heads / num_kv_heads;
-  args.part_tokens = max_blocks_per_seq * kBlockTokens;
-  args.num_parts = 1;
   args.scale_log2 = scale * kLog2e;
   return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
 }

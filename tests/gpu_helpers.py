@@ -56,10 +56,12 @@ class Dev:
         self.bt = to_dev(inp.block_tables)
         self.cl = to_dev(inp.context_lens)
 
-    def decode(self, pa, lse=False):
+    def decode(self, pa, lse=False, seq_order=None):
         out = torch.empty_like(self.q)
         lse_t = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda") if lse else None
-        pa.pa_decode(out, self.q, self.kc, self.vc, self.bt, self.cl, self.cfg.scale, lse_out=lse_t)
+        order = None if seq_order is None else to_dev(np.asarray(seq_order, np.int32))
+        pa.pa_decode(out, self.q, self.kc, self.vc, self.bt, self.cl, self.cfg.scale, lse_out=lse_t,
+                     seq_order=order)
         return out, lse_t
 
     def decode_split(self, pa, partition_size=None, lse=False, max_context_len=None):

@@ -65,7 +65,7 @@ def _decode(lib, **kw):
              scale=0.1, dtype=1, lse=None)
     a.update(kw)
     return lib.pa_decode(a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["S"], a["Hq"],
-                         a["Hkv"], a["d"], a["NB"], a["bs"], a["scale"], a["dtype"], a["lse"], None)
+                         a["Hkv"], a["d"], a["NB"], a["bs"], a["scale"], a["dtype"], a["lse"], None, None)
 
 
 @pytest.mark.parametrize("kw,status", [

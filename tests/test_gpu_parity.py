@@ -214,6 +214,20 @@ def test_shared_prefix_equals_private_copies(pa):
     np.testing.assert_array_equal(bits(o1), bits(o2))
 
 
+def test_seq_order_is_only_a_schedule(pa):
+    cfg = W.CONFIG_BY_NAME["llama3_8b_b64"]
+    inp = W.make_inputs(cfg, mode="perf")
+    d = Dev(inp)
+    a, la = d.decode(pa, lse=True)
+    longest_first = np.argsort(-inp.context_lens, kind="stable")
+    b, lb = d.decode(pa, lse=True, seq_order=longest_first)
+    c, lc = d.decode(pa, lse=True, seq_order=np.random.default_rng(1).permutation(cfg.num_seqs))
+    torch.cuda.synchronize()
+    for o, l in ((b, lb), (c, lc)):
+        np.testing.assert_array_equal(bits(a), bits(o))
+        np.testing.assert_array_equal(bits(la), bits(l))
+
+
 def test_run_to_run_deterministic(pa):
     cfg = W.CONFIG_BY_NAME["prefix_70b"]
     inp = W.make_inputs(cfg, mode="perf")
