@@ -129,9 +129,11 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
 /*
  * pa_decode_split_workspace_bytes - workspace pa_decode_split needs.
  *
- * num_parts = ceil(max_context_len / partition_size); the workspace holds
- * float32 partials o_p [num_seqs, num_heads, num_parts, head_size] followed (at
- * a 256-byte aligned offset) by float32 lse_p [num_seqs, num_heads, num_parts].
+ * slots = ceil(max_context_len / partition_size) + 1. The workspace holds, each
+ * part at a 256-byte aligned offset: float32 partials o_p
+ * [num_seqs, num_heads, slots, head_size], float32 lse_p
+ * [num_seqs, num_heads, slots], and a header (int64 total_blocks, int64
+ * num_ranges, int32 block prefix [num_seqs + 1]) describing the pieces.
  * Returns 0 for invalid arguments.
  */
 size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
@@ -139,33 +141,35 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
 
 /*
  * pa_decode_split - the same result as pa_decode, computed over context
- * partitions and merged exactly.
+ * pieces spread evenly over the whole GPU and merged exactly.
  *
- * Partition p of sequence i covers positions [p*P, min((p+1)*P, n_i)),
- * P = partition_size, so sequence i has ceil(n_i / P) partitions. A first
- * kernel computes each partition's normalised output o_p and log-sum-exp
- * lse_p; the units (sequence, kv head, partition) are spread evenly over
- * persistent workers, so long and short contexts share the GPU evenly. A
- * second kernel on the same stream merges the partials of every sequence with
- * more than one partition (the log-sum-exp merge of pa_merge_partitions);
- * sequences with a single partition get their output from the first kernel
- * directly. The merge rests on the softmax normaliser identity the pages lean
- * on for streaming (stanleyjacob.dev "vLLM", Part V "The attention backend
- * dispatch layer": tiling plus online softmax); the partitioned form itself is
- * this library's reading.
+ * The blocks of all (sequence i, kv head h) pairs are laid end to end (pair
+ * index i * num_kv_heads + h, nb_i = ceil(n_i / block_size) blocks each,
+ * total_blocks T) and cut into num_ranges R equal contiguous ranges, one per
+ * persistent worker, so long and short contexts share the GPU evenly: range r
+ * is blocks [r*T/R, (r+1)*T/R). R is at most the number of resident workers
+ * and at most T / (partition_size / block_size), so every range spans at least
+ * partition_size tokens. The piece of pair (i, h) inside range r gets slot
+ * r - r0 (r0 the range of the pair's first block); its normalised output and
+ * log-sum-exp go to o_p / lse_p of the g = num_heads / num_kv_heads query
+ * heads of the pair. A pair that one range covers whole is written straight to
+ * `out`; a second kernel on the same stream merges the pieces of the others
+ * with the log-sum-exp rule of pa_merge_partitions. The merge rests on the
+ * softmax normaliser identity the pages lean on for streaming
+ * (stanleyjacob.dev "vLLM", Part V "The attention backend dispatch layer":
+ * tiling plus online softmax); this way of cutting the work is this library's.
  *
  *   max_context_len   host-side upper bound of context_lens (sizes the
- *                     partial buffers without reading the lengths back).
- *                     Positions past ceil(max_context_len/P)*P are ignored,
- *                     so it must be >= every length.
- *   partition_size    multiple of block_size, > 0.
+ *                     workspace without reading the lengths back). Positions
+ *                     past ceil(max_context_len / P) * P are ignored, so it
+ *                     must be >= every length.
+ *   partition_size    P: multiple of block_size, > 0; the shortest piece.
  *   workspace         device memory of at least
  *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
- *                     aligned, owned by the caller. Only the slots of
- *                     sequences with more than one partition are written
- *                     (o_p at [i][h][p][:], lse_p at [i][h][p] for p <
- *                     ceil(n_i/P)); the rest is left untouched.
+ *                     aligned, owned by the caller. Slots of pairs that are
+ *                     not cut are left untouched.
  *   lse_out           optional float32 [num_seqs, num_heads]; NULL to skip.
+ * num_seqs + 1 block counts must fit in 64 KiB of LDS (num_seqs <= 16383).
  * Other arguments as pa_decode. Returns PA_OK or an error status.
  */
 int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,

@@ -207,14 +207,23 @@ def pa_decode_split(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Ten
 
 def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head_size: int,
                     max_context_len: int, partition_size: int):
-    """(o_parts, lse_parts) float32 views into a pa_decode_split workspace."""
-    num_parts = max(1, -(-max_context_len // partition_size))
-    rows = num_seqs * num_heads * num_parts
-    o_bytes = (rows * head_size * 4 + 255) // 256 * 256
+    """Views into a pa_decode_split workspace after a call.
+
+    Returns (o_parts [S, H, slots, d] float32, lse_parts [S, H, slots] float32,
+    total_blocks, num_ranges, block_prefix [S + 1] int32): the partials and the
+    layout of the pieces the call used (see include/pa.h).
+    """
+    slots = -(-max_context_len // partition_size) + 1
+    rows = num_seqs * num_heads * slots
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    lse_off = a256(rows * head_size * 4)
+    hdr_off = lse_off + a256(rows * 4)
     f = workspace.view(torch.uint8)
-    o_parts = f[:rows * head_size * 4].view(torch.float32).view(num_seqs, num_heads, num_parts, head_size)
-    lse_parts = f[o_bytes:o_bytes + rows * 4].view(torch.float32).view(num_seqs, num_heads, num_parts)
-    return o_parts, lse_parts
+    o_parts = f[:rows * head_size * 4].view(torch.float32).view(num_seqs, num_heads, slots, head_size)
+    lse_parts = f[lse_off:lse_off + rows * 4].view(torch.float32).view(num_seqs, num_heads, slots)
+    hdr = f[hdr_off:hdr_off + 16].view(torch.int64).cpu()
+    prefix = f[hdr_off + 16:hdr_off + 16 + 4 * (num_seqs + 1)].view(torch.int32)
+    return o_parts, lse_parts, int(hdr[0]), int(hdr[1]), prefix
 
 
 def pa_merge_partitions(out: torch.Tensor, o_parts: torch.Tensor, lse_parts: torch.Tensor,

@@ -386,18 +386,22 @@ __global__ __launch_bounds__(256, 1) void paged_decode_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ partitioned path
-// Persistent wave workers. A unit of work is (sequence, partition of
-// part_tokens positions, kv head). Units are numbered partition by partition
-// (sequence i owns ceil(n_i / P) partitions) with the kv head fastest, and
-// unit k goes to worker k % workers, so every worker gets the same number of
-// units, all but the last partition of each sequence exactly P long. Worker
-// ids are laid out so that the kv heads of one partition run on the same XCD
-// (whole 2 KiB token rows per L2). A worker is one wave: it streams the chunks
-// of its units back to back with the next chunk (possibly of the next unit)
-// in flight, and closes each unit by writing that partition's normalised
-// output and log-sum-exp (or the final output when the sequence has a single
-// partition). No LDS traffic or barriers inside the loop.
-struct UnitArgs {
+// Persistent wave workers over an exactly balanced split of the work. The
+// blocks of all (sequence, kv head) pairs are laid end to end, pair
+// (i, h) at index i * H_kv + h (kv head fastest), and worker r of R takes the
+// contiguous range [r*T/R, (r+1)*T/R) of the T blocks, so every worker reads
+// the same number of blocks (to within one). Where a range cuts a pair, the
+// pair is covered by several pieces: each piece's normalised output and
+// log-sum-exp go to a workspace slot and a merge kernel combines them; a pair
+// that one worker covers whole is written straight to the output. R is capped
+// so that every range holds at least partition_size tokens, which bounds the
+// pieces of a sequence by ceil(n / partition_size) + 1.
+//
+// Workers of one XCD take consecutive ranges (the kv heads of a sequence run
+// side by side and each XCD reads whole token rows). A worker is one wave: it
+// streams its chunks back to back with the next chunk (possibly of the next
+// pair) in flight. No LDS traffic or barriers inside the loop.
+struct SplitArgs {
   const void* query;
   const void* key_cache;
   const void* value_cache;
@@ -405,114 +409,111 @@ struct UnitArgs {
   const int32_t* context_lens;
   void* out;
   float* lse_out;
-  float* o_parts;
-  float* lse_parts;
+  float* o_parts;     // [S, H_q, slots, D]
+  float* lse_parts;   // [S, H_q, slots]
+  int64_t* header;    // [0] T, [1] R; followed by int32 prefix of blocks per sequence [S + 1]
   int64_t num_blocks;
   int32_t max_blocks;
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t part_tokens;
-  int32_t num_parts;
-  int32_t prefix_in_lds;  // 1: per-sequence unit prefix sums in LDS; 0: fixed num_parts units per sequence
+  int32_t part_tokens;  // minimum piece length, multiple of 16
+  int32_t slots;        // ceil(max_context_len / part_tokens) + 1
   float scale_log2;
 };
 
-// Tokens of sequence `seq` that the partitioned path covers.
-__device__ __forceinline__ int covered_tokens(const int32_t* context_lens, int seq, int max_blocks,
-                                              int part_tokens, int num_parts) {
-  int n = context_lens[seq];
+// Tokens of a sequence the partitioned path covers: clamped to the block
+// table and to what the workspace slots can hold.
+__device__ __forceinline__ int split_tokens(const int32_t* context_lens, int seq, int max_blocks, int part_tokens,
+                                            int slots) {
+  const int n = context_lens[seq];
   const int64_t cap = min(static_cast<int64_t>(max_blocks) * kBlockTokens,
-                          static_cast<int64_t>(part_tokens) * num_parts);
+                          static_cast<int64_t>(part_tokens) * (slots - 1));
   return n < 0 ? 0 : static_cast<int>(n > cap ? cap : n);
 }
 
-struct UnitCursor {
-  int k;         // unit index, or -1 when the worker is done
-  int kvh;
-  int seq;
-  int part;
-  int nparts;    // partitions of this sequence
-  int t_end;     // exclusive end position of the unit
-  int blk0;      // first block of the unit
-  int blk_last;  // last block of the unit (inclusive)
-  int nchunk;
-  int c;         // chunk within the unit
+// Worker (range) holding flattened block x when T blocks are split into R ranges.
+__device__ __forceinline__ int64_t range_of(int64_t x, int64_t T, int64_t R) { return (x * R + R - 1) / T; }
+
+struct PieceCursor {
+  int64_t x;      // flattened index of the piece's first block; -1 when done
+  int64_t x_end;  // end of this worker's range
+  int seq, kvh;
+  int nb;         // blocks of the pair
+  int b_lo, b_hi; // piece = blocks [b_lo, b_hi) of the pair
+  int t_end;      // exclusive end position of the piece
+  int nchunk, c;
+  int slot;       // partial slot of this piece, -1 when the piece is the whole pair
 };
 
 template <int CB>
-__device__ __forceinline__ void cursor_set_unit(UnitCursor& u, const UnitArgs& a, const int* s_pre, int stride) {
-  // Find the next unit with work at or after u.k.
-  for (;;) {
-    const int pu = u.k / a.num_kv_heads;  // partition-unit (sequence, partition)
-    if (a.prefix_in_lds) {
-      const int total = __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
-      if (pu >= total) { u.k = -1; return; }
-      int lo = 0, hi = a.num_seqs;  // largest seq with s_pre[seq] <= pu
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= pu) lo = mid; else hi = mid;
-      }
-      u.seq = __builtin_amdgcn_readfirstlane(lo);
-      u.part = pu - __builtin_amdgcn_readfirstlane(s_pre[u.seq]);
-      u.nparts = __builtin_amdgcn_readfirstlane(s_pre[u.seq + 1]) + u.part - pu;
-    } else {
-      if (pu >= a.num_seqs * a.num_parts) { u.k = -1; return; }
-      u.seq = pu / a.num_parts;
-      u.part = pu - u.seq * a.num_parts;
-    }
-    u.kvh = u.k - pu * a.num_kv_heads;
-    const int n = __builtin_amdgcn_readfirstlane(
-        covered_tokens(a.context_lens, u.seq, a.max_blocks, a.part_tokens, a.num_parts));
-    const int t0 = u.part * a.part_tokens;
-    if (t0 < n) {
-      if (!a.prefix_in_lds) u.nparts = (n + a.part_tokens - 1) / a.part_tokens;
-      u.t_end = min(n, t0 + a.part_tokens);
-      u.blk0 = t0 / kBlockTokens;
-      u.blk_last = (u.t_end + kBlockTokens - 1) / kBlockTokens - 1;
-      u.nchunk = (u.blk_last - u.blk0 + CB) / CB;
-      u.c = 0;
-      return;
-    }
-    u.k += stride;  // empty unit (only without LDS prefix sums)
+__device__ __forceinline__ void cursor_set_piece(PieceCursor& u, const SplitArgs& a, const int* s_pre, int64_t T,
+                                                 int64_t R) {
+  if (u.x >= u.x_end) { u.x = -1; return; }
+  const int64_t H = a.num_kv_heads;
+  int lo = 0, hi = a.num_seqs;  // largest seq with H * s_pre[seq] <= x
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (H * __builtin_amdgcn_readfirstlane(s_pre[mid]) <= u.x) lo = mid; else hi = mid;
+  }
+  u.seq = __builtin_amdgcn_readfirstlane(lo);
+  const int pre = __builtin_amdgcn_readfirstlane(s_pre[u.seq]);
+  u.nb = __builtin_amdgcn_readfirstlane(s_pre[u.seq + 1]) - pre;
+  const int64_t within = u.x - H * pre;
+  u.kvh = static_cast<int>(within / u.nb);
+  u.b_lo = static_cast<int>(within - static_cast<int64_t>(u.kvh) * u.nb);
+  const int64_t left = u.x_end - u.x;
+  u.b_hi = static_cast<int>(min(static_cast<int64_t>(u.nb), u.b_lo + left));
+  const int n = __builtin_amdgcn_readfirstlane(
+      split_tokens(a.context_lens, u.seq, a.max_blocks, a.part_tokens, a.slots));
+  u.t_end = min(n, u.b_hi * kBlockTokens);
+  u.nchunk = (u.b_hi - u.b_lo + CB - 1) / CB;
+  u.c = 0;
+  if (u.b_lo == 0 && u.b_hi == u.nb) {
+    u.slot = -1;
+  } else {
+    const int64_t pair_start = u.x - u.b_lo;
+    u.slot = static_cast<int>(range_of(u.x, T, R) - range_of(pair_start, T, R));
   }
 }
 
 template <int CB>
-__device__ __forceinline__ void cursor_advance(UnitCursor& u, const UnitArgs& a, const int* s_pre, int stride) {
+__device__ __forceinline__ void cursor_next(PieceCursor& u, const SplitArgs& a, const int* s_pre, int64_t T,
+                                            int64_t R) {
   if (++u.c < u.nchunk) return;
-  u.k += stride;
-  cursor_set_unit<CB>(u, a, s_pre, stride);
+  u.x += u.b_hi - u.b_lo;
+  cursor_set_piece<CB>(u, a, s_pre, T, R);
 }
 
-// Close a unit: sum over row groups, normalise, write the partial (or the final
-// output). After the xor reduction every row group holds the totals, so row
+// Close a piece: sum over row groups, normalise, write the partial or the
+// final output. After the reduction every row group holds the totals, so row
 // group rg writes heads h with h % 4 == rg.
 template <typename T, int D, int G, int CB>
-__device__ __forceinline__ void finish_unit(WaveState<T, D, G, CB>& st, const UnitArgs& a, const UnitCursor& u,
-                                            int lane) {
-  const int head0 = u.kvh * a.group;
+__device__ __forceinline__ void finish_piece(WaveState<T, D, G, CB>& st, const SplitArgs& a, const PieceCursor& u,
+                                             int lane) {
   using S = DecodeShape<T, D, G, CB>;
+  const int head0 = u.kvh * a.group;
   const float l = rows_sum(st.l);
   const float lse_col = (st.m + fast_log2(l)) * kLn2;  // head lane % 16
   const int rg = lane >> 4;
   const int c = lane & 15;
+  const bool whole = u.slot < 0;
+  const bool slot_ok = u.slot < a.slots;  // always true by construction; guards the writes
   static_for<G>([&](auto hc) {
     constexpr int h = decltype(hc)::value;
-    const float Lh = row_bcast<h>(l);
-    const float inv = 1.f / Lh;
+    const float inv = 1.f / row_bcast<h>(l);
     float o[S::kVec];
 #pragma unroll
     for (int e = 0; e < S::kVec; ++e) o[e] = rows_sum(st.acc[h][e]) * inv;
     if ((h & 3) == rg && h < a.group) {
       const int64_t row = static_cast<int64_t>(u.seq) * a.num_heads + head0 + h;
-      if (u.nparts == 1) {
+      if (whole) {
         T* dst = static_cast<T*>(a.out) + row * D + c * S::kVec;
 #pragma unroll
         for (int e = 0; e < S::kVec; ++e) store_elem<T>(dst + e, o[e]);
-      } else {
-        float* dst = a.o_parts + (row * a.num_parts + u.part) * D + c * S::kVec;
+      } else if (slot_ok) {
+        float* dst = a.o_parts + (row * a.slots + u.slot) * D + c * S::kVec;
 #pragma unroll
         for (int e = 0; e < S::kVec; e += 4)
           *reinterpret_cast<f32x4_t*>(dst + e) = f32x4_t{o[e], o[e + 1], o[e + 2], o[e + 3]};
@@ -521,10 +522,10 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, G, CB>& st, const Un
   });
   if (rg == 0 && c < a.group) {
     const int64_t row = static_cast<int64_t>(u.seq) * a.num_heads + head0 + c;
-    if (u.nparts == 1) {
+    if (whole) {
       if (a.lse_out != nullptr) a.lse_out[row] = lse_col;
-    } else {
-      a.lse_parts[row * a.num_parts + u.part] = lse_col;
+    } else if (slot_ok) {
+      a.lse_parts[row * a.slots + u.slot] = lse_col;
     }
   }
   st.m = -__builtin_inff();
@@ -536,36 +537,31 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, G, CB>& st, const Un
 }
 
 template <typename T, int D, int G, int CB>
-__global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) {
+__global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a) {
   using S = DecodeShape<T, D, G, CB>;
-  extern __shared__ int s_pre[];  // [num_seqs + 1] when a.prefix_in_lds
+  extern __shared__ int s_pre[];  // [num_seqs + 1] blocks per sequence, exclusive prefix
+  __shared__ int s_run[256];
   const int lane = threadIdx.x & 63;
   // Wave-uniform by construction; readfirstlane lets the compiler keep all
-  // per-wave indexing (units, block ids, base addresses) in scalar registers.
+  // per-wave indexing (pieces, block ids, base addresses) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
-  // gridDim.x is a multiple of 8; workgroup b runs on XCD b % 8. Workers of
-  // one XCD get consecutive ids, so consecutive units (the kv heads of one
-  // partition) share an XCD.
-  const int stride = gridDim.x * nwaves;
-  const int worker = (blockIdx.x & 7) * (gridDim.x >> 3) * nwaves + (blockIdx.x >> 3) * nwaves + wave;
 
-  if (a.prefix_in_lds) {
-    // Exclusive prefix sum of units per sequence: thread t sums a contiguous
-    // run of sequences, then the run totals are scanned in LDS.
+  // Prefix sum of blocks per sequence: thread t sums a contiguous run of
+  // sequences, the run totals are scanned in LDS.
+  {
     const int per = (a.num_seqs + blockDim.x - 1) / blockDim.x;
     const int s0 = threadIdx.x * per;
     const int s1 = min(a.num_seqs, s0 + per);
     int run = 0;
     for (int i = s0; i < s1; ++i) {
-      const int n = covered_tokens(a.context_lens, i, a.max_blocks, a.part_tokens, a.num_parts);
-      run += (n + a.part_tokens - 1) / a.part_tokens;
+      const int n = split_tokens(a.context_lens, i, a.max_blocks, a.part_tokens, a.slots);
+      run += (n + kBlockTokens - 1) / kBlockTokens;
     }
-    __shared__ int s_run[256];
     s_run[threadIdx.x] = run;
     __syncthreads();
     for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
-      const int v = threadIdx.x >= static_cast<unsigned>(off) ? s_run[threadIdx.x - off] : 0;
+      const int v = static_cast<int>(threadIdx.x) >= off ? s_run[threadIdx.x - off] : 0;
       __syncthreads();
       s_run[threadIdx.x] += v;
       __syncthreads();
@@ -573,17 +569,46 @@ __global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) 
     int base = s_run[threadIdx.x] - run;
     for (int i = s0; i < s1; ++i) {
       s_pre[i] = base;
-      const int n = covered_tokens(a.context_lens, i, a.max_blocks, a.part_tokens, a.num_parts);
-      base += (n + a.part_tokens - 1) / a.part_tokens;
+      const int n = split_tokens(a.context_lens, i, a.max_blocks, a.part_tokens, a.slots);
+      base += (n + kBlockTokens - 1) / kBlockTokens;
     }
     if (threadIdx.x == blockDim.x - 1) s_pre[a.num_seqs] = s_run[threadIdx.x];
     __syncthreads();
   }
 
-  UnitCursor cur;
-  cur.k = worker;
-  cursor_set_unit<CB>(cur, a, s_pre, stride);
-  if (cur.k < 0) return;
+  const int64_t nblk = static_cast<int64_t>(a.num_kv_heads) * __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
+  // Ranges: at least part_tokens per range, a multiple of 8 when possible
+  // (XCD x takes ranges [x*R/8, (x+1)*R/8)).
+  const int64_t launched = static_cast<int64_t>(gridDim.x) * nwaves;
+  int64_t R = min(launched, nblk / (a.part_tokens / kBlockTokens));
+  if (R >= 8) R = R / 8 * 8;
+  if (R < 1) R = 1;
+  if (blockIdx.x == 0) {
+    // Layout of the pieces, for the merge kernel.
+    if (threadIdx.x == 0) {
+      a.header[0] = nblk;
+      a.header[1] = R;
+    }
+    int* pre_out = reinterpret_cast<int*>(a.header + 2);
+    for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) pre_out[i] = s_pre[i];
+  }
+  if (nblk == 0) return;
+  const int xcd = blockIdx.x & 7;
+  const int local = (blockIdx.x >> 3) * nwaves + wave;  // worker index within its XCD
+  int64_t r;
+  if (R >= 8) {
+    if (local >= R / 8) return;
+    r = xcd * (R / 8) + local;
+  } else {
+    r = static_cast<int64_t>(blockIdx.x) * nwaves + wave;
+    if (r >= R) return;
+  }
+
+  PieceCursor cur;
+  cur.x = r * nblk / R;
+  cur.x_end = (r + 1) * nblk / R;
+  cursor_set_piece<CB>(cur, a, s_pre, nblk, R);
+  if (cur.x < 0) return;
 
   const int g = a.group;
   const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
@@ -604,61 +629,67 @@ __global__ __launch_bounds__(256, 2) void paged_decode_units_kernel(UnitArgs a) 
   u32x4_t q[S::kKSeg];
   load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
   Chunk<T, D, G, CB> fa, fb;
-  load_chunk<T, D, G, CB>(fa, kc, vc, bt_row(cur.seq), cur.blk0, cur.blk_last, a.num_blocks, tok_stride,
+  load_chunk<T, D, G, CB>(fa, kc, vc, bt_row(cur.seq), cur.b_lo, cur.b_hi - 1, a.num_blocks, tok_stride,
                           blk_stride, head_off(cur.kvh), lane);
-  UnitCursor nx = cur;
-  cursor_advance<CB>(nx, a, s_pre, stride);
+  PieceCursor nx = cur;
+  cursor_next<CB>(nx, a, s_pre, nblk, R);
 
   auto step = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
-    if (nx.k >= 0)
-      load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.blk0 + nx.c * CB, nx.blk_last, a.num_blocks,
+    if (nx.x >= 0)
+      load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.b_lo + nx.c * CB, nx.b_hi - 1, a.num_blocks,
                               tok_stride, blk_stride, head_off(nx.kvh), lane);
-    const int tok0 = (cur.blk0 + cur.c * CB) * kBlockTokens;
+    const int tok0 = (cur.b_lo + cur.c * CB) * kBlockTokens;
     const bool last = cur.c == cur.nchunk - 1;
     float sc[CB][4];
     qk_chunk<T, D, G, CB>(sc, fcur, q, a.scale_log2);
-    // The query of the next unit is fetched as soon as this unit's last
+    // The query of the next piece is fetched as soon as this piece's last
     // scores are out, so its latency hides behind the P*V work.
-    if (last && nx.k >= 0) load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, nx.kvh * g, g, lane, q);
+    if (last && nx.x >= 0) load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, nx.kvh * g, g, lane, q);
     softmax_pv_chunk<T, D, G, CB>(st, fcur, sc, tok0, cur.t_end, tok0 + CB * kBlockTokens > cur.t_end, lane);
-    if (last) finish_unit<T, D, G, CB>(st, a, cur, lane);
-    if (nx.k < 0) return false;
+    if (last) finish_piece<T, D, G, CB>(st, a, cur, lane);
+    if (nx.x < 0) return false;
     cur = nx;
-    cursor_advance<CB>(nx, a, s_pre, stride);
+    cursor_next<CB>(nx, a, s_pre, nblk, R);
     return true;
   };
   while (step(fa, fb) && step(fb, fa)) {
   }
 }
 
-// Merge for the partitioned path: row (sequence, head) combines the
-// ceil(n / P) partitions the unit kernel wrote. Sequences with one partition
-// were written directly by the unit kernel; an empty context gives 0 / -inf.
+// Merge for the partitioned path: row (sequence, head) combines the pieces its
+// (sequence, kv head) pair was cut into. Pairs covered by one piece were
+// written directly by the split kernel; an empty context gives 0 / -inf.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_units_kernel(T* __restrict__ out, float* __restrict__ lse_out,
-                                                          const float* __restrict__ o_parts,
-                                                          const float* __restrict__ lse_parts,
-                                                          const int32_t* __restrict__ context_lens, int num_seqs,
-                                                          int num_heads, int max_blocks, int part_tokens,
-                                                          int num_parts) {
+__global__ __launch_bounds__(256) void merge_pieces_kernel(T* __restrict__ out, float* __restrict__ lse_out,
+                                                           const float* __restrict__ o_parts,
+                                                           const float* __restrict__ lse_parts,
+                                                           const int64_t* __restrict__ header, int num_seqs,
+                                                           int num_heads, int num_kv_heads, int slots) {
   constexpr int kPer = D / kWave;
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= static_cast<int64_t>(num_seqs) * num_heads) return;
   const int seq = static_cast<int>(row / num_heads);
-  const int n = covered_tokens(context_lens, seq, max_blocks, part_tokens, num_parts);
-  const int np = (n + part_tokens - 1) / part_tokens;
+  const int kvh = static_cast<int>(row - static_cast<int64_t>(seq) * num_heads) / (num_heads / num_kv_heads);
+  const int64_t nblk = header[0];
+  const int64_t R = header[1];
+  const int* pre = reinterpret_cast<const int*>(header + 2);
+  const int nb = pre[seq + 1] - pre[seq];
+  int np = 0;
+  if (nb > 0) {
+    const int64_t x0 = static_cast<int64_t>(num_kv_heads) * pre[seq] + static_cast<int64_t>(kvh) * nb;
+    np = static_cast<int>(range_of(x0 + nb - 1, nblk, R) - range_of(x0, nblk, R)) + 1;
+  }
   if (np == 1) return;
-  const float* lp = lse_parts + row * num_parts;
+  if (np > slots) np = slots;
+  const float* lp = lse_parts + row * slots;
   float M = -__builtin_inff();
-  for (int p = lane; p < np; p += kWave) M = fmaxf(M, lp[p]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
+  for (int p = 0; p < np; ++p) M = fmaxf(M, lp[p]);
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float L = 0.f;
-  const float* op = o_parts + row * num_parts * D + lane * kPer;
+  const float* op = o_parts + row * slots * D + lane * kPer;
   for (int p = 0; p < np; ++p) {
     const float w = fast_exp2((lp[p] - M) * kLog2e);
     L += w;
@@ -795,80 +826,75 @@ int launch_decode(const DecodeArgs& args, int num_seqs, int dtype, int head_size
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-typedef void (*UnitKernel)(UnitArgs);
+typedef void (*SplitKernel)(SplitArgs);
 
 template <typename T, int D, int G>
-UnitKernel unit_kernel_for() {
+SplitKernel split_kernel_for() {
   using P = Policy<T, D, G>;
-  return paged_decode_units_kernel<T, D, G, P::CB>;
+  return paged_decode_split_kernel<T, D, G, P::CB>;
 }
 
 template <typename T, int D>
-UnitKernel pick_unit_group(int G) {
+SplitKernel pick_split_group(int G) {
   switch (G) {
-    case 1: return unit_kernel_for<T, D, 1>();
-    case 2: return unit_kernel_for<T, D, 2>();
-    case 4: return unit_kernel_for<T, D, 4>();
-    case 8: return unit_kernel_for<T, D, 8>();
-    case 16: return unit_kernel_for<T, D, 16>();
+    case 1: return split_kernel_for<T, D, 1>();
+    case 2: return split_kernel_for<T, D, 2>();
+    case 4: return split_kernel_for<T, D, 4>();
+    case 8: return split_kernel_for<T, D, 8>();
+    case 16: return split_kernel_for<T, D, 16>();
     default: return nullptr;
   }
 }
 
-UnitKernel pick_unit(int dtype, int D, int G) {
-  if (dtype == PA_DTYPE_BF16) return D == 128 ? pick_unit_group<bf16_t, 128>(G) : pick_unit_group<bf16_t, 64>(G);
-  return D == 128 ? pick_unit_group<float, 128>(G) : pick_unit_group<float, 64>(G);
+SplitKernel pick_split(int dtype, int D, int G) {
+  if (dtype == PA_DTYPE_BF16) return D == 128 ? pick_split_group<bf16_t, 128>(G) : pick_split_group<bf16_t, 64>(G);
+  return D == 128 ? pick_split_group<float, 128>(G) : pick_split_group<float, 64>(G);
 }
 
-constexpr int kUnitThreads = 256;
-constexpr int kMaxLdsSeqs = 8192;
+constexpr int kSplitThreads = 256;
 
-// Workgroups that fit on the device at once for `kernel` (persistent grid size).
+// Workgroups of `kernel` that fit on the device at once (persistent grid size).
 int resident_groups(const void* kernel, size_t lds) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kUnitThreads, lds) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, lds) != hipSuccess) return 0;
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
-int launch_units(const UnitArgs& args, int dtype, int head_size, hipStream_t stream) {
+int launch_split(const SplitArgs& args, int dtype, int head_size, hipStream_t stream) {
   const int G = next_pow2_group(args.group);
-  UnitKernel k = pick_unit(dtype, head_size, G);
+  SplitKernel k = pick_split(dtype, head_size, G);
   if (!k) return PA_ERR_UNSUPPORTED;
-  const size_t lds = args.prefix_in_lds ? (static_cast<size_t>(args.num_seqs) + 1) * sizeof(int) : 0;
+  const size_t lds = (static_cast<size_t>(args.num_seqs) + 1) * sizeof(int);
   const int resident = resident_groups(reinterpret_cast<const void*>(k), lds);
   if (resident <= 0) return PA_ERR_HIP;
   // Persistent grid: as many workgroups as fit at once, a multiple of 8 (one
-  // per XCD in turn), and no more than the units can use.
-  const int64_t units = static_cast<int64_t>(args.num_seqs) * args.num_parts * args.num_kv_heads;  // upper bound
-  const int64_t useful = (units + kUnitThreads / kWave - 1) / (kUnitThreads / kWave);
+  // per XCD in turn), and no more than the work can use.
+  const int64_t blocks_bound = static_cast<int64_t>(args.num_seqs) * args.max_blocks * args.num_kv_heads;
+  const int64_t ranges_bound = blocks_bound / (args.part_tokens / kBlockTokens) + 1;
+  const int64_t useful = (ranges_bound + kSplitThreads / kWave - 1) / (kSplitThreads / kWave);
   int64_t grid = resident / 8 * 8;
   if (grid > (useful + 7) / 8 * 8) grid = (useful + 7) / 8 * 8;
   if (grid < 8) grid = 8;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kUnitThreads), lds, stream, args);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
-int launch_merge_units(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
-                       const int32_t* context_lens, int num_seqs, int num_heads, int max_blocks, int part_tokens,
-                       int num_parts, int head_size, int dtype, hipStream_t stream) {
-  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
-  if (rows <= 0) return PA_OK;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kSplitThreads), lds, stream, args);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  const int64_t rows = static_cast<int64_t>(args.num_seqs) * args.num_heads;
   constexpr int kRowsPerBlock = 4;
-  const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
-#define PA_MERGE_UNITS(TT, DD)                                                                                    \
-  hipLaunchKernelGGL((merge_units_kernel<TT, DD>), g, b, 0, stream, static_cast<TT*>(out), lse_out, o_parts,     \
-                     lse_parts, context_lens, num_seqs, num_heads, max_blocks, part_tokens, num_parts)
+  const int64_t mgrid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (mgrid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  dim3 g(static_cast<unsigned>(mgrid)), b(kRowsPerBlock * kWave);
+#define PA_MERGE_PIECES(TT, DD)                                                                                    \
+  hipLaunchKernelGGL((merge_pieces_kernel<TT, DD>), g, b, 0, stream, static_cast<TT*>(args.out), args.lse_out,   \
+                     args.o_parts, args.lse_parts, args.header, args.num_seqs, args.num_heads, args.num_kv_heads, \
+                     args.slots)
   if (dtype == PA_DTYPE_BF16) {
-    if (head_size == 128) PA_MERGE_UNITS(bf16_t, 128); else PA_MERGE_UNITS(bf16_t, 64);
+    if (head_size == 128) PA_MERGE_PIECES(bf16_t, 128); else PA_MERGE_PIECES(bf16_t, 64);
   } else {
-    if (head_size == 128) PA_MERGE_UNITS(float, 128); else PA_MERGE_UNITS(float, 64);
+    if (head_size == 128) PA_MERGE_PIECES(float, 128); else PA_MERGE_PIECES(float, 64);
   }
-#undef PA_MERGE_UNITS
+#undef PA_MERGE_PIECES
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -899,10 +925,6 @@ int launch_merge(void* out, float* lse_out, const float* o_parts, const float* l
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-int64_t split_parts(int32_t max_context_len, int32_t partition_size) {
-  const int64_t np = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
-  return np < 1 ? 1 : np;
-}
 
 }  // namespace
 }  // namespace pa
@@ -936,11 +958,29 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
 }
 
+// Workspace layout: o_p [S, H_q, slots, D] float32 | lse_p [S, H_q, slots]
+// float32 | header: int64 T, int64 R, int32 blocks prefix [S + 1]; each part
+// 256-byte aligned.
+struct SplitLayout {
+  int64_t slots = 0;
+  size_t lse_off = 0, header_off = 0, total = 0;
+};
+
+bool split_layout(int32_t num_seqs, int32_t num_heads, int32_t head_size, int32_t max_context_len,
+                  int32_t partition_size, SplitLayout& L) {
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0 || partition_size <= 0) return false;
+  L.slots = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size + 1;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * static_cast<size_t>(L.slots);
+  L.lse_off = align256(rows * head_size * sizeof(float));
+  L.header_off = L.lse_off + align256(rows * sizeof(float));
+  L.total = L.header_off + align256(2 * sizeof(int64_t) + (static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t));
+  return L.slots <= INT32_MAX;
+}
+
 extern "C" size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                                   int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0 || partition_size <= 0) return 0;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * split_parts(max_context_len, partition_size);
-  return align256(rows * head_size * sizeof(float)) + align256(rows * sizeof(float));
+  SplitLayout L;
+  return split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size, L) ? L.total : 0;
 }
 
 extern "C" int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -955,17 +995,13 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
   if (st != PA_OK) return st;
   if (partition_size <= 0 || partition_size % kBlockTokens != 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
-  const size_t need = pa_decode_split_workspace_bytes(num_seqs, num_heads, head_size, max_context_len,
-                                                      partition_size);
+  SplitLayout L;
+  if (!split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size, L)) return PA_ERR_UNSUPPORTED;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
-  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
-  const int64_t np = split_parts(max_context_len, partition_size);
-  if (np > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * np;
-  float* o_parts = static_cast<float*>(workspace);
-  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * head_size * sizeof(float)));
+  if (workspace_bytes < L.total) return PA_ERR_WORKSPACE;
+  if ((static_cast<size_t>(num_seqs) + 1) * sizeof(int) > 64 * 1024) return PA_ERR_UNSUPPORTED;  // LDS prefix
 
-  UnitArgs args{};
+  SplitArgs args{};
   args.query = query;
   args.key_cache = key_cache;
   args.value_cache = value_cache;
@@ -973,8 +1009,9 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
   args.context_lens = context_lens;
   args.out = out;
   args.lse_out = lse_out;
-  args.o_parts = o_parts;
-  args.lse_parts = lse_parts;
+  args.o_parts = static_cast<float*>(workspace);
+  args.lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_off);
+  args.header = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + L.header_off);
   args.num_blocks = num_blocks;
   args.max_blocks = max_blocks_per_seq;
   args.num_seqs = num_seqs;
@@ -982,13 +1019,9 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
   args.num_kv_heads = num_kv_heads;
   args.group = num_heads / num_kv_heads;
   args.part_tokens = partition_size;
-  args.num_parts = static_cast<int32_t>(np);
-  args.prefix_in_lds = num_seqs <= kMaxLdsSeqs ? 1 : 0;
+  args.slots = static_cast<int32_t>(L.slots);
   args.scale_log2 = scale * kLog2e;
-  st = launch_units(args, dtype, head_size, static_cast<hipStream_t>(stream));
-  if (st != PA_OK) return st;
-  return launch_merge_units(out, lse_out, o_parts, lse_parts, context_lens, num_seqs, num_heads, max_blocks_per_seq,
-                            partition_size, static_cast<int>(np), head_size, dtype, static_cast<hipStream_t>(stream));
+  return launch_split(args, dtype, head_size, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int pa_merge_partitions(void* out, float* lse_out, const float* o_parts, const float* lse_parts,

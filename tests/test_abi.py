@@ -48,10 +48,12 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     f = lib.pa_decode_split_workspace_bytes
-    # 8 seqs x 32 heads x ceil(32768/512)=64 partitions: o_p (x128 floats) + lse_p, 256-aligned.
-    rows = 8 * 32 * 64
-    assert f(8, 32, 128, 32768, 512) == rows * 128 * 4 + rows * 4
-    assert f(4, 4, 64, 100, 32) == ((4 * 4 * 4 * 64 * 4 + 255) // 256) * 256 + 256
+    a = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    # 8 seqs x 32 heads x (ceil(32768/512) + 1) slots: o_p, lse_p, header, each 256-aligned.
+    rows = 8 * 32 * 65
+    assert f(8, 32, 128, 32768, 512) == a(rows * 128 * 4) + a(rows * 4) + a(16 + 9 * 4)
+    rows = 4 * 4 * 5
+    assert f(4, 4, 64, 100, 32) == a(rows * 64 * 4) + a(rows * 4) + a(16 + 5 * 4)
     assert f(1, 1, 64, 0, 16) > 0          # at least one partition
     assert f(1, 1, 64, 10, 0) == 0         # invalid partition size
     assert f(-1, 1, 64, 10, 16) == 0

@@ -53,21 +53,51 @@ def test_workload_reshape_then_decode(pa, cfg):
     assert e1 <= TOL[cfg.dtype] and e2 <= TOL[cfg.dtype]
     assert l1 <= LSE_TOL[cfg.dtype] and l2 <= LSE_TOL[cfg.dtype]
 
-    # The partials in the workspace are the per-partition attention results
-    # (written for sequences that span more than one partition).
-    P = cfg.partition_size
-    num_parts = max(1, -(-inp.max_context_len // P))
-    multi = [i for i in range(cfg.num_seqs) if -(-int(inp.context_lens[i]) // P) > 1][:8]
-    if multi:
-        o_parts, lse_parts = pa.workspace_views(ws, cfg.num_seqs, cfg.num_heads, cfg.head_size,
-                                                inp.max_context_len, P)
-        ro, rl = oracle.paged_decode_partitions(inp.query, ref_k, ref_v, inp.block_tables, inp.context_lens,
-                                                cfg.scale, cfg.dtype, P, num_parts, seqs=multi)
-        go, gl = f64(o_parts), f64(lse_parts)
-        for i in multi:
-            npi = -(-int(inp.context_lens[i]) // P)
-            assert np.abs(gl[i, :, :npi] - rl[i, :, :npi]).max() <= LSE_TOL[cfg.dtype]
-            assert np.abs(go[i, :, :npi] - ro[i, :, :npi]).max() <= PART_TOL[cfg.dtype]
+    check_split_pieces(pa, cfg, inp, ref_k, ref_v, ws, cfg.partition_size)
+
+
+def check_split_pieces(pa, cfg, inp, kc, vc, ws, P, max_pairs=24):
+    """The workspace pieces of pa_decode_split against the oracle, piece by piece.
+
+    The header gives the cut (T blocks, R ranges, per-sequence block prefix);
+    each piece of a cut pair must hold attention over exactly its token range.
+    """
+    S, Hq, Hkv, d = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size
+    g = Hq // Hkv
+    o_parts, lse_parts, T, R, prefix = pa.workspace_views(ws, S, Hq, d, inp.max_context_len, P)
+    n = inp.context_lens.astype(np.int64)
+    nb = (n + 15) // 16
+    np.testing.assert_array_equal(prefix.cpu().numpy(), np.concatenate([[0], np.cumsum(nb)]))
+    assert T == Hkv * nb.sum() and 1 <= R
+    assert R <= max(1, T // (P // 16))
+    rng_of = lambda x: (x * R + R - 1) // T  # noqa: E731
+    go, gl = f64(o_parts), f64(lse_parts)
+    q = oracle.decode_values(inp.query, cfg.dtype)
+    checked = 0
+    for i in range(S):
+        for h in range(Hkv):
+            x0 = Hkv * int(prefix[i]) + h * int(nb[i])
+            if nb[i] == 0:
+                continue
+            r0, r1 = rng_of(x0), rng_of(x0 + int(nb[i]) - 1)
+            if r0 == r1:
+                continue
+            Kc, Vc = oracle.gather_context(kc, vc, inp.block_tables[i], int(n[i]), 16)
+            Kf, Vf = oracle.decode_values(Kc, cfg.dtype), oracle.decode_values(Vc, cfg.dtype)
+            for r in range(r0, r1 + 1):
+                lo = max(x0, r * T // R) - x0
+                hi = min(x0 + int(nb[i]), (r + 1) * T // R) - x0
+                assert hi - lo >= 1
+                t0, t1 = lo * 16, min(hi * 16, int(n[i]))
+                ro, rl = oracle.attention_contiguous(q[i, h * g:(h + 1) * g], Kf[t0:t1, h:h + 1],
+                                                     Vf[t0:t1, h:h + 1], cfg.scale)
+                j = r - r0
+                assert np.abs(go[i, h * g:(h + 1) * g, j] - ro).max() <= PART_TOL[cfg.dtype]
+                assert np.abs(gl[i, h * g:(h + 1) * g, j] - rl).max() <= LSE_TOL[cfg.dtype]
+            checked += 1
+            if checked >= max_pairs:
+                return checked
+    return checked
 
 
 # --------------------------------------------------------------- shape sweep, ragged tails
@@ -95,6 +125,20 @@ def test_shape_sweep(pa, dtype, d_h, Hq, Hkv):
     for o, l in outs:
         assert max_err(o, ref) <= TOL[dtype]
         assert max_err(l, ref_lse) <= LSE_TOL[dtype]
+
+
+def test_split_pieces_long_contexts(pa):
+    cfg = W.small_case("pieces", 5, 16, 4, 128, "bf16", ("uniform", 900, 3000), seed=31, num_blocks=1200,
+                       partition_size=64)
+    inp = W.make_inputs(cfg)
+    d = Dev(inp)
+    for P in (16, 64, 256):
+        out, lse, ws = d.decode_split(pa, partition_size=P, lse=True)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                                           inp.context_lens, cfg.scale, cfg.dtype)
+        assert max_err(out, ref) <= TOL["bf16"] and max_err(lse, ref_lse) <= LSE_TOL["bf16"]
+        assert check_split_pieces(pa, cfg, inp, inp.key_cache, inp.value_cache, ws, P, max_pairs=8) >= 1
 
 
 # --------------------------------------------------------------- closed forms, bit-exact
