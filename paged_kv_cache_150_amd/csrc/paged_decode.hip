@@ -656,6 +656,66 @@ __global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a)
   }
 }
 
+// Log-sum-exp merge of np partials of one (sequence, head) row by one wave:
+// lane p holds lse_p (lanes stride over p when np > 64), the weights
+// 2^(lse_p - M) are broadcast through LDS and every lane accumulates its
+// head_size/64 output elements with eight partial loads in flight.
+// Partitions at -inf get weight 0 and their o_p is never read.
+template <typename T, int D>
+__device__ __forceinline__ void merge_row(T* out, float* lse_out, const float* o_row, const float* lse_row, int np,
+                                          int lane) {
+  constexpr int kPer = D / kWave;
+  __shared__ float s_w[4][kWave];
+  const int wv = (threadIdx.x >> 6) & 3;
+  float M = -__builtin_inff();
+  for (int p = lane; p < np; p += kWave) M = fmaxf(M, lse_row[p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int p0 = 0; p0 < np; p0 += kWave) {
+      const int p = p0 + lane;
+      const float lv = p < np ? lse_row[p] : -__builtin_inff();
+      const float w = lv == -__builtin_inff() ? 0.f : fast_exp2((lv - M) * kLog2e);
+      float wsum = w;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) wsum += xor_shfl(wsum, off);
+      L += wsum;
+      s_w[wv][lane] = w;
+      __builtin_amdgcn_wave_barrier();
+      const int cnt = min(kWave, np - p0);
+      const float* op = o_row + static_cast<int64_t>(p0) * D + lane * kPer;
+      int i = 0;
+      for (; i + 8 <= cnt; i += 8) {
+        float v[8][kPer];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) v[u][e] = s_w[wv][i + u] > 0.f ? op[(i + u) * D + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) acc[e] = fmaf(s_w[wv][i + u], v[u][e], acc[e]);
+      }
+      for (; i < cnt; ++i) {
+        const float wi = s_w[wv][i];
+        if (wi > 0.f) {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) acc[e] = fmaf(wi, op[i * D + e], acc[e]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  const bool empty = (M == -__builtin_inff());
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_elem<T>(out + lane * kPer + e, empty ? 0.f : acc[e] / L);
+  if (lse_out != nullptr && lane == 0) *lse_out = empty ? -__builtin_inff() : M + fast_log2(L) * kLn2;
+}
+
 // Merge for the partitioned path: row (sequence, head) combines the pieces its
 // (sequence, kv head) pair was cut into. Pairs covered by one piece were
 // written directly by the split kernel; an empty context gives 0 / -inf.
@@ -682,24 +742,8 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(T* __restrict__ out, 
   }
   if (np == 1) return;
   if (np > slots) np = slots;
-  const float* lp = lse_parts + row * slots;
-  float M = -__builtin_inff();
-  for (int p = 0; p < np; ++p) M = fmaxf(M, lp[p]);
-  float acc[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  const float* op = o_parts + row * slots * D + lane * kPer;
-  for (int p = 0; p < np; ++p) {
-    const float w = fast_exp2((lp[p] - M) * kLog2e);
-    L += w;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, op[p * D + e], acc[e]);
-  }
-  const bool empty = (np == 0);
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) store_elem<T>(out + row * D + lane * kPer + e, empty ? 0.f : acc[e] / L);
-  if (lse_out != nullptr && lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + fast_log2(L) * kLn2;
+  merge_row<T, D>(out + row * D, lse_out != nullptr ? lse_out + row : nullptr, o_parts + row * slots * D,
+                  lse_parts + row * slots, np, lane);
 }
 
 // One wave per (sequence, head) row: out = sum_p w_p o_p / sum_p w_p with
@@ -709,34 +753,11 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(T* __restrict__ o
                                                                const float* __restrict__ o_parts,
                                                                const float* __restrict__ lse_parts,
                                                                int64_t num_rows, int num_parts) {
-  constexpr int kPer = D / kWave;
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= num_rows) return;
-  const float* lp = lse_parts + row * num_parts;
-  float M = -__builtin_inff();
-  for (int p = lane; p < num_parts; p += kWave) M = fmaxf(M, lp[p]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
-  float acc[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  if (M != -__builtin_inff()) {
-    const float* op = o_parts + row * num_parts * D + lane * kPer;
-    for (int p = 0; p < num_parts; ++p) {
-      const float lv = lp[p];
-      if (lv == -__builtin_inff()) continue;
-      const float w = fast_exp2((lv - M) * kLog2e);
-      L += w;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, op[p * D + e], acc[e]);
-    }
-  }
-  const bool empty = (M == -__builtin_inff());
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) store_elem<T>(out + row * D + lane * kPer + e, empty ? 0.f : acc[e] / L);
-  if (lse_out != nullptr && lane == 0) lse_out[row] = empty ? -__builtin_inff() : M + fast_log2(L) * kLn2;
+  merge_row<T, D>(out + row * D, lse_out != nullptr ? lse_out + row : nullptr, o_parts + row * num_parts * D,
+                  lse_parts + row * num_parts, num_parts, lane);
 }
 
 // ------------------------------------------------------------------ host side
