@@ -143,16 +143,18 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * pa_decode_split - the same result as pa_decode, computed over context
  * pieces spread evenly over the whole GPU and merged exactly.
  *
- * The blocks of all (sequence i, kv head h) pairs are laid end to end (pair
- * index i * num_kv_heads + h, nb_i = ceil(n_i / block_size) blocks each,
- * total_blocks T) and cut into num_ranges R equal contiguous ranges, one per
- * persistent worker, so long and short contexts share the GPU evenly: range r
- * is blocks [r*T/R, (r+1)*T/R). R is at most the number of resident workers
+ * The kv heads are taken in groups of up to 8 (one persistent workgroup has
+ * one wave per kv head of its group, all walking the same blocks). Per head
+ * group, the blocks of all sequences are laid end to end (sequence i has
+ * nb_i = ceil(n_i / block_size) blocks; total_blocks T = groups * sum nb_i,
+ * group-major) and cut into num_ranges R equal contiguous ranges, one per
+ * workgroup, so long and short contexts share the GPU evenly: range r is
+ * blocks [r*T/R, (r+1)*T/R). R is at most the number of resident workgroups
  * and at most T / (partition_size / block_size), so every range spans at least
- * partition_size tokens. The piece of pair (i, h) inside range r gets slot
- * r - r0 (r0 the range of the pair's first block); its normalised output and
- * log-sum-exp go to o_p / lse_p of the g = num_heads / num_kv_heads query
- * heads of the pair. A pair that one range covers whole is written straight to
+ * partition_size tokens. The piece of (sequence i, head group) inside range r
+ * gets slot r - r0 (r0 the range of the sequence's first block); its
+ * normalised output and log-sum-exp go to o_p / lse_p of the query heads of
+ * that group. A sequence that one range covers whole is written straight to
  * `out`; a second kernel on the same stream merges the pieces of the others
  * with the log-sum-exp rule of pa_merge_partitions. The merge rests on the
  * softmax normaliser identity the pages lean on for streaming
@@ -166,8 +168,8 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  *   partition_size    P: multiple of block_size, > 0; the shortest piece.
  *   workspace         device memory of at least
  *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
- *                     aligned, owned by the caller. Slots of pairs that are
- *                     not cut are left untouched.
+ *                     aligned, owned by the caller. Slots of sequences
+ *                     that are not cut are left untouched.
  *   lse_out           optional float32 [num_seqs, num_heads]; NULL to skip.
  * num_seqs + 1 block counts must fit in 64 KiB of LDS (num_seqs <= 16383).
  * Other arguments as pa_decode. Returns PA_OK or an error status.

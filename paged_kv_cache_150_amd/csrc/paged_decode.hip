@@ -386,21 +386,22 @@ __global__ __launch_bounds__(256, 1) void paged_decode_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ partitioned path
-// Persistent wave workers over an exactly balanced split of the work. The
-// blocks of all (sequence, kv head) pairs are laid end to end, pair
-// (i, h) at index i * H_kv + h (kv head fastest), and worker r of R takes the
-// contiguous range [r*T/R, (r+1)*T/R) of the T blocks, so every worker reads
-// the same number of blocks (to within one). Where a range cuts a pair, the
-// pair is covered by several pieces: each piece's normalised output and
-// log-sum-exp go to a workspace slot and a merge kernel combines them; a pair
-// that one worker covers whole is written straight to the output. R is capped
-// so that every range holds at least partition_size tokens, which bounds the
-// pieces of a sequence by ceil(n / partition_size) + 1.
-//
-// Workers of one XCD take consecutive ranges (the kv heads of a sequence run
-// side by side and each XCD reads whole token rows). A worker is one wave: it
-// streams its chunks back to back with the next chunk (possibly of the next
-// pair) in flight. No LDS traffic or barriers inside the loop.
+// Persistent workgroups over an exactly balanced split of the work. A
+// workgroup has one wave per kv head of a head group (up to 8 kv heads); its
+// waves walk the same blocks at the same time, each computing its own kv head,
+// so a CU reads whole token rows of every block it touches (2 KiB for 8 kv
+// heads of 128 bf16). The blocks of all sequences are laid end to end, per
+// head group, and workgroup r of R takes the contiguous range
+// [r*T/R, (r+1)*T/R) of the T blocks: every workgroup reads the same amount
+// (to within one block). Where a range cuts a sequence, each piece's
+// normalised output and log-sum-exp go to a workspace slot and a merge kernel
+// combines them; a sequence that one range covers whole is written straight to
+// the output. R is capped so that every range holds at least partition_size
+// tokens, which bounds the pieces of a sequence by ceil(n / partition_size) + 1.
+// Each wave streams its chunks back to back with the next chunk (possibly of
+// the next sequence) in flight; no LDS traffic or barriers inside the loop.
+constexpr int kMaxHeadsPerGroup = 8;
+
 struct SplitArgs {
   const void* query;
   const void* key_cache;
@@ -418,8 +419,10 @@ struct SplitArgs {
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t part_tokens;  // minimum piece length, multiple of 16
-  int32_t slots;        // ceil(max_context_len / part_tokens) + 1
+  int32_t heads_per_group;  // kv heads per workgroup (= waves), <= 8
+  int32_t num_groups;       // ceil(num_kv_heads / heads_per_group)
+  int32_t part_tokens;      // minimum piece length, multiple of 16
+  int32_t slots;            // ceil(max_context_len / part_tokens) + 1
   float scale_log2;
 };
 
@@ -433,38 +436,39 @@ __device__ __forceinline__ int split_tokens(const int32_t* context_lens, int seq
   return n < 0 ? 0 : static_cast<int>(n > cap ? cap : n);
 }
 
-// Worker (range) holding flattened block x when T blocks are split into R ranges.
+// Range holding flattened block x when T blocks are split into R ranges.
 __device__ __forceinline__ int64_t range_of(int64_t x, int64_t T, int64_t R) { return (x * R + R - 1) / T; }
 
 struct PieceCursor {
   int64_t x;      // flattened index of the piece's first block; -1 when done
-  int64_t x_end;  // end of this worker's range
-  int seq, kvh;
-  int nb;         // blocks of the pair
-  int b_lo, b_hi; // piece = blocks [b_lo, b_hi) of the pair
+  int64_t x_end;  // end of this workgroup's range
+  int seq;
+  int kvh;        // this wave's kv head (head group * heads_per_group + wave)
+  int nb;         // blocks of the sequence
+  int b_lo, b_hi; // piece = blocks [b_lo, b_hi) of the sequence
   int t_end;      // exclusive end position of the piece
   int nchunk, c;
-  int slot;       // partial slot of this piece, -1 when the piece is the whole pair
+  int slot;       // partial slot of this piece, -1 when the piece is the whole sequence
 };
 
 template <int CB>
 __device__ __forceinline__ void cursor_set_piece(PieceCursor& u, const SplitArgs& a, const int* s_pre, int64_t T,
-                                                 int64_t R) {
+                                                 int64_t R, int wave) {
   if (u.x >= u.x_end) { u.x = -1; return; }
-  const int64_t H = a.num_kv_heads;
-  int lo = 0, hi = a.num_seqs;  // largest seq with H * s_pre[seq] <= x
+  const int64_t Tseq = __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
+  const int gi = static_cast<int>(u.x / Tseq);
+  const int64_t xs = u.x - static_cast<int64_t>(gi) * Tseq;
+  int lo = 0, hi = a.num_seqs;  // largest seq with s_pre[seq] <= xs
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (H * __builtin_amdgcn_readfirstlane(s_pre[mid]) <= u.x) lo = mid; else hi = mid;
+    if (__builtin_amdgcn_readfirstlane(s_pre[mid]) <= xs) lo = mid; else hi = mid;
   }
   u.seq = __builtin_amdgcn_readfirstlane(lo);
   const int pre = __builtin_amdgcn_readfirstlane(s_pre[u.seq]);
   u.nb = __builtin_amdgcn_readfirstlane(s_pre[u.seq + 1]) - pre;
-  const int64_t within = u.x - H * pre;
-  u.kvh = static_cast<int>(within / u.nb);
-  u.b_lo = static_cast<int>(within - static_cast<int64_t>(u.kvh) * u.nb);
-  const int64_t left = u.x_end - u.x;
-  u.b_hi = static_cast<int>(min(static_cast<int64_t>(u.nb), u.b_lo + left));
+  u.kvh = gi * a.heads_per_group + wave;
+  u.b_lo = static_cast<int>(xs - pre);
+  u.b_hi = static_cast<int>(min(static_cast<int64_t>(u.nb), u.b_lo + (u.x_end - u.x)));
   const int n = __builtin_amdgcn_readfirstlane(
       split_tokens(a.context_lens, u.seq, a.max_blocks, a.part_tokens, a.slots));
   u.t_end = min(n, u.b_hi * kBlockTokens);
@@ -473,17 +477,16 @@ __device__ __forceinline__ void cursor_set_piece(PieceCursor& u, const SplitArgs
   if (u.b_lo == 0 && u.b_hi == u.nb) {
     u.slot = -1;
   } else {
-    const int64_t pair_start = u.x - u.b_lo;
-    u.slot = static_cast<int>(range_of(u.x, T, R) - range_of(pair_start, T, R));
+    u.slot = static_cast<int>(range_of(u.x, T, R) - range_of(u.x - u.b_lo, T, R));
   }
 }
 
 template <int CB>
 __device__ __forceinline__ void cursor_next(PieceCursor& u, const SplitArgs& a, const int* s_pre, int64_t T,
-                                            int64_t R) {
+                                            int64_t R, int wave) {
   if (++u.c < u.nchunk) return;
   u.x += u.b_hi - u.b_lo;
-  cursor_set_piece<CB>(u, a, s_pre, T, R);
+  cursor_set_piece<CB>(u, a, s_pre, T, R, wave);
 }
 
 // Close a piece: sum over row groups, normalise, write the partial or the
@@ -537,15 +540,14 @@ __device__ __forceinline__ void finish_piece(WaveState<T, D, G, CB>& st, const S
 }
 
 template <typename T, int D, int G, int CB>
-__global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64 * kMaxHeadsPerGroup, 1) void paged_decode_split_kernel(SplitArgs a) {
   using S = DecodeShape<T, D, G, CB>;
   extern __shared__ int s_pre[];  // [num_seqs + 1] blocks per sequence, exclusive prefix
-  __shared__ int s_run[256];
+  __shared__ int s_run[64 * kMaxHeadsPerGroup];
   const int lane = threadIdx.x & 63;
   // Wave-uniform by construction; readfirstlane lets the compiler keep all
   // per-wave indexing (pieces, block ids, base addresses) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
 
   // Prefix sum of blocks per sequence: thread t sums a contiguous run of
   // sequences, the run totals are scanned in LDS.
@@ -576,12 +578,8 @@ __global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a)
     __syncthreads();
   }
 
-  const int64_t nblk = static_cast<int64_t>(a.num_kv_heads) * __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
-  // Ranges: at least part_tokens per range, a multiple of 8 when possible
-  // (XCD x takes ranges [x*R/8, (x+1)*R/8)).
-  const int64_t launched = static_cast<int64_t>(gridDim.x) * nwaves;
-  int64_t R = min(launched, nblk / (a.part_tokens / kBlockTokens));
-  if (R >= 8) R = R / 8 * 8;
+  const int64_t nblk = static_cast<int64_t>(a.num_groups) * __builtin_amdgcn_readfirstlane(s_pre[a.num_seqs]);
+  int64_t R = min(static_cast<int64_t>(gridDim.x), nblk / (a.part_tokens / kBlockTokens));
   if (R < 1) R = 1;
   if (blockIdx.x == 0) {
     // Layout of the pieces, for the merge kernel.
@@ -592,22 +590,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a)
     int* pre_out = reinterpret_cast<int*>(a.header + 2);
     for (int i = threadIdx.x; i <= a.num_seqs; i += blockDim.x) pre_out[i] = s_pre[i];
   }
-  if (nblk == 0) return;
-  const int xcd = blockIdx.x & 7;
-  const int local = (blockIdx.x >> 3) * nwaves + wave;  // worker index within its XCD
-  int64_t r;
-  if (R >= 8) {
-    if (local >= R / 8) return;
-    r = xcd * (R / 8) + local;
-  } else {
-    r = static_cast<int64_t>(blockIdx.x) * nwaves + wave;
-    if (r >= R) return;
-  }
+  const int64_t r = blockIdx.x;
+  if (nblk == 0 || r >= R) return;
 
   PieceCursor cur;
   cur.x = r * nblk / R;
   cur.x_end = (r + 1) * nblk / R;
-  cursor_set_piece<CB>(cur, a, s_pre, nblk, R);
+  cursor_set_piece<CB>(cur, a, s_pre, nblk, R, wave);
   if (cur.x < 0) return;
 
   const int g = a.group;
@@ -616,7 +605,11 @@ __global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a)
   const char* kc = static_cast<const char*>(a.key_cache);
   const char* vc = static_cast<const char*>(a.value_cache);
   auto bt_row = [&](int seq) { return a.block_tables + static_cast<int64_t>(seq) * a.max_blocks; };
-  auto head_off = [&](int kvh) { return static_cast<int64_t>(kvh) * D * S::kElemBytes; };
+  // An idle wave (kv head past the last) reads kv head 0 and writes nothing.
+  auto live = [&](const PieceCursor& u) { return u.kvh < a.num_kv_heads; };
+  auto head_off = [&](const PieceCursor& u) {
+    return static_cast<int64_t>(live(u) ? u.kvh : 0) * D * S::kElemBytes;
+  };
 
   WaveState<T, D, G, CB> st;
   st.m = -__builtin_inff();
@@ -627,29 +620,41 @@ __global__ __launch_bounds__(256, 2) void paged_decode_split_kernel(SplitArgs a)
     for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
 
   u32x4_t q[S::kKSeg];
-  load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
+  load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, (live(cur) ? cur.kvh : 0) * g, g, lane, q);
   Chunk<T, D, G, CB> fa, fb;
   load_chunk<T, D, G, CB>(fa, kc, vc, bt_row(cur.seq), cur.b_lo, cur.b_hi - 1, a.num_blocks, tok_stride,
-                          blk_stride, head_off(cur.kvh), lane);
+                          blk_stride, head_off(cur), lane);
   PieceCursor nx = cur;
-  cursor_next<CB>(nx, a, s_pre, nblk, R);
+  cursor_next<CB>(nx, a, s_pre, nblk, R, wave);
 
   auto step = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
     if (nx.x >= 0)
       load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.b_lo + nx.c * CB, nx.b_hi - 1, a.num_blocks,
-                              tok_stride, blk_stride, head_off(nx.kvh), lane);
+                              tok_stride, blk_stride, head_off(nx), lane);
     const int tok0 = (cur.b_lo + cur.c * CB) * kBlockTokens;
     const bool last = cur.c == cur.nchunk - 1;
     float sc[CB][4];
     qk_chunk<T, D, G, CB>(sc, fcur, q, a.scale_log2);
     // The query of the next piece is fetched as soon as this piece's last
     // scores are out, so its latency hides behind the P*V work.
-    if (last && nx.x >= 0) load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, nx.kvh * g, g, lane, q);
+    if (last && nx.x >= 0)
+      load_query<T, D, G, CB>(a.query, nx.seq, a.num_heads, (live(nx) ? nx.kvh : 0) * g, g, lane, q);
     softmax_pv_chunk<T, D, G, CB>(st, fcur, sc, tok0, cur.t_end, tok0 + CB * kBlockTokens > cur.t_end, lane);
-    if (last) finish_piece<T, D, G, CB>(st, a, cur, lane);
+    if (last) {
+      if (live(cur)) {
+        finish_piece<T, D, G, CB>(st, a, cur, lane);
+      } else {
+        st.m = -__builtin_inff();
+        st.l = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
+      }
+    }
     if (nx.x < 0) return false;
     cur = nx;
-    cursor_next<CB>(nx, a, s_pre, nblk, R);
+    cursor_next<CB>(nx, a, s_pre, nblk, R, wave);
     return true;
   };
   while (step(fa, fb) && step(fb, fa)) {
@@ -724,20 +729,22 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(T* __restrict__ out, 
                                                            const float* __restrict__ o_parts,
                                                            const float* __restrict__ lse_parts,
                                                            const int64_t* __restrict__ header, int num_seqs,
-                                                           int num_heads, int num_kv_heads, int slots) {
-  constexpr int kPer = D / kWave;
+                                                           int num_heads, int num_kv_heads, int heads_per_group,
+                                                           int slots) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= static_cast<int64_t>(num_seqs) * num_heads) return;
   const int seq = static_cast<int>(row / num_heads);
   const int kvh = static_cast<int>(row - static_cast<int64_t>(seq) * num_heads) / (num_heads / num_kv_heads);
+  const int gi = kvh / heads_per_group;
   const int64_t nblk = header[0];
   const int64_t R = header[1];
   const int* pre = reinterpret_cast<const int*>(header + 2);
+  const int64_t Tseq = pre[num_seqs];
   const int nb = pre[seq + 1] - pre[seq];
   int np = 0;
   if (nb > 0) {
-    const int64_t x0 = static_cast<int64_t>(num_kv_heads) * pre[seq] + static_cast<int64_t>(kvh) * nb;
+    const int64_t x0 = static_cast<int64_t>(gi) * Tseq + pre[seq];
     np = static_cast<int>(range_of(x0 + nb - 1, nblk, R) - range_of(x0, nblk, R)) + 1;
   }
   if (np == 1) return;
@@ -872,14 +879,12 @@ SplitKernel pick_split(int dtype, int D, int G) {
   return D == 128 ? pick_split_group<float, 128>(G) : pick_split_group<float, 64>(G);
 }
 
-constexpr int kSplitThreads = 256;
-
-// Workgroups of `kernel` that fit on the device at once (persistent grid size).
-int resident_groups(const void* kernel, size_t lds) {
+// Workgroups of `kernel` with `threads` threads that fit on the device at once.
+int resident_groups(const void* kernel, int threads, size_t lds) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSplitThreads, lds) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
@@ -887,19 +892,19 @@ int launch_split(const SplitArgs& args, int dtype, int head_size, hipStream_t st
   const int G = next_pow2_group(args.group);
   SplitKernel k = pick_split(dtype, head_size, G);
   if (!k) return PA_ERR_UNSUPPORTED;
+  const int threads = kWave * args.heads_per_group;
   const size_t lds = (static_cast<size_t>(args.num_seqs) + 1) * sizeof(int);
-  const int resident = resident_groups(reinterpret_cast<const void*>(k), lds);
+  const int resident = resident_groups(reinterpret_cast<const void*>(k), threads, lds);
   if (resident <= 0) return PA_ERR_HIP;
-  // Persistent grid: as many workgroups as fit at once, a multiple of 8 (one
-  // per XCD in turn), and no more than the work can use.
-  const int64_t blocks_bound = static_cast<int64_t>(args.num_seqs) * args.max_blocks * args.num_kv_heads;
-  const int64_t ranges_bound = blocks_bound / (args.part_tokens / kBlockTokens) + 1;
-  const int64_t useful = (ranges_bound + kSplitThreads / kWave - 1) / (kSplitThreads / kWave);
-  int64_t grid = resident / 8 * 8;
-  if (grid > (useful + 7) / 8 * 8) grid = (useful + 7) / 8 * 8;
-  if (grid < 8) grid = 8;
+  // Persistent grid: as many workgroups as fit at once, and no more than the
+  // work can use (each range spans at least partition_size tokens).
+  const int64_t blocks_bound = static_cast<int64_t>(args.num_seqs) * args.max_blocks * args.num_groups;
+  const int64_t useful = blocks_bound / (args.part_tokens / kBlockTokens) + 1;
+  int64_t grid = resident;
+  if (grid > useful) grid = useful;
+  if (grid < 1) grid = 1;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kSplitThreads), lds, stream, args);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(threads), lds, stream, args);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   const int64_t rows = static_cast<int64_t>(args.num_seqs) * args.num_heads;
   constexpr int kRowsPerBlock = 4;
@@ -909,7 +914,7 @@ int launch_split(const SplitArgs& args, int dtype, int head_size, hipStream_t st
 #define PA_MERGE_PIECES(TT, DD)                                                                                    \
   hipLaunchKernelGGL((merge_pieces_kernel<TT, DD>), g, b, 0, stream, static_cast<TT*>(args.out), args.lse_out,   \
                      args.o_parts, args.lse_parts, args.header, args.num_seqs, args.num_heads, args.num_kv_heads, \
-                     args.slots)
+                     args.heads_per_group, args.slots)
   if (dtype == PA_DTYPE_BF16) {
     if (head_size == 128) PA_MERGE_PIECES(bf16_t, 128); else PA_MERGE_PIECES(bf16_t, 64);
   } else {
@@ -1039,6 +1044,8 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
   args.num_heads = num_heads;
   args.num_kv_heads = num_kv_heads;
   args.group = num_heads / num_kv_heads;
+  args.heads_per_group = num_kv_heads < kMaxHeadsPerGroup ? num_kv_heads : kMaxHeadsPerGroup;
+  args.num_groups = (num_kv_heads + args.heads_per_group - 1) / args.heads_per_group;
   args.part_tokens = partition_size;
   args.slots = static_cast<int32_t>(L.slots);
   args.scale_log2 = scale * kLog2e;

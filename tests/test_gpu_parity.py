@@ -60,25 +60,30 @@ def check_split_pieces(pa, cfg, inp, kc, vc, ws, P, max_pairs=24):
     """The workspace pieces of pa_decode_split against the oracle, piece by piece.
 
     The header gives the cut (T blocks, R ranges, per-sequence block prefix);
-    each piece of a cut pair must hold attention over exactly its token range.
+    kv heads go in groups of up to 8, the blocks of all sequences laid end to
+    end per group. Each piece of a cut sequence must hold attention over
+    exactly its token range, for every query head of its group.
     """
     S, Hq, Hkv, d = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size
     g = Hq // Hkv
+    HG = min(Hkv, 8)
+    NG = -(-Hkv // HG)
     o_parts, lse_parts, T, R, prefix = pa.workspace_views(ws, S, Hq, d, inp.max_context_len, P)
     n = inp.context_lens.astype(np.int64)
     nb = (n + 15) // 16
-    np.testing.assert_array_equal(prefix.cpu().numpy(), np.concatenate([[0], np.cumsum(nb)]))
-    assert T == Hkv * nb.sum() and 1 <= R
-    assert R <= max(1, T // (P // 16))
+    pre = prefix.cpu().numpy().astype(np.int64)
+    np.testing.assert_array_equal(pre, np.concatenate([[0], np.cumsum(nb)]))
+    Tseq = int(nb.sum())
+    assert T == NG * Tseq and 1 <= R <= max(1, T // (P // 16))
     rng_of = lambda x: (x * R + R - 1) // T  # noqa: E731
     go, gl = f64(o_parts), f64(lse_parts)
     q = oracle.decode_values(inp.query, cfg.dtype)
     checked = 0
     for i in range(S):
-        for h in range(Hkv):
-            x0 = Hkv * int(prefix[i]) + h * int(nb[i])
-            if nb[i] == 0:
-                continue
+        if nb[i] == 0:
+            continue
+        for gi in range(NG):
+            x0 = gi * Tseq + int(pre[i])
             r0, r1 = rng_of(x0), rng_of(x0 + int(nb[i]) - 1)
             if r0 == r1:
                 continue
@@ -89,11 +94,12 @@ def check_split_pieces(pa, cfg, inp, kc, vc, ws, P, max_pairs=24):
                 hi = min(x0 + int(nb[i]), (r + 1) * T // R) - x0
                 assert hi - lo >= 1
                 t0, t1 = lo * 16, min(hi * 16, int(n[i]))
-                ro, rl = oracle.attention_contiguous(q[i, h * g:(h + 1) * g], Kf[t0:t1, h:h + 1],
-                                                     Vf[t0:t1, h:h + 1], cfg.scale)
                 j = r - r0
-                assert np.abs(go[i, h * g:(h + 1) * g, j] - ro).max() <= PART_TOL[cfg.dtype]
-                assert np.abs(gl[i, h * g:(h + 1) * g, j] - rl).max() <= LSE_TOL[cfg.dtype]
+                for h in range(gi * HG, min(Hkv, (gi + 1) * HG)):
+                    ro, rl = oracle.attention_contiguous(q[i, h * g:(h + 1) * g], Kf[t0:t1, h:h + 1],
+                                                         Vf[t0:t1, h:h + 1], cfg.scale)
+                    assert np.abs(go[i, h * g:(h + 1) * g, j] - ro).max() <= PART_TOL[cfg.dtype]
+                    assert np.abs(gl[i, h * g:(h + 1) * g, j] - rl).max() <= LSE_TOL[cfg.dtype]
             checked += 1
             if checked >= max_pairs:
                 return checked
@@ -127,8 +133,9 @@ def test_shape_sweep(pa, dtype, d_h, Hq, Hkv):
         assert max_err(l, ref_lse) <= LSE_TOL[dtype]
 
 
-def test_split_pieces_long_contexts(pa):
-    cfg = W.small_case("pieces", 5, 16, 4, 128, "bf16", ("uniform", 900, 3000), seed=31, num_blocks=1200,
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (24, 12)])
+def test_split_pieces_long_contexts(pa, Hq, Hkv):
+    cfg = W.small_case("pieces", 5, Hq, Hkv, 128, "bf16", ("uniform", 900, 3000), seed=31, num_blocks=1200,
                        partition_size=64)
     inp = W.make_inputs(cfg)
     d = Dev(inp)
