@@ -106,16 +106,18 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
  * softmax is evaluated online over the streamed blocks (stanleyjacob.dev
  * "vLLM", Part IV "Stage 6: The forward pass").
  *
+ * Work is cut into jobs of one (sequence, kv head) each, taken by persistent
+ * workgroups (as many as fit on the GPU at once) in a fixed order.
+ *
  *   out               [num_seqs, num_heads, head_size], written (dtype).
  *   lse_out           optional float32 [num_seqs, num_heads]: ln sum_t exp(s_t).
  *                     NULL to skip.
  *   seq_order         optional int32 [num_seqs], a permutation of the sequence
- *                     indices: the order in which sequences are handed to the
- *                     GPU (one workgroup per sequence and kv head, dispatched
- *                     in order). Longest-first keeps the last wave of work
- *                     short. It is a schedule only: every output is
- *                     bit-identical to the NULL (natural order) result.
- *                     Entries outside [0, num_seqs) are clamped.
+ *                     indices: the order in which sequences are handed out.
+ *                     Longest-first evens out the work of the workgroups. It is
+ *                     a schedule only: every output is bit-identical to the
+ *                     NULL (natural order) result. Entries outside
+ *                     [0, num_seqs) are clamped.
  *   n = 0             gives out = 0 and lse = -inf.
  *   Table entries at index >= ceil(n / block_size) are never read.
  * Returns PA_OK or an error status.

@@ -168,7 +168,7 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
     """One-pass paged decode attention into ``out`` (optionally ln-sum-exp into ``lse_out``).
 
     ``seq_order`` (int32 [num_seqs], a permutation) is a schedule hint: the order
-    in which sequences are dispatched, e.g. longest first. Results do not depend on it.
+    in which sequences are handed out, e.g. longest first. Results do not depend on it.
     """
     p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
                                                    context_lens, lse_out)

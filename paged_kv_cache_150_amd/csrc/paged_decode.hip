@@ -73,6 +73,7 @@ struct DecodeArgs {
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t group;        // H_q / H_kv
+  int32_t num_jobs;     // job ids: ceil(num_seqs / 8) * 8 * num_kv_heads
   float scale_log2;     // scale * log2(e)
 };
 
@@ -254,8 +255,76 @@ __device__ __forceinline__ void load_query(const void* query, int seq, int num_h
   }
 }
 
+// One decode job is one (sequence, kv head); job ids follow the XCD-aware
+// order of wg_to_seq_head (id % 8 names the XCD meant to run it, and all kv
+// heads of a sequence share it), and ids past the last sequence are padding.
+struct DecodeJob {
+  int seq;  // -1 for a padding id
+  int kvh;
+  int n;    // context tokens, clamped to the block table
+};
+
+__device__ __forceinline__ DecodeJob decode_job(const DecodeArgs& a, int id) {
+  DecodeJob j;
+  int seq, kvh;
+  wg_to_seq_head(id, a.num_kv_heads, seq, kvh);
+  j.kvh = kvh;
+  j.seq = -1;
+  j.n = 0;
+  if (seq >= a.num_seqs) return j;
+  if (a.seq_order != nullptr) {
+    // Schedule hint: the j-th dispatched sequence is seq_order[j]. Out-of-range
+    // entries are clamped (wrong output for that caller, never a bad access).
+    const uint32_t o = static_cast<uint32_t>(a.seq_order[seq]);
+    seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
+  }
+  const int max_tokens = a.max_blocks * kBlockTokens;
+  const int n = a.context_lens[seq];
+  j.n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+  j.seq = seq;
+  return j;
+}
+
+// Job k of persistent workgroup w out of `grid`: rounds of `grid` consecutive
+// ids, walked forwards in even rounds and backwards in odd ones, so that with
+// jobs in longest-first order every workgroup gets a similar total. grid is a
+// multiple of 8, so the kv heads of one sequence (ids equal mod 8) still run on
+// one XCD.
+__device__ __forceinline__ int job_of(int k, int w, int grid) {
+  const int base = k * grid;
+  return (k & 1) ? base + grid - 1 - w : base + w;
+}
+
+// This wave's share of one job: chunks wave, wave + W, ... of the context.
+struct JobPlan {
+  const int32_t* bt_row;
+  int64_t head_off;
+  int blk_last;    // last block of the context
+  int mine;        // chunks of this wave
+  int mask_chunk;  // the chunk that reaches past the context end, or -1
+};
+
+template <typename T, int D, int CB>
+__device__ __forceinline__ JobPlan plan_job(const DecodeArgs& a, const DecodeJob& j, int wave, int nwaves) {
+  JobPlan p;
+  p.bt_row = a.block_tables + static_cast<int64_t>(j.seq < 0 ? 0 : j.seq) * a.max_blocks;
+  p.head_off = static_cast<int64_t>(j.kvh) * D * static_cast<int>(sizeof(T));
+  const int blk_end = (j.n + kBlockTokens - 1) / kBlockTokens;
+  const int nchunk = (blk_end + CB - 1) / CB;
+  p.blk_last = blk_end - 1;
+  p.mine = (j.seq >= 0 && wave < nchunk) ? (nchunk - wave + nwaves - 1) / nwaves : 0;
+  p.mask_chunk = (nchunk * CB * kBlockTokens > j.n) ? nchunk - 1 : -1;
+  return p;
+}
+
+// Persistent workgroups, each taking the jobs job_of(0, w), job_of(1, w), ...
+// While a job's waves merge their partial results, the next job's query and
+// first chunk are already being loaded, so no workgroup waits on a cold start
+// between jobs.
+// Two workgroups per CU (at most 256 registers per lane); the 16-head group
+// needs more registers and runs one workgroup per CU.
 template <typename T, int D, int G, int CB, bool PF>
-__global__ __launch_bounds__(256, 1) void paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D, G, CB>;
   extern __shared__ float s_acc[];  // [W][G][D]
   __shared__ float s_m[8][16];
@@ -266,123 +335,153 @@ __global__ __launch_bounds__(256, 1) void paged_decode_kernel(DecodeArgs a) {
   // per-wave indexing (units, block ids, base addresses) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
-
-  int seq, kvh;
-  wg_to_seq_head(blockIdx.x, a.num_kv_heads, seq, kvh);
-  if (seq >= a.num_seqs) return;  // padding workgroups of the last XCD round
-  if (a.seq_order != nullptr) {
-    // Schedule hint: the j-th dispatched sequence is seq_order[j]. Out-of-range
-    // entries are clamped (wrong output for that caller, never a bad access).
-    const uint32_t o = static_cast<uint32_t>(a.seq_order[seq]);
-    seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
-  }
-
-  const int max_tokens = a.max_blocks * kBlockTokens;
-  int n = a.context_lens[seq];
-  n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-  const int t_begin = 0;
-  const int t_end = n;
+  const int grid = gridDim.x;
+  const int w = blockIdx.x;
   const int g = a.group;
-  const int head0 = kvh * g;
 
   const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
   const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
-  const int64_t head_off = static_cast<int64_t>(kvh) * D * S::kElemBytes;
   const char* kc = static_cast<const char*>(a.key_cache);
   const char* vc = static_cast<const char*>(a.value_cache);
-  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
 
-  WaveState<T, D, G, CB> st;
-  st.m = -__builtin_inff();
-  st.l = 0.f;
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
+  int k = 0;
+  const int id0 = job_of(0, w, grid);
+  DecodeJob cur;
+  cur.seq = -1;
+  cur.kvh = 0;
+  cur.n = 0;
+  if (id0 < a.num_jobs) cur = decode_job(a, id0);
+  JobPlan pc = plan_job<T, D, CB>(a, cur, wave, nwaves);
+  // Block of this wave's i-th chunk of a job.
+  auto blk_of = [&](int i) { return (wave + i * nwaves) * CB; };
 
-  if (t_begin < t_end) {
-    // Query fragment (MFMA B operand): head lane%16 of the group, same d order as K.
-    u32x4_t q[S::kKSeg];
-    load_query<T, D, G, CB>(a.query, seq, a.num_heads, head0, g, lane, q);
-    const int blk_begin = t_begin / kBlockTokens;
-    const int blk_end = (t_end + kBlockTokens - 1) / kBlockTokens;
-    const int blk_last = blk_end - 1;
-    const int nchunk = (blk_end - blk_begin + CB - 1) / CB;
-    // Only the final chunk can reach past t_end.
-    const int mask_chunk = ((blk_begin + nchunk * CB) * kBlockTokens > t_end) ? nchunk - 1 : -1;
-
-    Chunk<T, D, G, CB> fa;
-    int c = wave;
-    if constexpr (PF) {
-      // One chunk of lookahead: the next chunk's loads are in flight while
-      // this one is computed.
-      Chunk<T, D, G, CB> fb;
-      if (c < nchunk)
-        load_chunk<T, D, G, CB>(fa, kc, vc, bt_row, blk_begin + c * CB, blk_last, a.num_blocks,
-                                tok_stride, blk_stride, head_off, lane);
-      while (c < nchunk) {
-        int cn = c + nwaves;
-        if (cn < nchunk)
-          load_chunk<T, D, G, CB>(fb, kc, vc, bt_row, blk_begin + cn * CB, blk_last, a.num_blocks,
-                                  tok_stride, blk_stride, head_off, lane);
-        compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, (blk_begin + c * CB) * kBlockTokens, t_end,
-                                   c == mask_chunk, lane);
-        if (cn >= nchunk) break;
-        c = cn;
-        cn = c + nwaves;
-        if (cn < nchunk)
-          load_chunk<T, D, G, CB>(fa, kc, vc, bt_row, blk_begin + cn * CB, blk_last, a.num_blocks,
-                                  tok_stride, blk_stride, head_off, lane);
-        compute_chunk<T, D, G, CB>(st, fb, q, a.scale_log2, (blk_begin + c * CB) * kBlockTokens, t_end,
-                                   c == mask_chunk, lane);
-        c = cn;
-      }
-    } else {
-      for (; c < nchunk; c += nwaves) {
-        load_chunk<T, D, G, CB>(fa, kc, vc, bt_row, blk_begin + c * CB, blk_last, a.num_blocks,
-                                tok_stride, blk_stride, head_off, lane);
-        compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, (blk_begin + c * CB) * kBlockTokens, t_end,
-                                   c == mask_chunk, lane);
-      }
-    }
+  u32x4_t q[S::kKSeg];
+  Chunk<T, D, G, CB> fa;
+  if (cur.n > 0 && cur.seq >= 0) {
+    load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
+    if (PF && pc.mine > 0)
+      load_chunk<T, D, G, CB>(fa, kc, vc, pc.bt_row, blk_of(0), pc.blk_last, a.num_blocks, tok_stride,
+                              blk_stride, pc.head_off, lane);
   }
+  int id = id0;
+  while (id < a.num_jobs) {
+    // The next job is known now: its metadata is fetched a whole job ahead.
+    const int id_next = job_of(k + 1, w, grid);
+    DecodeJob nxt;
+    nxt.seq = -1;
+    nxt.kvh = 0;
+    nxt.n = 0;
+    if (id_next < a.num_jobs) nxt = decode_job(a, id_next);
 
-  // Sum this wave's partials over the 4 row groups (lanes l, l^16, l^32, l^48).
-  st.l = rows_sum(st.l);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = rows_sum(st.acc[h][e]);
-  if (lane < 16) {
-    s_m[wave][lane] = st.m;
-    s_l[wave][lane] = st.l;
+    WaveState<T, D, G, CB> st;
+    st.m = -__builtin_inff();
+    st.l = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < S::kVec; ++e) s_acc[(wave * G + h) * D + lane * S::kVec + e] = st.acc[h][e];
-  }
-  __syncthreads();
+      for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
 
-  // Merge the waves: weights 2^(m_w - M).
-  for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -__builtin_inff();
-    for (int w = 0; w < nwaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float o = 0.f, L = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int w = 0; w < nwaves; ++w) {
-        const float wt = fast_exp2(s_m[w][h] - M);
-        L = fmaf(wt, s_l[w][h], L);
-        o = fmaf(wt, s_acc[(w * G + h) * D + d], o);
+    const int mine = pc.mine;
+    auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
+    auto is_mask = [&](int i) { return wave + i * nwaves == pc.mask_chunk; };
+    if constexpr (PF) {
+      // One chunk of lookahead, fa already in flight. The steady-state loop
+      // issues its lookahead loads unconditionally and the last one or two
+      // chunks are peeled off: with a conditional load inside the loop the
+      // hardware wait counts on the two paths differ and the wait before the
+      // current chunk's use would also cover the lookahead. The scheduling
+      // barriers keep the loads ahead of the current chunk's arithmetic (left
+      // alone, the scheduler sinks them to shorten register live ranges).
+      // Only the final chunk of the context, a wave's last, can need a mask.
+      Chunk<T, D, G, CB> fb;
+      if (mine > 0) {
+        int i = 0;
+        for (; i + 2 < mine; i += 2) {
+          load_chunk<T, D, G, CB>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
+                                  blk_stride, pc.head_off, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          load_chunk<T, D, G, CB>(fa, kc, vc, pc.bt_row, blk_of(i + 2), pc.blk_last, a.num_blocks, tok_stride,
+                                  blk_stride, pc.head_off, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_chunk<T, D, G, CB>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, false, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i + 1 < mine) {
+          load_chunk<T, D, G, CB>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
+                                  blk_stride, pc.head_off, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
+          compute_chunk<T, D, G, CB>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, is_mask(i + 1), lane);
+        } else {
+          compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
+        }
       }
-      o = o / L;
+    } else {
+      for (int i = 0; i < mine; ++i) {
+        load_chunk<T, D, G, CB>(fa, kc, vc, pc.bt_row, blk_of(i), pc.blk_last, a.num_blocks, tok_stride,
+                                blk_stride, pc.head_off, lane);
+        compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
+      }
     }
-    const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
-    const int64_t row = static_cast<int64_t>(seq) * a.num_heads + head0 + h;
-    store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
-    if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
+
+    // The next job's query and first chunk go out before this job's merge.
+    const JobPlan pn = plan_job<T, D, CB>(a, nxt, wave, nwaves);
+    if (nxt.n > 0 && nxt.seq >= 0) {
+      load_query<T, D, G, CB>(a.query, nxt.seq, a.num_heads, nxt.kvh * g, g, lane, q);
+      if (PF && pn.mine > 0)
+        load_chunk<T, D, G, CB>(fa, kc, vc, pn.bt_row, blk_of(0), pn.blk_last, a.num_blocks, tok_stride,
+                                blk_stride, pn.head_off, lane);
+    }
+
+    // Sum this wave's partials over the 4 row groups (lanes l, l^16, l^32, l^48).
+    st.l = rows_sum(st.l);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = rows_sum(st.acc[h][e]);
+    if (lane < 16) {
+      s_m[wave][lane] = st.m;
+      s_l[wave][lane] = st.l;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < S::kVec; ++e) s_acc[(wave * G + h) * D + lane * S::kVec + e] = st.acc[h][e];
+    }
+    __syncthreads();
+
+    if (cur.seq >= 0) {
+      // Merge the waves: weights 2^(m_w - M).
+      const int head0 = cur.kvh * g;
+      for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = -__builtin_inff();
+        for (int v = 0; v < nwaves; ++v) M = fmaxf(M, s_m[v][h]);
+        float o = 0.f, L = 0.f;
+        if (M != -__builtin_inff()) {
+          for (int v = 0; v < nwaves; ++v) {
+            const float wt = fast_exp2(s_m[v][h] - M);
+            L = fmaf(wt, s_l[v][h], L);
+            o = fmaf(wt, s_acc[(v * G + h) * D + d], o);
+          }
+          o = o / L;
+        }
+        const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
+        const int64_t row = static_cast<int64_t>(cur.seq) * a.num_heads + head0 + h;
+        store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
+        if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
+      }
+    }
+    __syncthreads();  // the next job rewrites the LDS partials
+
+    id = id_next;
+    cur = nxt;
+    pc = pn;
+    ++k;
   }
+
 }
 
 // ------------------------------------------------------------------ partitioned path
@@ -627,10 +726,9 @@ __global__ __launch_bounds__(64 * kMaxHeadsPerGroup, 1) void paged_decode_split_
   PieceCursor nx = cur;
   cursor_next<CB>(nx, a, s_pre, nblk, R, wave);
 
-  auto step = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
-    if (nx.x >= 0)
-      load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.b_lo + nx.c * CB, nx.b_hi - 1, a.num_blocks,
-                              tok_stride, blk_stride, head_off(nx), lane);
+  // Computes the current chunk (fcur) and closes its piece when it is the
+  // piece's last chunk.
+  auto compute = [&](Chunk<T, D, G, CB>& fcur) {
     const int tok0 = (cur.b_lo + cur.c * CB) * kBlockTokens;
     const bool last = cur.c == cur.nchunk - 1;
     float sc[CB][4];
@@ -652,12 +750,26 @@ __global__ __launch_bounds__(64 * kMaxHeadsPerGroup, 1) void paged_decode_split_
           for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
       }
     }
-    if (nx.x < 0) return false;
+  };
+  // The lookahead load is issued unconditionally inside the loop (the exit
+  // test comes first), so the hardware wait before the current chunk's use
+  // leaves the lookahead in flight; the scheduling barriers keep the loads
+  // ahead of the arithmetic.
+  auto advance = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
+    if (nx.x < 0) {
+      compute(fcur);
+      return false;
+    }
+    load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.b_lo + nx.c * CB, nx.b_hi - 1, a.num_blocks,
+                            tok_stride, blk_stride, head_off(nx), lane);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(fcur);
+    __builtin_amdgcn_sched_barrier(0);
     cur = nx;
     cursor_next<CB>(nx, a, s_pre, nblk, R, wave);
     return true;
   };
-  while (step(fa, fb) && step(fb, fa)) {
+  while (advance(fa, fb) && advance(fb, fa)) {
   }
 }
 
@@ -841,25 +953,44 @@ int check_common(const void* out, const void* query, const void* key_cache, cons
   return PA_OK;
 }
 
-int launch_decode(const DecodeArgs& args, int num_seqs, int dtype, int head_size, hipStream_t stream) {
+// Workgroups of `kernel` with `threads` threads that fit on the device at once.
+int resident_groups(const void* kernel, int threads, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
+  return cus * (per_cu > 0 ? per_cu : 1);
+}
+
+int launch_decode(DecodeArgs args, int num_seqs, int dtype, int head_size, hipStream_t stream) {
   const int G = next_pow2_group(args.group);
   DecodeKernel k = pick_decode(dtype, head_size, G);
   if (!k) return PA_ERR_UNSUPPORTED;
-  const int64_t grid = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * args.num_kv_heads;
-  if (grid <= 0) return PA_OK;
-  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  // Job ids padded to whole XCD rounds (a multiple of 8).
+  const int64_t jobs = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * args.num_kv_heads;
+  if (jobs <= 0) return PA_OK;
+  if (jobs > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
   const int W = waves_per_group();
   const size_t lds = static_cast<size_t>(W) * G * head_size * sizeof(float);
+  // Persistent grid: the workgroups that fit at once, a multiple of 8 (one
+  // round over the XCDs), and no more than there are jobs.
+  int64_t grid = resident_groups(reinterpret_cast<const void*>(k), W * kWave, lds);
+  if (grid <= 0) return PA_ERR_HIP;
+  if (grid >= 8) grid -= grid % 8;
+  if (grid > jobs) grid = jobs;
+
+  args.num_jobs = static_cast<int32_t>(jobs);
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), lds, stream, args);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 typedef void (*SplitKernel)(SplitArgs);
 
+// The partitioned path keeps a cursor and the next piece's state live across
+// its loop, so it streams one block per chunk.
 template <typename T, int D, int G>
 SplitKernel split_kernel_for() {
-  using P = Policy<T, D, G>;
-  return paged_decode_split_kernel<T, D, G, P::CB>;
+  return paged_decode_split_kernel<T, D, G, 1>;
 }
 
 template <typename T, int D>
@@ -877,15 +1008,6 @@ SplitKernel pick_split_group(int G) {
 SplitKernel pick_split(int dtype, int D, int G) {
   if (dtype == PA_DTYPE_BF16) return D == 128 ? pick_split_group<bf16_t, 128>(G) : pick_split_group<bf16_t, 64>(G);
   return D == 128 ? pick_split_group<float, 128>(G) : pick_split_group<float, 64>(G);
-}
-
-// Workgroups of `kernel` with `threads` threads that fit on the device at once.
-int resident_groups(const void* kernel, int threads, size_t lds) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
-  return cus * (per_cu > 0 ? per_cu : 1);
 }
 
 int launch_split(const SplitArgs& args, int dtype, int head_size, hipStream_t stream) {
@@ -950,6 +1072,8 @@ int launch_merge(void* out, float* lse_out, const float* o_parts, const float* l
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+
 
 
 }  // namespace

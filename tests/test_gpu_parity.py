@@ -279,6 +279,31 @@ def test_seq_order_is_only_a_schedule(pa):
         np.testing.assert_array_equal(bits(la), bits(l))
 
 
+def test_many_jobs_per_workgroup(pa):
+    """Far more (sequence, kv head) jobs than resident workgroups: each
+    persistent workgroup walks many jobs, short and empty ones included, and the
+    schedule (natural order, longest first, random) never changes a bit."""
+    S = 1100
+    cfg = W.small_case("many_jobs", S, 16, 8, 64, "bf16", ("uniform", 1, 40), seed=41, num_blocks=4000)
+    inp = W.make_inputs(cfg)
+    lens = inp.context_lens.copy()
+    lens[::7] = 0
+    inp.context_lens = lens
+    d = Dev(inp)
+    _say(f"many_jobs: {S * cfg.num_kv_heads} jobs")
+    a, la = d.decode(pa, lse=True)
+    others = [d.decode(pa, lse=True, seq_order=np.argsort(-lens, kind="stable")),
+              d.decode(pa, lse=True, seq_order=np.random.default_rng(2).permutation(S))]
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                                       lens, cfg.scale, "bf16")
+    assert max_err(a, ref) <= TOL["bf16"] and max_err(la, ref_lse) <= LSE_TOL["bf16"]
+    assert (f64(a)[lens == 0] == 0).all() and np.isneginf(f64(la)[lens == 0]).all()
+    for o, l in others:
+        np.testing.assert_array_equal(bits(a), bits(o))
+        np.testing.assert_array_equal(bits(la), bits(l))
+
+
 def test_run_to_run_deterministic(pa):
     cfg = W.CONFIG_BY_NAME["prefix_70b"]
     inp = W.make_inputs(cfg, mode="perf")
