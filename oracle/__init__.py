@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged decode attention and reshape_and_cache.
+"""fp64 CPU oracle for paged decode attention and reshape_and_cache, and a
+plain Python KV block pool with its step-input builder.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -30,4 +31,9 @@ from .kv_sizes import (  # noqa: F401
     bytes_per_block,
     blocks_in_pool,
     blocks_for_tokens,
+)
+from .block_pool import (  # noqa: F401
+    BlockPool,
+    PoolError,
+    prepare_step,
 )
