@@ -66,7 +66,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, negative size, bad enum   */
   PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (block_size, head_size)   */
   PA_ERR_WORKSPACE = 3,    /* workspace smaller than pa_decode_split_workspace_bytes */
-  PA_ERR_HIP = 4           /* the HIP runtime refused a launch                     */
+  PA_ERR_HIP = 4,          /* the HIP runtime refused a launch                     */
+  PA_ERR_NO_BLOCKS = 5     /* a block pool (pa_pool.h) has too few free blocks     */
 } pa_status;
 
 /*

@@ -74,6 +74,7 @@ extern "C" const char* pa_status_string(int status) {
                                     "num_heads/num_kv_heads at most 16)";
     case PA_ERR_WORKSPACE: return "workspace smaller than pa_decode_split_workspace_bytes()";
     case PA_ERR_HIP: return "HIP runtime refused the launch";
+    case PA_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
     default: return "unknown status";
   }
 }

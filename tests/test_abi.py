@@ -1,6 +1,7 @@
-"""The C ABI without a GPU: libpa.so loads, exports every symbol pa.h declares,
-and rejects bad arguments on the host before any GPU work is queued."""
+"""The C ABI without a GPU: libpa.so loads, exports every symbol include/*.h
+declares, and rejects bad arguments on the host before any GPU work is queued."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -8,7 +9,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -18,16 +19,24 @@ def lib():
     return pa.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+def declared_functions(header=None):
+    names = set()
+    for h in ([header] if header else HEADERS):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
-def test_header_declares_the_boundary():
-    assert declared_functions() == sorted([
+def test_headers_declare_the_boundary():
+    inc = os.path.join(ROOT, "include")
+    assert declared_functions(os.path.join(inc, "pa.h")) == sorted([
         "pa_reshape_and_cache", "pa_decode", "pa_decode_split_workspace_bytes", "pa_decode_split",
         "pa_merge_partitions", "pa_status_string"])
+    assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
+        "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
+        "pa_pool_allocate", "pa_pool_append_slot", "pa_pool_share", "pa_pool_release",
+        "pa_pool_make_writable", "pa_prepare_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -41,8 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
-        assert lib.pa_status_string(code)
+    for code in range(6):
+        assert lib.pa_status_string(code) != b"unknown status"
     assert lib.pa_status_string(99) == b"unknown status"
 
 
