@@ -25,6 +25,7 @@ from .paged_attention import (  # noqa: F401
     paged_decode_partitions,
     lse_merge,
     reshape_and_cache,
+    copy_blocks,
 )
 from .kv_sizes import (  # noqa: F401
     kv_bytes,

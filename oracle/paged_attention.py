@@ -176,3 +176,25 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, key_cache: np.ndarray,
         kc[slot // block_size, slot % block_size] = key[t]
         vc[slot // block_size, slot % block_size] = value[t]
     return kc, vc
+
+
+def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray, block_mapping):
+    """Whole-block copies for copy-on-write; return new (key_cache, value_cache).
+
+    For each (source, destination) pair, in order, the destination block's K
+    and V (all token rows, all kv heads) become the source block's: the GPU
+    half of copy-on-write, which gives a writer a private copy of a block that
+    others still read (llm-stack-book 7.3 "vLLM: Architecture,
+    PagedAttention & Internals", section "Copy-on-write for shared blocks").
+    A pair naming a block outside the pool is skipped (reading: the pages
+    never name one). The inputs are not modified.
+    """
+    kc = key_cache.copy()
+    vc = value_cache.copy()
+    nb = kc.shape[0]
+    for src, dst in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= src < nb and 0 <= dst < nb):
+            continue
+        kc[dst] = kc[src]
+        vc[dst] = vc[src]
+    return kc, vc

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from oracle.block_pool import BlockPool, PoolError, prepare_step
+import oracle
 from oracle import kv_bytes
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -209,3 +210,37 @@ def test_random_operations_keep_the_books():
                 held[b] = held.get(b, 0) + 1
         assert held == pool.refs
         assert sorted(pool.free + list(held)) == list(range(40))
+
+
+def test_copy_on_write_keeps_every_reader_correct():
+    """Through the pool and the block copy: after a writer's shared block is
+    copied, both tables still read the same K/V at every position, blocks not
+    named are untouched, and the writer can then change its copy without the
+    reader seeing it."""
+    rng = np.random.default_rng(5)
+    pool = BlockPool(12, 16)
+    kc = rng.standard_normal((12, 16, 2, 8))
+    vc = rng.standard_normal((12, 16, 2, 8))
+    a = pool.allocate(40)
+    b = list(a)
+    pool.share(b)
+    copy = pool.make_writable(b, 2)
+    k2, v2 = oracle.copy_blocks(kc, vc, [copy])
+    for p in range(40):
+        for t in (a, b):
+            assert np.array_equal(k2[t[p // 16], p % 16], kc[a[p // 16], p % 16])
+            assert np.array_equal(v2[t[p // 16], p % 16], vc[a[p // 16], p % 16])
+    untouched = [i for i in range(12) if i != copy[1]]
+    assert np.array_equal(k2[untouched], kc[untouched]) and np.array_equal(v2[untouched], vc[untouched])
+    # The writer's new token lands in its private block only.
+    k3, v3 = oracle.reshape_and_cache(np.ones((1, 2, 8)), np.ones((1, 2, 8)), k2, v2,
+                                      np.array([b[40 // 16] * 16 + 40 % 16]))
+    assert np.array_equal(k3[a[2], 8], k2[a[2], 8]) and (k3[b[2], 8] == 1).all()
+
+
+def test_copy_blocks_skips_pairs_outside_the_pool():
+    kc = np.arange(4 * 16 * 2, dtype=np.float64).reshape(4, 16, 2)
+    vc = -kc
+    k2, v2 = oracle.copy_blocks(kc, vc, [[0, 7], [-1, 2], [1, 3]])
+    assert np.array_equal(k2[3], kc[1]) and np.array_equal(v2[3], vc[1])
+    assert np.array_equal(k2[:3], kc[:3]) and np.array_equal(v2[:3], vc[:3])
