@@ -68,7 +68,54 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 20 times (counter calibration) and exit")
+    ap.add_argument("--op", choices=["step", "copy_blocks"], default="step",
+                    help="step: reshape + decode (the headline); copy_blocks: pa_copy_blocks on the "
+                         "workload's pool (copy-on-write copies), one JSON line of its own")
+    ap.add_argument("--pairs", type=int, default=4096, help="copy_blocks: block pairs per launch")
     return ap.parse_args()
+
+
+def bench_copy_blocks(args):
+    """pa_copy_blocks on the workload's pool shape: `pairs` random (source,
+    destination) block pairs per launch, timed with HIP events."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_150_amd as pa
+    import workloads as W
+    pa.load_library()
+    cfg = W.CONFIG_BY_NAME[args.config]
+    shape = (cfg.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_size)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    kc = torch.zeros(shape, dtype=tdt, device="cuda")
+    vc = torch.zeros(shape, dtype=tdt, device="cuda")
+    rng = np.random.default_rng(0)
+    maps = []
+    for _ in range(2):
+        ids = rng.permutation(cfg.num_blocks)
+        maps.append(torch.from_numpy(np.stack([ids[:args.pairs], ids[args.pairs:2 * args.pairs]], 1)
+                                     .astype(np.int64)).cuda())
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        pa.pa_copy_blocks(kc, vc, maps[i & 1], stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pa.pa_copy_blocks(kc, vc, maps[i & 1], stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    block_bytes = cfg.block_size * cfg.num_kv_heads * cfg.head_size * (2 if cfg.dtype == "bf16" else 4)
+    moved = 2 * 2 * args.pairs * block_bytes  # K and V, read + write
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "pa_copy_blocks HBM GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "pairs": args.pairs, "block_bytes": block_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa::copy_blocks_kernel", "algorithmic_bytes_per_launch": moved}}))
 
 
 def copy_calibration(mib: int):
@@ -127,6 +174,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args)
         return
 
     import paged_kv_cache_150_amd as pa

@@ -95,6 +95,29 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
                          int32_t dtype, void* stream);
 
 /*
+ * pa_copy_blocks - whole-block copies: the GPU half of copy-on-write.
+ *
+ * When a sequence must write into a block that others still read, it gets a
+ * fresh block holding a copy of the shared one (llm-stack-book 7.3, section
+ * "Copy-on-write for shared blocks"; the host side is pa_pool_make_writable in
+ * pa_pool.h). For every pair p, block block_mapping[p][1] of both caches
+ * receives block block_mapping[p][0] (all block_size token rows, all kv
+ * heads), bitwise.
+ *
+ *   key_cache,
+ *   value_cache       [num_blocks, block_size, num_kv_heads, head_size], device.
+ *   block_mapping     int64 [num_pairs, 2] (source, destination), device. A
+ *                     pair naming a block outside [0, num_blocks) is skipped.
+ *                     Destinations must be distinct and must not be the source
+ *                     of another pair (the pairs run in parallel).
+ *   num_pairs         may be 0 (nothing is launched).
+ * Returns PA_OK or an error status.
+ */
+int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping, int64_t num_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                   int32_t dtype, void* stream);
+
+/*
  * pa_decode - one decode step of paged attention, one pass over each context.
  *
  * For every sequence i and query head h, with n = context_lens[i] and

@@ -17,7 +17,7 @@
  *    block goes back to the free list when nobody holds it;
  *  - a sequence about to write into a block others hold gets a private copy
  *    first (copy-on-write): the caller then copies the block's K/V on the GPU
- *    (pa_copy_blocks, when built, or any device copy);
+ *    (pa_copy_blocks in pa.h);
  *  - pa_prepare_step turns the tables into what the GPU kernels take: a slot
  *    per token being written, its position, padded block tables and context
  *    lengths.

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library",
-    "pa_reshape_and_cache", "pa_decode", "pa_decode_split_workspace_bytes", "pa_decode_split",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_split_workspace_bytes", "pa_decode_split",
     "pa_merge_partitions", "pa_status_string",
 ]
 
@@ -54,6 +54,8 @@ def load_library() -> ctypes.CDLL:
                                           ctypes.c_void_p, ctypes.c_size_t)
     lib.pa_reshape_and_cache.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
     lib.pa_reshape_and_cache.restype = c_int
+    lib.pa_copy_blocks.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
+    lib.pa_copy_blocks.restype = c_int
     lib.pa_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
                               c_f, c_i32, c_p, c_p, c_p]
     lib.pa_decode.restype = c_int
@@ -136,6 +138,19 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
                                   _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d,
                                   _dtype_code(key_cache), _stream(stream))
     _check(st, "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mapping: torch.Tensor,
+                   stream=None) -> None:
+    """Copy whole blocks: block_mapping int64 [num_pairs, 2] of (source, destination)."""
+    NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
+    if block_mapping.dim() != 2 or int(block_mapping.shape[1]) != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    lib = load_library()
+    st = lib.pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                            _dev(block_mapping, "block_mapping", torch.int64, 2), int(block_mapping.shape[0]), NB,
+                            bs, Hkv, d, _dtype_code(key_cache), _stream(stream))
+    _check(st, "pa_copy_blocks")
 
 
 def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens, lse_out):

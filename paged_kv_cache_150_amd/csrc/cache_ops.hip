@@ -34,6 +34,39 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const u32x4_t* _
   }
 }
 
+// pa_copy_blocks: workgroup (pair, cache) copies one whole block, source to
+// destination (the GPU half of copy-on-write: llm-stack-book 7.3, section
+// "Copy-on-write for shared blocks"). Each thread keeps kCopyBatch 16-byte
+// pieces in flight before storing them; the pair's ids are wave-uniform
+// scalar loads. Pairs naming a block outside the pool are skipped.
+constexpr int kCopyBatch = 8;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ key_cache,
+                                                          u32x4_t* __restrict__ value_cache,
+                                                          const int64_t* __restrict__ block_mapping,
+                                                          int64_t num_blocks, int64_t block_pieces) {
+  const int64_t src = block_mapping[2 * static_cast<int64_t>(blockIdx.x)];
+  const int64_t dst = block_mapping[2 * static_cast<int64_t>(blockIdx.x) + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  u32x4_t* cache = blockIdx.y == 0 ? key_cache : value_cache;
+  const u32x4_t* from = cache + src * block_pieces;
+  u32x4_t* to = cache + dst * block_pieces;
+  const int64_t step = static_cast<int64_t>(blockDim.x) * kCopyBatch;
+  for (int64_t base = threadIdx.x; base < block_pieces; base += step) {
+    u32x4_t v[kCopyBatch];
+#pragma unroll
+    for (int i = 0; i < kCopyBatch; ++i) {
+      const int64_t j = base + static_cast<int64_t>(i) * blockDim.x;
+      if (j < block_pieces) v[i] = from[j];
+    }
+#pragma unroll
+    for (int i = 0; i < kCopyBatch; ++i) {
+      const int64_t j = base + static_cast<int64_t>(i) * blockDim.x;
+      if (j < block_pieces) to[j] = v[i];
+    }
+  }
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -77,4 +110,24 @@ extern "C" const char* pa_status_string(int status) {
     case PA_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
     default: return "unknown status";
   }
+}
+
+extern "C" int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                              int64_t num_pairs, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_size, int32_t dtype, void* stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache);
+  if (mis & 15u) return PA_ERR_INVALID_ARG;
+  if (num_pairs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int64_t block_bytes =
+      static_cast<int64_t>(kBlockTokens) * num_kv_heads * head_size * (dtype == PA_DTYPE_F32 ? 4 : 2);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(num_pairs), 2), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<u32x4_t*>(key_cache),
+                     static_cast<u32x4_t*>(value_cache), block_mapping, num_blocks, block_bytes / 16);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

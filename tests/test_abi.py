@@ -31,8 +31,8 @@ def declared_functions(header=None):
 def test_headers_declare_the_boundary():
     inc = os.path.join(ROOT, "include")
     assert declared_functions(os.path.join(inc, "pa.h")) == sorted([
-        "pa_reshape_and_cache", "pa_decode", "pa_decode_split_workspace_bytes", "pa_decode_split",
-        "pa_merge_partitions", "pa_status_string"])
+        "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_split_workspace_bytes",
+        "pa_decode_split", "pa_merge_partitions", "pa_status_string"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
         "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
         "pa_pool_allocate", "pa_pool_append_slot", "pa_pool_share", "pa_pool_release",
@@ -122,3 +122,13 @@ def test_binding_refuses_host_tensors():
         pa.pa_decode(torch.empty_like(q), q, kc, kc.clone(), bt, cl, 0.1)
     with pytest.raises(ValueError):
         pa.pa_decode(torch.empty_like(q), q, kc, kc.clone(), bt[:1], cl, 0.1)
+
+
+def test_copy_blocks_host_validation(lib):
+    f = lib.pa_copy_blocks
+    assert f(16, 16, 16, 0, 10, 16, 2, 128, 1, None) == 0        # nothing to do
+    assert f(16, 16, 16, 4, 10, 8, 2, 128, 1, None) == 2         # block size
+    assert f(16, 16, None, 4, 10, 16, 2, 128, 1, None) == 1      # no mapping
+    assert f(16, 8, 16, 4, 10, 16, 2, 128, 1, None) == 1         # misaligned cache
+    assert f(16, 16, 16, -1, 10, 16, 2, 128, 1, None) == 1       # negative count
+    assert f(16, 16, 16, 4, 10, 16, 2, 96, 1, None) == 2         # head size
