@@ -38,3 +38,12 @@ from .block_pool import (  # noqa: F401
     PoolError,
     prepare_step,
 )
+from .fp8 import (  # noqa: F401
+    FP8_MAX,
+    fp8_value,
+    fp8_encode,
+    quantize,
+    dequantize,
+    reshape_and_cache_fp8,
+    paged_decode_fp8,
+)

@@ -38,6 +38,8 @@ def decode_values(x: np.ndarray, dtype: str) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(dtype)
 
 
@@ -86,12 +88,15 @@ def attention_contiguous(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: flo
 
 def paged_decode(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
                  block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
-                 dtype: str, block_size: int = 16, seqs=None):
+                 dtype: str, block_size: int = 16, seqs=None, kv_dtype: str | None = None):
     """Decode-step attention for every sequence, reading K/V through the block table.
 
     Returns (out [S, H_q, d_h], lse [S, H_q]) in float64. ``seqs`` optionally
     restricts the work to a subset of sequence indices (the rest stay NaN).
+    ``kv_dtype`` names the caches' storage when it differs from the query's
+    ("f64": values already decoded, as for FP8 caches).
     """
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     S, Hq, d = query.shape
     out = np.full((S, Hq, d), np.nan, dtype=np.float64)
     lse = np.full((S, Hq), np.nan, dtype=np.float64)
@@ -100,8 +105,8 @@ def paged_decode(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarr
         n = int(context_lens[i])
         Kc, Vc = gather_context(key_cache, value_cache, block_tables[i], n, block_size)
         q = decode_values(query[i], dtype)
-        out[i], lse[i] = attention_contiguous(q, decode_values(Kc, dtype),
-                                              decode_values(Vc, dtype), scale)
+        out[i], lse[i] = attention_contiguous(q, decode_values(Kc, kv_dtype),
+                                              decode_values(Vc, kv_dtype), scale)
     return out, lse
 
 
