@@ -141,8 +141,12 @@ def cpu_baseline(cfg, inp, budget_s: float):
         threads = 1
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
-                            cfg.scale, cfg.dtype)
+        if cfg.cache_dtype == "fp8":
+            oracle.paged_decode_fp8(inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                                    inp.context_lens, cfg.scale, cfg.k_scale, cfg.v_scale)
+        else:
+            oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
+                                cfg.scale, cfg.dtype)
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -199,6 +203,11 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    fp8 = cfg.cache_dtype == "fp8"
+    if fp8 and args.decode != "fused":
+        print("bench.py: FP8 caches have the fused decode only (pa_decode_fp8)", file=sys.stderr)
+        sys.exit(2)
+
     # Two resident copies of the pool (same contents), used on alternate steps.
     pools = [(up(inp.key_cache), up(inp.value_cache)) for _ in range(2)]
     q, bt, cl = up(inp.query), up(inp.block_tables), up(inp.context_lens)
@@ -214,14 +223,23 @@ def main():
     stream = torch.cuda.current_stream()
 
     def decode(kc, vc):
-        if args.decode == "fused":
+        if fp8:
+            pa.pa_decode_fp8(out, q, kc, vc, bt, cl, cfg.scale, cfg.k_scale, cfg.v_scale, seq_order=order,
+                             stream=stream)
+        elif args.decode == "fused":
             pa.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, seq_order=order, stream=stream)
         else:
             pa.pa_decode_split(out, q, kc, vc, bt, cl, cfg.scale, mcl, P, ws, stream=stream)
 
+    def reshape(kc, vc):
+        if fp8:
+            pa.pa_reshape_and_cache_fp8(new_k, new_v, kc, vc, slots, cfg.k_scale, cfg.v_scale, stream=stream)
+        else:
+            pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+
     def step(i):
         kc, vc = pools[i & 1]
-        pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+        reshape(kc, vc)
         decode(kc, vc)
 
     print(f"[bench] warmup {args.warmup}, timed {args.steps} steps", file=sys.stderr, flush=True)
@@ -239,7 +257,7 @@ def main():
     t_begin.record(stream)
     for i in range(args.steps):
         kc, vc = pools[i & 1]
-        pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+        reshape(kc, vc)
         ev[i][0].record(stream)
         decode(kc, vc)
         ev[i][1].record(stream)
@@ -274,8 +292,10 @@ def main():
                    "num_blocks": cfg.num_blocks, "mean_context": float(inp.context_lens.mean()),
                    "decode": args.decode, "partition_size": P if args.decode == "split" else None,
                    "seq_order": args.order if args.decode == "fused" else None,
-                   "step": "pa_reshape_and_cache + " + ("pa_decode" if args.decode == "fused" else
-                                                        "pa_decode_split")},
+                   "kv_cache": cfg.cache_dtype,
+                   "step": ("pa_reshape_and_cache_fp8 + pa_decode_fp8" if fp8 else
+                            "pa_reshape_and_cache + " + ("pa_decode" if args.decode == "fused" else
+                                                         "pa_decode_split"))},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

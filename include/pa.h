@@ -95,6 +95,47 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
                          int32_t dtype, void* stream);
 
 /*
+ * FP8 KV caches.
+ *
+ * The pages name an FP8 KV cache as a way to enlarge the pool (llm-stack-book
+ * 7.3, "Running vLLM well in practice", item 5) without fixing a format. This
+ * library's reading: caches hold OCP FP8 E4M3 codes (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; largest finite 448; S.1111.111 is NaN; no
+ * infinity), one code per element, in the same [num_blocks, block_size,
+ * num_kv_heads, head_size] layout, with one float32 scale per cache (k_scale,
+ * v_scale > 0). A value x is stored as the code nearest to float32(x)/scale
+ * (IEEE float32 division; ties to even; magnitudes above 448, infinities
+ * included, saturate to 448; NaN is stored as a NaN code with x's sign) and
+ * reads back as value(code) * scale.
+ */
+
+/*
+ * pa_reshape_and_cache_fp8 - pa_reshape_and_cache into FP8 caches: each new
+ * token's K and V (dtype: PA_DTYPE_BF16 or PA_DTYPE_F32, 16-byte aligned) are
+ * quantized with k_scale / v_scale and written to their slot (caches 8-byte
+ * aligned). Negative and out-of-pool slots are skipped.
+ */
+int pa_reshape_and_cache_fp8(const void* key, const void* value, uint8_t* key_cache, uint8_t* value_cache,
+                             const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                             int32_t block_size, int32_t num_kv_heads, int32_t head_size, int32_t dtype,
+                             float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode_fp8 - pa_decode over FP8 caches: attention on the caches' values
+ * value(code) * scale. Query and out are bf16 (dtype PA_DTYPE_BF16; anything
+ * else is PA_ERR_UNSUPPORTED); lse_out and seq_order as for pa_decode. The
+ * keys' scale folds into the scores (s_t = scale * k_scale * <q, K_code_t>),
+ * the values' into the normalised output; every code converts exactly to
+ * bf16/float32, so this reads half the bytes of a bf16 cache for the same
+ * arithmetic on the stored values.
+ */
+int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                  int32_t block_size, float scale, float k_scale, float v_scale, int32_t dtype, float* lse_out,
+                  const int32_t* seq_order, void* stream);
+
+/*
  * pa_copy_blocks - whole-block copies: the GPU half of copy-on-write.
  *
  * When a sequence must write into a block that others still read, it gets a

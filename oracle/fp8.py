@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paged_attention import decode_values, paged_decode
+from .paged_attention import attention_contiguous, decode_values, gather_context
 
 FP8_MAX = 448.0
 
@@ -88,8 +88,17 @@ def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_sc
 
 
 def paged_decode_fp8(query, key_cache, value_cache, block_tables, context_lens, scale: float,
-                     k_scale: float, v_scale: float, q_dtype: str = "bf16"):
-    """Paged decode over FP8 caches: the caches' values are code values times
-    their scale, then ordinary paged attention in float64."""
-    return paged_decode(query, dequantize(key_cache, k_scale), dequantize(value_cache, v_scale),
-                        block_tables, context_lens, scale, q_dtype, kv_dtype="f64")
+                     k_scale: float, v_scale: float, q_dtype: str = "bf16", block_size: int = 16, seqs=None):
+    """Paged decode over FP8 caches: each sequence's codes are gathered through
+    its block table, read as code value times scale, and attended in float64
+    (only the blocks a sequence owns are decoded, so pools of any size fit).
+    ``seqs`` optionally restricts the work to some sequences (the rest: NaN)."""
+    S, Hq, d = query.shape
+    out = np.full((S, Hq, d), np.nan)
+    lse = np.full((S, Hq), np.nan)
+    for i in (range(S) if seqs is None else seqs):
+        n = int(context_lens[i])
+        Kc, Vc = gather_context(key_cache, value_cache, block_tables[i], n, block_size)
+        out[i], lse[i] = attention_contiguous(decode_values(query[i], q_dtype), dequantize(Kc, k_scale),
+                                              dequantize(Vc, v_scale), scale)
+    return out, lse

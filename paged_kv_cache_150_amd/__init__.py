@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library",
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_split_workspace_bytes", "pa_decode_split",
+    "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
+    "pa_decode_split_workspace_bytes", "pa_decode_split",
     "pa_merge_partitions", "pa_status_string",
 ]
 
@@ -54,6 +55,12 @@ def load_library() -> ctypes.CDLL:
                                           ctypes.c_void_p, ctypes.c_size_t)
     lib.pa_reshape_and_cache.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
     lib.pa_reshape_and_cache.restype = c_int
+    lib.pa_reshape_and_cache_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
+                                             c_f, c_f, c_p]
+    lib.pa_reshape_and_cache_fp8.restype = c_int
+    lib.pa_decode_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
+                                  c_f, c_f, c_f, c_i32, c_p, c_p, c_p]
+    lib.pa_decode_fp8.restype = c_int
     lib.pa_copy_blocks.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p]
     lib.pa_copy_blocks.restype = c_int
     lib.pa_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
@@ -153,12 +160,17 @@ def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_map
     _check(st, "pa_copy_blocks")
 
 
-def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens, lse_out):
+def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens, lse_out, fp8=False):
     NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
     if query.dim() != 3 or int(query.shape[2]) != d:
         raise ValueError("query must be [num_seqs, num_heads, head_size]")
     S, Hq = int(query.shape[0]), int(query.shape[1])
-    if out.shape != query.shape or out.dtype != query.dtype or query.dtype != key_cache.dtype:
+    if fp8:
+        if key_cache.dtype != torch.uint8:
+            raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+        if out.shape != query.shape or out.dtype != query.dtype:
+            raise ValueError("out must match query's shape and dtype")
+    elif out.shape != query.shape or out.dtype != query.dtype or query.dtype != key_cache.dtype:
         raise ValueError("out must match query's shape; query, out and caches share one dtype")
     if block_tables.dim() != 2 or int(block_tables.shape[0]) != S:
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
@@ -196,6 +208,45 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
     st = lib.pa_decode(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
                        float(scale), _dtype_code(query), p["lse"], order_ptr, _stream(stream))
     _check(st, "pa_decode")
+
+
+def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float, v_scale: float,
+                             stream=None) -> None:
+    """Quantize key[t], value[t] to E4M3 codes (uint8 caches) at slot_mapping[t]."""
+    NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
+    if key_cache.dtype != torch.uint8:
+        raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (Hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_size] matching the cache")
+    T = int(key.shape[0])
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    lib = load_library()
+    st = lib.pa_reshape_and_cache_fp8(_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+                                      _dev(value_cache, "value_cache"),
+                                      _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d,
+                                      _dtype_code(key), float(k_scale), float(v_scale), _stream(stream))
+    _check(st, "pa_reshape_and_cache_fp8")
+
+
+def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, k_scale: float,
+                  v_scale: float, lse_out: torch.Tensor | None = None, seq_order: torch.Tensor | None = None,
+                  stream=None) -> None:
+    """pa_decode over FP8 (E4M3 code) caches with scales k_scale, v_scale; bf16 query/out."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out, fp8=True)
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.shape != (S,):
+            raise ValueError("seq_order must be [num_seqs]")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
+    lib = load_library()
+    st = lib.pa_decode_fp8(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
+                           float(scale), float(k_scale), float(v_scale), _dtype_code(query), p["lse"], order_ptr,
+                           _stream(stream))
+    _check(st, "pa_decode_fp8")
 
 
 def pa_decode_split_workspace_bytes(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,

@@ -34,6 +34,79 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const u32x4_t* _
   }
 }
 
+// pa_reshape_and_cache_fp8: the quantizing scatter. A thread turns 8 values
+// of a token row (bf16 or float32) into 8 E4M3 codes: x / scale in float32
+// (IEEE division, round to nearest), magnitudes above 448 (infinities
+// included) clamped to 448, NaN written as S.1111.111 with x's sign, and the
+// rest converted by the hardware to the nearest code, ties to even. The format
+// and the scale are this library's reading: the pages name an FP8 KV cache
+// without fixing one (llm-stack-book 7.3, "Running vLLM well in practice").
+__device__ __forceinline__ uint32_t quantize4_e4m3(float a, float b, float c, float d, float scale) {
+  float v[4] = {__fdiv_rn(a, scale), __fdiv_rn(b, scale), __fdiv_rn(c, scale), __fdiv_rn(d, scale)};
+  uint32_t nan_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] != v[i]) {
+      nan_bits |= ((__builtin_bit_cast(uint32_t, v[i]) >> 31) << 7 | 0x7Fu) << (8 * i);
+      v[i] = 0.f;
+    } else {
+      v[i] = fminf(fmaxf(v[i], -448.f), 448.f);
+    }
+  }
+  uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
+  w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], static_cast<int>(w), true));
+  // NaN lanes were converted as zero (code 0): OR in their NaN code.
+  return w | nan_bits;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(const T* __restrict__ key,
+                                                                    const T* __restrict__ value,
+                                                                    u32x2_t* __restrict__ key_cache,
+                                                                    u32x2_t* __restrict__ value_cache,
+                                                                    const int64_t* __restrict__ slot_mapping,
+                                                                    int64_t num_tokens, int64_t num_slots,
+                                                                    int row_groups, float k_scale, float v_scale) {
+  // One group = 8 consecutive elements of a token row = one 8-byte piece of
+  // its cache row.
+  const int64_t total = num_tokens * row_groups;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t t = i / row_groups;
+    const int64_t grp = i - t * row_groups;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;  // padding token, or a slot outside the pool
+    float k[8], v[8];
+    if constexpr (sizeof(T) == 2) {
+      const u32x4_t kw = reinterpret_cast<const u32x4_t*>(key)[i];
+      const u32x4_t vw = reinterpret_cast<const u32x4_t*>(value)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[2 * e] = bf16_lo(kw[e]);
+        k[2 * e + 1] = bf16_hi(kw[e]);
+        v[2 * e] = bf16_lo(vw[e]);
+        v[2 * e + 1] = bf16_hi(vw[e]);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t kw = reinterpret_cast<const u32x4_t*>(key)[2 * i + h];
+        const u32x4_t vw = reinterpret_cast<const u32x4_t*>(value)[2 * i + h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k[4 * h + e] = as_float(kw[e]);
+          v[4 * h + e] = as_float(vw[e]);
+        }
+      }
+    }
+    const int64_t dst = slot * row_groups + grp;
+    key_cache[dst] = u32x2_t{quantize4_e4m3(k[0], k[1], k[2], k[3], k_scale),
+                             quantize4_e4m3(k[4], k[5], k[6], k[7], k_scale)};
+    value_cache[dst] = u32x2_t{quantize4_e4m3(v[0], v[1], v[2], v[3], v_scale),
+                               quantize4_e4m3(v[4], v[5], v[6], v[7], v_scale)};
+  }
+}
+
 // pa_copy_blocks: workgroup (pair, cache) copies one whole block, source to
 // destination (the GPU half of copy-on-write: llm-stack-book 7.3, section
 // "Copy-on-write for shared blocks"). Each thread keeps kCopyBatch 16-byte
@@ -129,5 +202,43 @@ extern "C" int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t*
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(num_pairs), 2), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<u32x4_t*>(key_cache),
                      static_cast<u32x4_t*>(value_cache), block_mapping, num_blocks, block_bytes / 16);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, uint8_t* key_cache,
+                                        uint8_t* value_cache, const int64_t* slot_mapping, int64_t num_tokens,
+                                        int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                        int32_t head_size, int32_t dtype, float k_scale, float v_scale,
+                                        void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value);
+  if ((mis & 15u) || ((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) & 7u))
+    return PA_ERR_INVALID_ARG;
+  const int64_t row_groups = static_cast<int64_t>(num_kv_heads) * head_size / 8;
+  if (row_groups > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int64_t total = num_tokens * row_groups;
+  constexpr int kThreads = 256;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PA_DTYPE_BF16)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       s, static_cast<const bf16_t*>(key), static_cast<const bf16_t*>(value),
+                       reinterpret_cast<u32x2_t*>(key_cache), reinterpret_cast<u32x2_t*>(value_cache),
+                       slot_mapping, num_tokens, num_blocks * kBlockTokens, static_cast<int>(row_groups), k_scale,
+                       v_scale);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       s, static_cast<const float*>(key), static_cast<const float*>(value),
+                       reinterpret_cast<u32x2_t*>(key_cache), reinterpret_cast<u32x2_t*>(value_cache),
+                       slot_mapping, num_tokens, num_blocks * kBlockTokens, static_cast<int>(row_groups), k_scale,
+                       v_scale);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

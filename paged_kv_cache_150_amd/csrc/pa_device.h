@@ -87,6 +87,34 @@ __device__ __forceinline__ u32x4_t gload16(const gchar_t* p) {
 }
 
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// FP8 E4M3 (OCP) codes to float32, two at a time with the hardware converter:
+// bytes 0,1 (hi = false) or 2,3 (hi = true) of w. On gfx950 the converter reads
+// the OCP E4M3 format (finite values up to 448, S.1111.111 = NaN) and every
+// code's value is exact in float32.
+template <bool HI>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+  a = v[0];
+  b = v[1];
+}
+
+// Eight FP8 codes (two dwords) to eight bf16 values, the MFMA operand. Every
+// E4M3 value is exact in bfloat16 (3 mantissa bits, exponents 2^-9 .. 2^8), so
+// keeping the upper half of the float32 is exact.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  uint32_t out[4];
+  const uint32_t w[2] = {w0, w1};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float a, b, c, d;
+    fp8x2_to_f32<false>(w[i], a, b);
+    fp8x2_to_f32<true>(w[i], c, d);
+    out[2 * i] = (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u) | (__builtin_bit_cast(uint32_t, a) >> 16);
+    out[2 * i + 1] = (__builtin_bit_cast(uint32_t, d) & 0xFFFF0000u) | (__builtin_bit_cast(uint32_t, c) >> 16);
+  }
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{out[0], out[1], out[2], out[3]});
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
@@ -108,7 +136,9 @@ __device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, float x) { *p = f3
 // Load `NDW` dwords (8, 16 or 32 bytes) that are 16-byte (or 8-byte) aligned.
 template <int NDW>
 __device__ __forceinline__ void load_dwords(uint32_t (&dst)[NDW], const gchar_t* src) {
-  if constexpr (NDW == 2) {
+  if constexpr (NDW == 1) {
+    dst[0] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(src);
+  } else if constexpr (NDW == 2) {
     u32x2_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t*>(src);
     dst[0] = v[0];
     dst[1] = v[1];

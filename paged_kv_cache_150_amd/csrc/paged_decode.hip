@@ -41,19 +41,23 @@
 
 namespace pa {
 
-template <typename T, int D, int G, int CB>
+// T: query/output element; F8: the caches hold FP8 E4M3 codes (with bf16
+// queries) instead of T.
+template <typename T, int D, int G, int CB, bool F8 = false>
 struct DecodeShape {
-  static constexpr int kElemBytes = static_cast<int>(sizeof(T));
+  static constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));  // cache element
   static constexpr int kKSeg = D * kElemBytes / 64;  // 16-byte K loads per lane per block
+  static constexpr int kQSeg = F8 ? 2 * kKSeg : kKSeg;  // 16-byte query pieces per lane (MFMA k-steps)
   static constexpr int kVec = D / 16;                // V elements per lane per token
   static constexpr int kVDw = kVec * kElemBytes / 4; // ... as dwords
-  static_assert(kKSeg >= 1 && kVDw >= 2, "shape");
+  static_assert(kKSeg >= 1 && kVDw >= 1, "shape");
   static_assert(G >= 1 && G <= 16, "group");
+  static_assert(!F8 || sizeof(T) == 2, "FP8 caches take bf16 queries");
 };
 
-template <typename T, int D, int G, int CB>
+template <typename T, int D, int G, int CB, bool F8 = false>
 struct Chunk {
-  using S = DecodeShape<T, D, G, CB>;
+  using S = DecodeShape<T, D, G, CB, F8>;
   u32x4_t k[CB][S::kKSeg];
   uint32_t v[CB][4][S::kVDw];
 };
@@ -74,7 +78,8 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t group;        // H_q / H_kv
   int32_t num_jobs;     // job ids: ceil(num_seqs / 8) * 8 * num_kv_heads
-  float scale_log2;     // scale * log2(e)
+  float scale_log2;     // scale * log2(e) (times k_scale for FP8 caches)
+  float v_scale;        // multiplies the normalised output: v_scale for FP8 caches, else 1
 };
 
 // Workgroup -> (sequence, kv head). Consecutive workgroups are dispatched to
@@ -91,13 +96,13 @@ __device__ __forceinline__ void wg_to_seq_head(int id, int num_kv_heads, int& se
 // Loads one chunk (CB blocks) of K and V for this wave's kv head. Block ids
 // are wave-uniform, so each load is a scalar base (block, head, row) plus a
 // 32-bit per-lane offset.
-template <typename T, int D, int G, int CB>
-__device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB>& f, const char* kc, const char* vc,
+template <typename T, int D, int G, int CB, bool F8 = false>
+__device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
                                            const int32_t* bt_row, int blk0, int blk_last,
                                            int64_t num_blocks, uint32_t tok_stride_bytes,
                                            int64_t blk_stride_bytes, int64_t head_off_bytes,
                                            int lane) {
-  using S = DecodeShape<T, D, G, CB>;
+  using S = DecodeShape<T, D, G, CB, F8>;
   const int tok = lane & 15;
   const int j = lane >> 4;
   const uint32_t koff = tok * tok_stride_bytes + j * 16;                      // K: row tok, piece j
@@ -129,16 +134,24 @@ struct WaveState {
 
 // Scores of one chunk: s[i][r] = scale*log2(e) * <q, K> for token 4*(lane/16)+r
 // of block i and head lane % 16.
-template <typename T, int D, int G, int CB>
-__device__ __forceinline__ void qk_chunk(float (&s)[CB][4], const Chunk<T, D, G, CB>& f,
-                                         const u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg], float scale_log2) {
-  using S = DecodeShape<T, D, G, CB>;
+template <typename T, int D, int G, int CB, bool F8 = false>
+__device__ __forceinline__ void qk_chunk(float (&s)[CB][4], const Chunk<T, D, G, CB, F8>& f,
+                                         const u32x4_t (&q)[DecodeShape<T, D, G, CB, F8>::kQSeg],
+                                         float scale_log2) {
+  using S = DecodeShape<T, D, G, CB, F8>;
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sg = 0; sg < S::kKSeg; ++sg) {
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (F8) {
+        // 16 codes per load: dwords 0-1 feed k-step 2*sg, dwords 2-3 k-step
+        // 2*sg+1, converted exactly to bf16 (the query uses the same d order).
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(f.k[i][sg][2 * h], f.k[i][sg][2 * h + 1]),
+                                                      __builtin_bit_cast(bf16x8_t, q[2 * sg + h]), c, 0, 0, 0);
+      } else if constexpr (sizeof(T) == 2) {
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[i][sg]),
                                                     __builtin_bit_cast(bf16x8_t, q[sg]), c, 0, 0, 0);
       } else {
@@ -155,10 +168,10 @@ __device__ __forceinline__ void qk_chunk(float (&s)[CB][4], const Chunk<T, D, G,
 }
 
 // Online-softmax update and P*V for one chunk whose scores are in s.
-template <typename T, int D, int G, int CB>
-__device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB>& f,
+template <typename T, int D, int G, int CB, bool F8 = false>
+__device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB, F8>& f,
                                                  float (&s)[CB][4], int tok0, int t_end, bool mask, int lane) {
-  using S = DecodeShape<T, D, G, CB>;
+  using S = DecodeShape<T, D, G, CB, F8>;
   const int rg = lane >> 4;
   // The chunk that straddles the end of the context: positions >= t_end get
   // weight exactly 0 and their V rows (stale or poisoned) are replaced by 0.
@@ -211,7 +224,13 @@ __device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, con
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float vf[S::kVec];
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (F8) {
+#pragma unroll
+        for (int w = 0; w < S::kVDw; ++w) {
+          fp8x2_to_f32<false>(vz[i][r][w], vf[4 * w], vf[4 * w + 1]);
+          fp8x2_to_f32<true>(vz[i][r][w], vf[4 * w + 2], vf[4 * w + 3]);
+        }
+      } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int w = 0; w < S::kVDw; ++w) {
           vf[2 * w] = bf16_lo(vz[i][r][w]);
@@ -231,26 +250,32 @@ __device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, con
     }
 }
 
-template <typename T, int D, int G, int CB>
-__device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB>& f,
-                                              const u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg],
+template <typename T, int D, int G, int CB, bool F8 = false>
+__device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB, F8>& f,
+                                              const u32x4_t (&q)[DecodeShape<T, D, G, CB, F8>::kQSeg],
                                               float scale_log2, int tok0, int t_end, bool mask, int lane) {
   float s[CB][4];
-  qk_chunk<T, D, G, CB>(s, f, q, scale_log2);
-  softmax_pv_chunk<T, D, G, CB>(st, f, s, tok0, t_end, mask, lane);
+  qk_chunk<T, D, G, CB, F8>(s, f, q, scale_log2);
+  softmax_pv_chunk<T, D, G, CB, F8>(st, f, s, tok0, t_end, mask, lane);
 }
 
-template <typename T, int D, int G, int CB>
+template <typename T, int D, int G, int CB, bool F8 = false>
 __device__ __forceinline__ void load_query(const void* query, int seq, int num_heads, int head0, int g, int lane,
-                                           u32x4_t (&q)[DecodeShape<T, D, G, CB>::kKSeg]) {
-  using S = DecodeShape<T, D, G, CB>;
+                                           u32x4_t (&q)[DecodeShape<T, D, G, CB, F8>::kQSeg]) {
+  using S = DecodeShape<T, D, G, CB, F8>;
+  constexpr int kQBytes = static_cast<int>(sizeof(T));
   const int hq = lane & 15;
+  const int j = lane >> 4;
   const gchar_t* qb = uniform_ptr(static_cast<const char*>(query) +
-                                  (static_cast<int64_t>(seq) * num_heads + head0) * D * S::kElemBytes);
-  const uint32_t qoff = (hq < g ? hq : 0) * (D * S::kElemBytes) + (lane >> 4) * 16;
+                                  (static_cast<int64_t>(seq) * num_heads + head0) * D * kQBytes);
+  const uint32_t qoff = (hq < g ? hq : 0) * (D * kQBytes);
 #pragma unroll
-  for (int sg = 0; sg < S::kKSeg; ++sg) {
-    u32x4_t v = gload16(qb + sg * 64 + qoff);
+  for (int sg = 0; sg < S::kQSeg; ++sg) {
+    // Same d order as the K operand: for bf16 caches k-step sg holds
+    // d = 32 sg + 8 j + e; for FP8 caches (16 codes per lane per load)
+    // d = 64 (sg / 2) + 16 j + 8 (sg % 2) + e.
+    const uint32_t off = F8 ? 128 * (sg / 2) + 32 * j + 16 * (sg % 2) : sg * 64 + j * 16;
+    u32x4_t v = gload16(qb + off + qoff);
     q[sg] = hq < g ? v : u32x4_t{0u, 0u, 0u, 0u};
   }
 }
@@ -304,11 +329,11 @@ struct JobPlan {
   int mask_chunk;  // the chunk that reaches past the context end, or -1
 };
 
-template <typename T, int D, int CB>
+template <int EB, int D, int CB>  // EB: bytes per cache element
 __device__ __forceinline__ JobPlan plan_job(const DecodeArgs& a, const DecodeJob& j, int wave, int nwaves) {
   JobPlan p;
   p.bt_row = a.block_tables + static_cast<int64_t>(j.seq < 0 ? 0 : j.seq) * a.max_blocks;
-  p.head_off = static_cast<int64_t>(j.kvh) * D * static_cast<int>(sizeof(T));
+  p.head_off = static_cast<int64_t>(j.kvh) * D * EB;
   const int blk_end = (j.n + kBlockTokens - 1) / kBlockTokens;
   const int nchunk = (blk_end + CB - 1) / CB;
   p.blk_last = blk_end - 1;
@@ -323,9 +348,9 @@ __device__ __forceinline__ JobPlan plan_job(const DecodeArgs& a, const DecodeJob
 // between jobs.
 // Two workgroups per CU (at most 256 registers per lane); the 16-head group
 // needs more registers and runs one workgroup per CU.
-template <typename T, int D, int G, int CB, bool PF>
+template <typename T, int D, int G, int CB, bool PF, bool F8 = false>
 __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(DecodeArgs a) {
-  using S = DecodeShape<T, D, G, CB>;
+  using S = DecodeShape<T, D, G, CB, F8>;
   extern __shared__ float s_acc[];  // [W][G][D]
   __shared__ float s_m[8][16];
   __shared__ float s_l[8][16];
@@ -351,16 +376,16 @@ __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(Deco
   cur.kvh = 0;
   cur.n = 0;
   if (id0 < a.num_jobs) cur = decode_job(a, id0);
-  JobPlan pc = plan_job<T, D, CB>(a, cur, wave, nwaves);
+  JobPlan pc = plan_job<S::kElemBytes, D, CB>(a, cur, wave, nwaves);
   // Block of this wave's i-th chunk of a job.
   auto blk_of = [&](int i) { return (wave + i * nwaves) * CB; };
 
-  u32x4_t q[S::kKSeg];
-  Chunk<T, D, G, CB> fa;
+  u32x4_t q[S::kQSeg];
+  Chunk<T, D, G, CB, F8> fa;
   if (cur.n > 0 && cur.seq >= 0) {
-    load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
+    load_query<T, D, G, CB, F8>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
     if (PF && pc.mine > 0)
-      load_chunk<T, D, G, CB>(fa, kc, vc, pc.bt_row, blk_of(0), pc.blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, G, CB, F8>(fa, kc, vc, pc.bt_row, blk_of(0), pc.blk_last, a.num_blocks, tok_stride,
                               blk_stride, pc.head_off, lane);
   }
   int id = id0;
@@ -393,45 +418,45 @@ __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(Deco
       // barriers keep the loads ahead of the current chunk's arithmetic (left
       // alone, the scheduler sinks them to shorten register live ranges).
       // Only the final chunk of the context, a wave's last, can need a mask.
-      Chunk<T, D, G, CB> fb;
+      Chunk<T, D, G, CB, F8> fb;
       if (mine > 0) {
         int i = 0;
         for (; i + 2 < mine; i += 2) {
-          load_chunk<T, D, G, CB>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
+          load_chunk<T, D, G, CB, F8>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
                                   blk_stride, pc.head_off, lane);
           __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
+          compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
           __builtin_amdgcn_sched_barrier(0);
-          load_chunk<T, D, G, CB>(fa, kc, vc, pc.bt_row, blk_of(i + 2), pc.blk_last, a.num_blocks, tok_stride,
+          load_chunk<T, D, G, CB, F8>(fa, kc, vc, pc.bt_row, blk_of(i + 2), pc.blk_last, a.num_blocks, tok_stride,
                                   blk_stride, pc.head_off, lane);
           __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<T, D, G, CB>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, false, lane);
+          compute_chunk<T, D, G, CB, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, false, lane);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (i + 1 < mine) {
-          load_chunk<T, D, G, CB>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
+          load_chunk<T, D, G, CB, F8>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
                                   blk_stride, pc.head_off, lane);
           __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
-          compute_chunk<T, D, G, CB>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, is_mask(i + 1), lane);
+          compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
+          compute_chunk<T, D, G, CB, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, is_mask(i + 1), lane);
         } else {
-          compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
+          compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
         }
       }
     } else {
       for (int i = 0; i < mine; ++i) {
-        load_chunk<T, D, G, CB>(fa, kc, vc, pc.bt_row, blk_of(i), pc.blk_last, a.num_blocks, tok_stride,
+        load_chunk<T, D, G, CB, F8>(fa, kc, vc, pc.bt_row, blk_of(i), pc.blk_last, a.num_blocks, tok_stride,
                                 blk_stride, pc.head_off, lane);
-        compute_chunk<T, D, G, CB>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
+        compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
       }
     }
 
     // The next job's query and first chunk go out before this job's merge.
-    const JobPlan pn = plan_job<T, D, CB>(a, nxt, wave, nwaves);
+    const JobPlan pn = plan_job<S::kElemBytes, D, CB>(a, nxt, wave, nwaves);
     if (nxt.n > 0 && nxt.seq >= 0) {
-      load_query<T, D, G, CB>(a.query, nxt.seq, a.num_heads, nxt.kvh * g, g, lane, q);
+      load_query<T, D, G, CB, F8>(a.query, nxt.seq, a.num_heads, nxt.kvh * g, g, lane, q);
       if (PF && pn.mine > 0)
-        load_chunk<T, D, G, CB>(fa, kc, vc, pn.bt_row, blk_of(0), pn.blk_last, a.num_blocks, tok_stride,
+        load_chunk<T, D, G, CB, F8>(fa, kc, vc, pn.bt_row, blk_of(0), pn.blk_last, a.num_blocks, tok_stride,
                                 blk_stride, pn.head_off, lane);
     }
 
@@ -466,7 +491,7 @@ __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(Deco
             L = fmaf(wt, s_l[v][h], L);
             o = fmaf(wt, s_acc[(v * G + h) * D + d], o);
           }
-          o = o / L;
+          o = o / L * a.v_scale;
         }
         const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
         const int64_t row = static_cast<int64_t>(cur.seq) * a.num_heads + head0 + h;
@@ -884,11 +909,14 @@ namespace {
 
 // Blocks per chunk (CB) and one-chunk register lookahead (PF), chosen per
 // shape so a wave fits in 256 VGPRs without spilling (2 waves per SIMD).
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool F8 = false>
 struct Policy {
-  static constexpr int kRegsPerBlock = D * static_cast<int>(sizeof(T)) / 8;  // K + V dwords per lane
+  static constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));
+  static constexpr int kRegsPerBlock = D * kElemBytes / 8;  // K + V dwords per lane
   static constexpr int kAcc = G * D / 16;
-  static constexpr int CB = (kRegsPerBlock <= 32 && G <= 4) ? 2 : 1;
+  // FP8 blocks take half the registers; small groups use twice the blocks per
+  // chunk (larger ones would spill the conversion temporaries).
+  static constexpr int CB = (kRegsPerBlock <= 16 && G <= 2) ? 4 : (kRegsPerBlock <= 32 && G <= 4) ? 2 : 1;
   static constexpr bool PF = 2 * CB * kRegsPerBlock + kAcc <= 160;
 };
 
@@ -911,10 +939,22 @@ int waves_per_group() {
 
 typedef void (*DecodeKernel)(DecodeArgs);
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool F8 = false>
 DecodeKernel kernel_for() {
-  using P = Policy<T, D, G>;
-  return paged_decode_kernel<T, D, G, P::CB, P::PF>;
+  using P = Policy<T, D, G, F8>;
+  return paged_decode_kernel<T, D, G, P::CB, P::PF, F8>;
+}
+
+template <int D>
+DecodeKernel pick_group_fp8(int G) {
+  switch (G) {
+    case 1: return kernel_for<bf16_t, D, 1, true>();
+    case 2: return kernel_for<bf16_t, D, 2, true>();
+    case 4: return kernel_for<bf16_t, D, 4, true>();
+    case 8: return kernel_for<bf16_t, D, 8, true>();
+    case 16: return kernel_for<bf16_t, D, 16, true>();
+    default: return nullptr;
+  }
 }
 
 template <typename T, int D>
@@ -962,9 +1002,11 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
-int launch_decode(DecodeArgs args, int num_seqs, int dtype, int head_size, hipStream_t stream) {
+int launch_decode(DecodeArgs args, int num_seqs, int dtype, int head_size, hipStream_t stream,
+                  bool fp8_cache = false) {
   const int G = next_pow2_group(args.group);
-  DecodeKernel k = pick_decode(dtype, head_size, G);
+  DecodeKernel k = fp8_cache ? (head_size == 128 ? pick_group_fp8<128>(G) : pick_group_fp8<64>(G))
+                             : pick_decode(dtype, head_size, G);
   if (!k) return PA_ERR_UNSUPPORTED;
   // Job ids padded to whole XCD rounds (a multiple of 8).
   const int64_t jobs = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * args.num_kv_heads;
@@ -1105,7 +1147,41 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   args.num_kv_heads = num_kv_heads;
   args.group = num_heads / num_kv_heads;
   args.scale_log2 = scale * kLog2e;
+  args.v_scale = 1.0f;
   return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
+                             float scale, float k_scale, float v_scale, int32_t dtype, float* lse_out,
+                             const int32_t* seq_order, void* stream) {
+  int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
+    return PA_ERR_INVALID_ARG;
+  DecodeArgs args{};
+  args.query = query;
+  args.key_cache = key_cache;
+  args.value_cache = value_cache;
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.out = out;
+  args.lse_out = lse_out;
+  args.seq_order = seq_order;
+  args.num_blocks = num_blocks;
+  args.max_blocks = max_blocks_per_seq;
+  args.num_seqs = num_seqs;
+  args.num_heads = num_heads;
+  args.num_kv_heads = num_kv_heads;
+  args.group = num_heads / num_kv_heads;
+  // Keys are code values times k_scale: the scale folds into the scores'.
+  args.scale_log2 = scale * k_scale * kLog2e;
+  args.v_scale = v_scale;
+  return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream), true);
 }
 
 // Workspace layout: o_p [S, H_q, slots, D] float32 | lse_p [S, H_q, slots]

@@ -25,6 +25,7 @@ from __future__ import annotations
 
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
+import dataclasses
 import math
 import os
 
@@ -49,6 +50,9 @@ class PagedConfig:
     seed: int
     partition_size: int = 512
     description: str = ""
+    kv_dtype: str = ""     # "" (caches in dtype) or "fp8" (E4M3 codes, bf16 query/out)
+    k_scale: float = 1.0   # FP8 caches: value = code value * scale
+    v_scale: float = 1.0
 
     @property
     def scale(self) -> float:
@@ -59,6 +63,14 @@ class PagedConfig:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.cache_dtype == "fp8" else self.elem_bytes
 
     @property
     def group(self) -> int:
@@ -94,7 +106,16 @@ CONFIGS: list[PagedConfig] = [
         description="70B-shaped heads: 128 seqs share one 1024-token prefix + suffix U{64..512}"),
 ]
 
-CONFIG_BY_NAME = {c.name: c for c in CONFIGS}
+# Beyond the five workloads above: the batch-256 step with an FP8 (E4M3) KV
+# cache. Codes are drawn directly (log-uniform magnitudes); with the scales
+# below, keys and values span about 2^-12 .. 4.
+EXTRA_CONFIGS: list[PagedConfig] = [
+    dataclasses.replace(CONFIGS[2], name="llama3_8b_b256_fp8", kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64,
+                        description="Batch-256 Llama-3-8B-shaped decode over an FP8 E4M3 KV cache "
+                                    "(bf16 query/out, k_scale = v_scale = 1/64)"),
+]
+
+CONFIG_BY_NAME = {c.name: c for c in CONFIGS + EXTRA_CONFIGS}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -159,11 +180,40 @@ def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return out.reshape(shape)
 
 
+def _codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Random FP8 E4M3 codes: uniform sign and mantissa, exponent field uniform
+    in 1..14 (never NaN), i.e. log-uniform magnitudes 2^-6 .. 240. Drawn the
+    same chunked way as _values."""
+    n = int(np.prod(shape))
+    seed = int(rng.integers(0, 2 ** 63))
+    kids = np.random.SeedSequence(seed).spawn(max(1, -(-n // _CHUNK)))
+    out = np.empty(n, dtype=np.uint8)
+
+    def fill(i):
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        u = np.random.default_rng(kids[i]).integers(0, 1 << 16, size=hi - lo, dtype=np.uint32)
+        out[lo:hi] = ((u & 1) << 7 | (1 + (u >> 4) % 14) << 3 | (u >> 1) & 7).astype(np.uint8)
+
+    if len(kids) == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(len(kids))))
+    return out.reshape(shape)
+
+
+FP8_NAN_CODE = np.uint8(0x7F)
+
+
 def poison_value(dtype: str):
+    if dtype == "fp8":
+        return FP8_NAN_CODE
     return np.float32(np.nan) if dtype == "f32" else BF16_NAN_BITS
 
 
 def storage_dtype(dtype: str):
+    if dtype == "fp8":
+        return np.uint8
     return np.float32 if dtype == "f32" else np.uint16
 
 
@@ -247,8 +297,9 @@ def make_inputs(cfg: PagedConfig, mode: str = "parity", seed: int | None = None,
     Hq, Hkv, d = cfg.num_heads, cfg.num_kv_heads, cfg.head_size
     query = _values(rng, (S, Hq, d), cfg.dtype)
 
-    sdt = storage_dtype(cfg.dtype)
-    fill = poison_value(cfg.dtype) if mode == "parity" else sdt(0)
+    cdt = cfg.cache_dtype
+    sdt = storage_dtype(cdt)
+    fill = poison_value(cdt) if mode == "parity" else sdt(0)
     caches = []
     for _ in range(2):  # K then V
         pool = np.empty((cfg.num_blocks, bs, Hkv, d), dtype=sdt)
@@ -256,7 +307,8 @@ def make_inputs(cfg: PagedConfig, mode: str = "parity", seed: int | None = None,
             pool[...] = fill
         else:
             pool[...] = 0
-        pool[referenced] = _values(rng, (referenced.size, bs, Hkv, d), cfg.dtype)
+        shape = (referenced.size, bs, Hkv, d)
+        pool[referenced] = _codes(rng, shape) if cdt == "fp8" else _values(rng, shape, cfg.dtype)
         caches.append(pool)
     key_cache, value_cache = caches
 
@@ -276,13 +328,20 @@ def make_inputs(cfg: PagedConfig, mode: str = "parity", seed: int | None = None,
     for i in range(S):
         if n[i] > 0:
             slot[i] = int(tables[i, pos[i] // bs]) * bs + int(pos[i] % bs)
-    flat_k = key_cache.reshape(cfg.num_blocks * bs, Hkv, d)
-    flat_v = value_cache.reshape(cfg.num_blocks * bs, Hkv, d)
     ok = slot >= 0
-    new_key = np.zeros((S, Hkv, d), dtype=sdt)
-    new_value = np.zeros((S, Hkv, d), dtype=sdt)
-    new_key[ok] = flat_k[slot[ok]]
-    new_value[ok] = flat_v[slot[ok]]
+    if cdt == "fp8":
+        # The new token's K/V arrive in the query's dtype and are quantized by
+        # the write, so they are drawn here and the caches hold the state
+        # before the write (their rows at the slots are overwritten by it).
+        new_key = _values(rng, (S, Hkv, d), cfg.dtype)
+        new_value = _values(rng, (S, Hkv, d), cfg.dtype)
+    else:
+        flat_k = key_cache.reshape(cfg.num_blocks * bs, Hkv, d)
+        flat_v = value_cache.reshape(cfg.num_blocks * bs, Hkv, d)
+        new_key = np.zeros((S, Hkv, d), dtype=sdt)
+        new_value = np.zeros((S, Hkv, d), dtype=sdt)
+        new_key[ok] = flat_k[slot[ok]]
+        new_value[ok] = flat_v[slot[ok]]
 
     return PagedInputs(cfg=cfg, context_lens=n, block_tables=tables, query=query,
                        key_cache=key_cache, value_cache=value_cache, new_key=new_key,
@@ -302,7 +361,7 @@ def caches_before_write(inp: PagedInputs):
     kc = inp.key_cache.copy()
     vc = inp.value_cache.copy()
     ok = (inp.slot_mapping >= 0) & (inp.slot_mapping < rows)
-    fill = poison_value(cfg.dtype)
+    fill = poison_value(cfg.cache_dtype)
     kc.reshape(rows, cfg.num_kv_heads, cfg.head_size)[inp.slot_mapping[ok]] = fill
     vc.reshape(rows, cfg.num_kv_heads, cfg.head_size)[inp.slot_mapping[ok]] = fill
     return kc, vc
@@ -310,7 +369,7 @@ def caches_before_write(inp: PagedInputs):
 
 def algorithmic_kv_bytes(cfg: PagedConfig, context_lens: np.ndarray) -> int:
     """K and V bytes one decode call must read: sum_i n_i * 2 * H_kv * d_h * b."""
-    return int(np.asarray(context_lens, dtype=np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_size * cfg.elem_bytes
+    return int(np.asarray(context_lens, dtype=np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_size * cfg.kv_elem_bytes
 
 
 def unique_kv_bytes(inp: PagedInputs) -> int:
@@ -329,13 +388,15 @@ def unique_kv_bytes(inp: PagedInputs) -> int:
                 continue
             seen.add(key)
             total_tokens += used
-    return total_tokens * 2 * cfg.num_kv_heads * cfg.head_size * cfg.elem_bytes
+    return total_tokens * 2 * cfg.num_kv_heads * cfg.head_size * cfg.kv_elem_bytes
 
 
 def small_case(name: str, num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
-               dtype: str, ctx: tuple, seed: int, num_blocks: int, partition_size: int = 64) -> PagedConfig:
+               dtype: str, ctx: tuple, seed: int, num_blocks: int, partition_size: int = 64,
+               kv_dtype: str = "", k_scale: float = 1.0, v_scale: float = 1.0) -> PagedConfig:
     """A small ad-hoc config for parity sweeps (same generator, different shape)."""
     return PagedConfig(name=name, num_seqs=num_seqs, num_heads=num_heads,
                        num_kv_heads=num_kv_heads, head_size=head_size, block_size=16,
                        num_blocks=num_blocks, dtype=dtype, ctx=ctx, seed=seed,
-                       partition_size=partition_size, description="ad-hoc parity case")
+                       partition_size=partition_size, description="ad-hoc parity case",
+                       kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
