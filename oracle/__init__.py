@@ -47,3 +47,4 @@ from .fp8 import (  # noqa: F401
     reshape_and_cache_fp8,
     paged_decode_fp8,
 )
+from .multi_query import paged_multi_query  # noqa: F401
