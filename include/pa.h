@@ -194,6 +194,43 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               float scale, int32_t dtype, float* lse_out, const int32_t* seq_order, void* stream);
 
 /*
+ * pa_multi_query - paged attention for several new tokens per sequence.
+ *
+ * One step may give a sequence more than one new token: a slice of a long
+ * prompt (chunked prefill) or the k+1 positions of a speculative step, mixed
+ * freely with one-token decodes of other sequences (llm-stack-book 7.3,
+ * sections "Prefill, decode, and chunked prefill" and "Speculative decoding
+ * support"). The new tokens' K/V are written first (pa_reshape_and_cache), so
+ * with n = context_lens[i] tokens stored and q_i = query_start_loc[i+1] -
+ * query_start_loc[i] of them new, the new token in row t = query_start_loc[i]
+ * + j sits at position p = n - q_i + j, and for every query head h:
+ *     s_u = scale * <query[t][h], K_u>            for u in [0, p]
+ *     out[t][h] = sum_u softmax(s)_u * V_u
+ * with K_u, V_u found through block_tables[i] as in pa_decode. A token with
+ * p < 0 (more new tokens than stored ones) gets out = 0 and lse = -inf. With
+ * every q_i = 1 this is pa_decode.
+ *
+ * Work is cut into tiles of one sequence and kv head covering 16 or 32
+ * (new token, query head) pairs; each tile reads the keys up to its last
+ * token's position once.
+ *
+ *   out, query        [num_tokens, num_heads, head_size] (dtype), device.
+ *   query_start_loc   int32 [num_seqs + 1], device: non-decreasing, starting at
+ *                     0 and ending at num_tokens. Entries are clamped to
+ *                     [0, num_tokens]; other violations give unspecified
+ *                     output rows, never an out-of-bounds access.
+ *   num_tokens        rows of query/out (host value); 0 launches nothing.
+ *   lse_out           optional float32 [num_tokens, num_heads]; NULL to skip.
+ *   scale             > 0 and finite.
+ * Other arguments as pa_decode. Returns PA_OK or an error status.
+ */
+int pa_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                   const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                   int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size, float scale,
+                   int32_t dtype, float* lse_out, void* stream);
+
+/*
  * pa_decode_split_workspace_bytes - workspace pa_decode_split needs.
  *
  * slots = ceil(max_context_len / partition_size) + 1. The workspace holds, each

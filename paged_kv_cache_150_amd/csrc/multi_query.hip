@@ -1,0 +1,499 @@
+// Multi-query paged attention for gfx950: pa_multi_query.
+//
+// What is computed (llm-stack-book 7.3 "vLLM: Architecture, PagedAttention &
+// Internals", sections "Prefill, decode, and chunked prefill", "The forward
+// step in detail" and "Speculative decoding support"): one step may hand a
+// sequence several new tokens (a prompt chunk, or the k+1 positions a
+// speculative step verifies). Their K/V are already in the cache, so with n
+// tokens stored and q of them new, new token j sits at position n - q + j and
+// attends over positions 0 .. n - q + j of the sequence's paged context.
+//
+// Work decomposition: a workgroup takes one tile of one sequence and one kv
+// head. A tile is 16*NT "columns", each a (new token, query head) pair: the
+// group's g heads for 16*NT/g consecutive new tokens. Its 4 waves split the
+// tile's key range into chunks of CB blocks (chunk c to wave c % 4) and merge
+// through LDS at the end, as in the decode kernel.
+//  * Scores: the decode kernel's 16x16 MFMA tile, A = 16 K rows of a block,
+//    B = 16 columns; lane l gets the scores of keys 4*(l/16)+r of the block for
+//    column l % 16.
+//  * Causal limit per column: column (token j, head h) sees keys up to its own
+//    position. Only the last one to three chunks of a tile reach past the first
+//    token's position, and each is the last chunk of its wave.
+//  * P*V on MFMA, without moving data between lanes: lane l already holds V
+//    rows 4*(l/16)..+3, elements (l%16)*D/16 .. +D/16 of each (the decode
+//    tile layout), and the probabilities of the same four keys for column
+//    l % 16. Taking element t of each lane's piece gives the A operand of a
+//    16x16 MFMA whose rows are d = (D/16)*m + t, contracted over the keys
+//    (K = 4 keys of a block, or 8 keys of two blocks), with B = the
+//    probabilities. Lane l ends up owning output elements
+//    d in [(l/16)*D/4, (l/16+1)*D/4) of column l % 16.
+//  * Probabilities enter the bf16 MFMA rounded to bf16 (relative error at
+//    most 2^-9 per weight); the normaliser and the log-sum-exp use the fp32
+//    values. fp32 caches use the fp32 MFMA and keep fp32 probabilities.
+//  * Online softmax in base 2, per column; a column with no visible key yet
+//    keeps weight 0 (its running maximum stays -inf).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_tiles.h"
+
+namespace pa {
+
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4_t;
+
+constexpr int kMqWaves = 4;
+
+struct MultiArgs {
+  const void* query;              // [num_tokens, num_heads, D]
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;    // tokens stored per sequence, new ones included
+  const int32_t* query_start_loc; // [num_seqs + 1]: sequence i's new tokens are rows [loc[i], loc[i+1])
+  void* out;                      // [num_tokens, num_heads, D]
+  float* lse_out;                 // optional [num_tokens, num_heads]
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;        // H_q / H_kv
+  int32_t tile_tokens;  // new tokens per tile: 16 * NT / group
+  int32_t num_slots;    // tile slots: num_tokens / tile_tokens + num_seqs
+  float scale_log2;     // scale * log2(e)
+};
+
+// Tile slots: sequence i owns slots [B_i, B_{i+1}) with
+// B_i = loc[i] / tile_tokens + i. That is at least ceil(q_i / tile_tokens)
+// slots (at most one more), B is non-decreasing, and B_S is a host-known
+// bound, so a slot's sequence is the number of i >= 1 with B_i <= slot.
+__device__ __forceinline__ int clamp_loc(int v, int num_tokens) { return v < 0 ? 0 : (v > num_tokens ? num_tokens : v); }
+
+__device__ __forceinline__ int slot_owner(const MultiArgs& a, int slot, int lane) {
+  int count = 0;
+  for (int base = 1; base <= a.num_seqs; base += kWave) {
+    const int i = base + lane;
+    bool le = false;
+    if (i <= a.num_seqs) le = clamp_loc(a.query_start_loc[i], a.num_tokens) / a.tile_tokens + i <= slot;
+    const uint64_t m = __ballot(le);
+    count += __popcll(m);
+    if (m != ~0ull) break;  // B is non-decreasing: no later i qualifies
+  }
+  return count;
+}
+
+template <typename T, int D, int CB, int NT>
+struct MqState {
+  static constexpr int kTiles = D / 16;  // output d-tiles: tile t holds d = (D/16)*m + t
+  float m[NT];              // running max (base-2 scaled) of column lane%16 of part p
+  float l[NT];              // partial normaliser over this lane's keys
+  f32x4_t acc[NT][kTiles];  // d = (D/16)*(4*(lane/16) + r) + t, column lane%16
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{a, b}, bf16x2v_t));
+}
+// Element t of a lane's bf16 piece, taken from two rows, packed (row a low).
+template <int T_>
+__device__ __forceinline__ uint32_t pick_bf16(const uint32_t* ra, const uint32_t* rb) {
+  const uint32_t x = ra[T_ / 2], y = rb[T_ / 2];
+  return (T_ & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+}
+
+template <typename T, int D, int CB, int NT>
+__device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<T, D, 16, CB>& f,
+                                         const u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB>::kQSeg],
+                                         float scale_log2, int tok0, const int (&lim)[NT], int key_end,
+                                         bool mask, int lane) {
+  using S = DecodeShape<T, D, 16, CB>;
+  constexpr int kTiles = D / 16;
+  const int rg = lane >> 4;
+  uint32_t vz[CB][4][S::kVDw];
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int w = 0; w < S::kVDw; ++w) vz[i][r][w] = f.v[i][r][w];
+  float s[NT][CB][4];
+#pragma unroll
+  for (int p = 0; p < NT; ++p) qk_chunk<T, D, 16, CB>(s[p], f, q[p], scale_log2);
+  if (mask) {
+    // Keys at or past the tile's last position: weight 0 for every column,
+    // and their V rows (possibly stale or poisoned) are replaced by 0.
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = tok0 + i * 16 + 4 * rg + r;
+#pragma unroll
+        for (int p = 0; p < NT; ++p) s[p][i][r] = key < lim[p] ? s[p][i][r] : -__builtin_inff();
+        const bool live = key < key_end;
+#pragma unroll
+        for (int w = 0; w < S::kVDw; ++w) vz[i][r][w] = live ? vz[i][r][w] : 0u;
+      }
+  }
+  float pw[NT][CB][4];
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    float mx = s[p][0][0];
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[p][i][r]);
+    mx = rows_max(mx);
+    const float m_new = fmaxf(st.m[p], mx);
+    // With no visible key yet the reference point is 0: every weight is then
+    // exp2(-inf) = 0 and the (zero) partial sums stay zero.
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m[p] - m_use);
+    st.m[p] = m_new;
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[p][i][r] = fast_exp2(s[p][i][r] - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) psum += pw[p][i][r];
+    st.l[p] = st.l[p] * alpha + psum;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[p][t][r] *= alpha;
+  }
+
+  if constexpr (sizeof(T) == 2) {
+    // bf16: probabilities rounded to bf16, contracted with V over 8 keys of
+    // two blocks per MFMA, or 4 keys of the odd block out.
+#pragma unroll
+    for (int i = 0; i < CB; i += 2) {
+      if (i + 1 < CB) {
+        u32x4_t b[NT];
+#pragma unroll
+        for (int p = 0; p < NT; ++p) {
+          b[p] = u32x4_t{pack_bf16(pw[p][i][0], pw[p][i][1]), pack_bf16(pw[p][i][2], pw[p][i][3]),
+                         pack_bf16(pw[p][i + 1][0], pw[p][i + 1][1]), pack_bf16(pw[p][i + 1][2], pw[p][i + 1][3])};
+        }
+        static_for<kTiles>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          const u32x4_t av = {pick_bf16<t>(vz[i][0], vz[i][1]), pick_bf16<t>(vz[i][2], vz[i][3]),
+                              pick_bf16<t>(vz[i + 1][0], vz[i + 1][1]), pick_bf16<t>(vz[i + 1][2], vz[i + 1][3])};
+#pragma unroll
+          for (int p = 0; p < NT; ++p)
+            st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                   __builtin_bit_cast(bf16x8_t, b[p]),
+                                                                   st.acc[p][t], 0, 0, 0);
+        });
+      } else {
+        u32x2_t b[NT];
+#pragma unroll
+        for (int p = 0; p < NT; ++p) {
+          b[p] = u32x2_t{pack_bf16(pw[p][i][0], pw[p][i][1]), pack_bf16(pw[p][i][2], pw[p][i][3])};
+        }
+        static_for<kTiles>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          const u32x2_t av = {pick_bf16<t>(vz[i][0], vz[i][1]), pick_bf16<t>(vz[i][2], vz[i][3])};
+#pragma unroll
+          for (int p = 0; p < NT; ++p)
+            st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, av),
+                                                                     __builtin_bit_cast(bf16x4_t, b[p]),
+                                                                     st.acc[p][t], 0, 0, 0);
+        });
+      }
+    }
+  } else {
+    // fp32: one key per lane per MFMA (K = 4: keys 4*(l/16) + r of a block).
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+          for (int p = 0; p < NT; ++p)
+            st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(as_float(vz[i][r][t]), pw[p][i][r], st.acc[p][t],
+                                                                0, 0, 0);
+  }
+}
+
+
+// Workgroup -> (tile slot, kv head): consecutive workgroups go to the 8 XCDs
+// in turn; the kv heads of one slot share an XCD.
+__device__ __forceinline__ void wg_to_slot_head(int id, int num_kv_heads, int& slot, int& kvh) {
+  const int xcd = id & 7;
+  const int k = id >> 3;
+  kvh = k % num_kv_heads;
+  slot = (k / num_kv_heads) * 8 + xcd;
+}
+
+// Query fragments of a tile's columns: column c = 16 p + (lane % 16) is new
+// token c / g (row `row0` + c / g) and head head0 + c % g; columns past the
+// tile's `ncols` get zeros. Same d order as the K operand of qk_chunk.
+template <typename T, int D, int CB, int NT>
+__device__ __forceinline__ void load_query_cols(const void* query, int64_t row0, int num_heads, int head0, int g,
+                                                int ncols, int lane,
+                                                u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB>::kQSeg]) {
+  using S = DecodeShape<T, D, 16, CB>;
+  constexpr int kQBytes = static_cast<int>(sizeof(T));
+  const int j = lane >> 4;
+  const gchar_t* qb = uniform_ptr(static_cast<const char*>(query) + (row0 * num_heads + head0) * D * kQBytes);
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    const int c = 16 * p + (lane & 15);
+    const bool valid = c < ncols;
+    const int tok = c / g;
+    const uint32_t qoff = valid ? static_cast<uint32_t>((tok * num_heads + c - tok * g) * D * kQBytes) : 0u;
+#pragma unroll
+    for (int sg = 0; sg < S::kQSeg; ++sg) {
+      u32x4_t v = gload16(qb + sg * 64 + j * 16 + qoff);
+      q[p][sg] = valid ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// One workgroup per (tile slot, kv head); slot ids follow the decode kernel's
+// XCD-aware order (id % 8 names the XCD; the kv heads of a slot share it).
+template <typename T, int D, int CB, int NT>
+__global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(MultiArgs a) {
+  using S = DecodeShape<T, D, 16, CB>;
+  constexpr int kCols = 16 * NT;
+  constexpr int kRow = D + 1;  // LDS row stride in floats (spreads the 16 columns over banks)
+  __shared__ float s_acc[kMqWaves][kCols][kRow];
+  __shared__ float s_m[kMqWaves][kCols];
+  __shared__ float s_l[kMqWaves][kCols];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = a.group;
+
+  int slot, kvh;
+  wg_to_slot_head(blockIdx.x, a.num_kv_heads, slot, kvh);
+  if (slot >= a.num_slots) return;
+  const int seq = __builtin_amdgcn_readfirstlane(slot_owner(a, slot, lane));
+  if (seq >= a.num_seqs) return;
+  const int q0 = clamp_loc(a.query_start_loc[seq], a.num_tokens);
+  const int q1 = clamp_loc(a.query_start_loc[seq + 1], a.num_tokens);
+  const int ql = q1 - q0;
+  if (ql <= 0) return;
+  const int ntiles = (ql + a.tile_tokens - 1) / a.tile_tokens;
+  const int r = slot - (q0 / a.tile_tokens + seq);
+  if (r < 0 || r >= ntiles) return;
+  // Later tiles see longer contexts: they take the lower slots of the sequence.
+  const int tile = ntiles - 1 - r;
+  const int tok0 = tile * a.tile_tokens;                     // first new token of the tile
+  const int ntok = min(a.tile_tokens, ql - tok0);
+  const int ncols = ntok * g;
+
+  const int max_tokens = a.max_blocks * kBlockTokens;
+  const int n_raw = a.context_lens[seq];
+  const int n = n_raw < 0 ? 0 : (n_raw > max_tokens ? max_tokens : n_raw);
+  const int pos0 = n - ql + tok0;                            // position of the tile's first token
+  const int key_end = max(0, pos0 + ntok);                   // keys [0, key_end) are read
+  int lim[NT];
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    const int c = 16 * p + (lane & 15);
+    lim[p] = c < ncols ? pos0 + c / g + 1 : 0;
+  }
+
+  const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
+  const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
+  const int64_t head_off = static_cast<int64_t>(kvh) * D * S::kElemBytes;
+  const char* kc = static_cast<const char*>(a.key_cache);
+  const char* vc = static_cast<const char*>(a.value_cache);
+  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
+  const int blk_end = (key_end + kBlockTokens - 1) / kBlockTokens;
+  const int nchunk = (blk_end + CB - 1) / CB;
+  const int blk_last = blk_end - 1;
+  // Chunks from mask_from on reach past the first token's position.
+  constexpr int kChunkTokens = CB * kBlockTokens;
+  const int mask_from = max(pos0 + 1, 0) / kChunkTokens;
+  const int mine = wave < nchunk ? (nchunk - wave + kMqWaves - 1) / kMqWaves : 0;
+  auto blk_of = [&](int i) { return (wave + i * kMqWaves) * CB; };
+  auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
+  auto is_mask = [&](int i) { return wave + i * kMqWaves >= mask_from; };
+
+  u32x4_t q[NT][S::kQSeg];
+  load_query_cols<T, D, CB, NT>(a.query, q0 + tok0, a.num_heads, kvh * g, g, ncols, lane, q);
+
+  MqState<T, D, CB, NT> st;
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    st.m[p] = -__builtin_inff();
+    st.l[p] = 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) st.acc[p][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Register double buffer with unconditional steady-state loads and a peeled
+  // tail, as in the decode kernel; only a wave's last chunk can need a mask.
+  Chunk<T, D, 16, CB> fa, fb;
+  if (mine > 0) {
+    load_chunk<T, D, 16, CB>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
+                             head_off, lane);
+    int i = 0;
+    for (; i + 2 < mine; i += 2) {
+      load_chunk<T, D, 16, CB>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
+                               head_off, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, false, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      load_chunk<T, D, 16, CB>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride, blk_stride,
+                               head_off, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mq_chunk<T, D, CB, NT>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, false, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i + 1 < mine) {
+      load_chunk<T, D, 16, CB>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
+                               head_off, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      mq_chunk<T, D, CB, NT>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
+    } else {
+      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+    }
+  }
+
+  // Wave partials to LDS: per column the running max and normaliser, and the
+  // lane's D/4 output elements.
+  const int j = lane >> 4;
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    const float l = rows_sum(st.l[p]);
+    const int c = 16 * p + (lane & 15);
+    if (lane < 16) {
+      s_m[wave][c] = st.m[p];
+      s_l[wave][c] = l;
+    }
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) s_acc[wave][c][(D / 16) * (4 * j + rr) + t] = st.acc[p][t][rr];
+  }
+  __syncthreads();
+
+  // Merge the waves with weights 2^(m_w - M) and write each column's row.
+  for (int idx = threadIdx.x; idx < ncols * D; idx += kMqWaves * kWave) {
+    const int c = idx / D;
+    const int d = idx - c * D;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int v = 0; v < kMqWaves; ++v) M = fmaxf(M, s_m[v][c]);
+    float o = 0.f, L = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int v = 0; v < kMqWaves; ++v) {
+        const float wt = fast_exp2(s_m[v][c] - M);
+        L = fmaf(wt, s_l[v][c], L);
+        o = fmaf(wt, s_acc[v][c][d], o);
+      }
+      o = o / L;
+    }
+    const int tok = c / g;
+    const int64_t row = (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
+    store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
+    if (a.lse_out != nullptr && d == 0)
+      a.lse_out[row] = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
+  }
+}
+
+}  // namespace pa
+
+// ------------------------------------------------------------------ host side
+namespace {
+
+using namespace pa;
+
+typedef void (*MultiKernel)(MultiArgs);
+
+template <typename T, int D, int NT>
+MultiKernel multi_kernel_for() {
+  constexpr int kRegsPerBlock = D * static_cast<int>(sizeof(T)) / 8;  // K + V dwords per lane
+  constexpr int CB = (kRegsPerBlock <= 32 && NT == 1) ? 2 : 1;
+  return paged_multi_query_kernel<T, D, CB, NT>;
+}
+
+MultiKernel pick_multi(int dtype, int D, int NT) {
+  if (dtype == PA_DTYPE_BF16) {
+    if (D == 128) return NT == 1 ? multi_kernel_for<bf16_t, 128, 1>() : multi_kernel_for<bf16_t, 128, 2>();
+    return NT == 1 ? multi_kernel_for<bf16_t, 64, 1>() : multi_kernel_for<bf16_t, 64, 2>();
+  }
+  if (D == 128) return multi_kernel_for<float, 128, 1>();
+  return NT == 1 ? multi_kernel_for<float, 64, 1>() : multi_kernel_for<float, 64, 2>();
+}
+
+inline bool aligned16_mq(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tiles of 32 columns when the step averages more new tokens per sequence
+// than one 16-column tile holds: prompt chunks and longer speculative runs
+// then read each key once per 32 columns instead of per 16.
+int pick_tiles(int num_tokens, int num_seqs, int group) {
+  if (const char* e = getenv("PA_MQ_TILE_COLUMNS")) {
+    const int v = atoi(e);
+    if (v == 16 || v == 32) return v / 16;
+  }
+  return static_cast<int64_t>(num_tokens) * group > static_cast<int64_t>(num_seqs) * 16 ? 2 : 1;
+}
+
+}  // namespace
+
+extern "C" int pa_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                              int32_t block_size, float scale, int32_t dtype, float* lse_out, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens || !query_start_loc)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16_mq(out) || !aligned16_mq(query) || !aligned16_mq(key_cache) || !aligned16_mq(value_cache))
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+
+  const int g = num_heads / num_kv_heads;
+  // fp32 caches with 128-element heads keep 16-column tiles (32 would spill).
+  const int NT = (dtype == PA_DTYPE_F32 && head_size == 128) ? 1 : pick_tiles(num_tokens, num_seqs, g);
+  MultiKernel k = pick_multi(dtype, head_size, NT);
+  MultiArgs a;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = g;
+  a.tile_tokens = 16 * NT / g;
+  const int64_t slots = static_cast<int64_t>(num_tokens) / a.tile_tokens + num_seqs;
+  const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
+  if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  a.num_slots = static_cast<int32_t>(slots);
+  a.scale_log2 = scale * kLog2e;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

@@ -1,0 +1,99 @@
+// K/V tile loads and the MFMA score tile shared by the paged-attention
+// kernels (gfx950 only). Layout of one tile (16 tokens of one block, one kv
+// head): for the score MFMA, lane l holds K row (l % 16), 16-byte pieces at
+// byte offset s*64 + (l/16)*16; for the value side, lane l holds rows
+// 4*(l/16) .. 4*(l/16)+3, elements (l%16)*D/16 .. (l%16+1)*D/16 - 1 of each.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+// T: query/output element; F8: the caches hold FP8 E4M3 codes (with bf16
+// queries) instead of T.
+template <typename T, int D, int G, int CB, bool F8 = false>
+struct DecodeShape {
+  static constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));  // cache element
+  static constexpr int kKSeg = D * kElemBytes / 64;  // 16-byte K loads per lane per block
+  static constexpr int kQSeg = F8 ? 2 * kKSeg : kKSeg;  // 16-byte query pieces per lane (MFMA k-steps)
+  static constexpr int kVec = D / 16;                // V elements per lane per token
+  static constexpr int kVDw = kVec * kElemBytes / 4; // ... as dwords
+  static_assert(kKSeg >= 1 && kVDw >= 1, "shape");
+  static_assert(G >= 1 && G <= 16, "group");
+  static_assert(!F8 || sizeof(T) == 2, "FP8 caches take bf16 queries");
+};
+
+template <typename T, int D, int G, int CB, bool F8 = false>
+struct Chunk {
+  using S = DecodeShape<T, D, G, CB, F8>;
+  u32x4_t k[CB][S::kKSeg];
+  uint32_t v[CB][4][S::kVDw];
+};
+
+// Loads one chunk (CB blocks) of K and V for this wave's kv head. Block ids
+// are wave-uniform, so each load is a scalar base (block, head, row) plus a
+// 32-bit per-lane offset.
+template <typename T, int D, int G, int CB, bool F8 = false>
+__device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
+                                           const int32_t* bt_row, int blk0, int blk_last,
+                                           int64_t num_blocks, uint32_t tok_stride_bytes,
+                                           int64_t blk_stride_bytes, int64_t head_off_bytes,
+                                           int lane) {
+  using S = DecodeShape<T, D, G, CB, F8>;
+  const int tok = lane & 15;
+  const int j = lane >> 4;
+  const uint32_t koff = tok * tok_stride_bytes + j * 16;                      // K: row tok, piece j
+  const uint32_t voff = (4 * j) * tok_stride_bytes + tok * (S::kVDw * 4);     // V: rows 4j.., piece tok
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int b = min(blk0 + i, blk_last);
+    // Out-of-range ids (negative included) are clamped so a bad table never
+    // leads to an out-of-bounds access.
+    uint64_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bt_row[b]));
+    phys = phys < static_cast<uint64_t>(num_blocks) ? phys : static_cast<uint64_t>(num_blocks - 1);
+    const int64_t base = static_cast<int64_t>(phys) * blk_stride_bytes + head_off_bytes;
+    const gchar_t* kb = uniform_ptr(kc + base);
+    const gchar_t* vb = uniform_ptr(vc + base);
+#pragma unroll
+    for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + koff);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_dwords<S::kVDw>(f.v[i][r], vb + r * tok_stride_bytes + voff);
+  }
+}
+
+// Scores of one chunk: s[i][r] = scale*log2(e) * <q, K> for token 4*(lane/16)+r
+// of block i and head lane % 16.
+template <typename T, int D, int G, int CB, bool F8 = false>
+__device__ __forceinline__ void qk_chunk(float (&s)[CB][4], const Chunk<T, D, G, CB, F8>& f,
+                                         const u32x4_t (&q)[DecodeShape<T, D, G, CB, F8>::kQSeg],
+                                         float scale_log2) {
+  using S = DecodeShape<T, D, G, CB, F8>;
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sg = 0; sg < S::kKSeg; ++sg) {
+      if constexpr (F8) {
+        // 16 codes per load: dwords 0-1 feed k-step 2*sg, dwords 2-3 k-step
+        // 2*sg+1, converted exactly to bf16 (the query uses the same d order).
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(f.k[i][sg][2 * h], f.k[i][sg][2 * h + 1]),
+                                                      __builtin_bit_cast(bf16x8_t, q[2 * sg + h]), c, 0, 0, 0);
+      } else if constexpr (sizeof(T) == 2) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.k[i][sg]),
+                                                    __builtin_bit_cast(bf16x8_t, q[sg]), c, 0, 0, 0);
+      } else {
+        // Vector elements are read into scalars first: bit-casting a vector
+        // element in place is not reliable.
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(as_float(f.k[i][sg][e]), as_float(q[sg][e]), c, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[i][r] = c[r] * scale_log2;
+  }
+}
+
+}  // namespace pa

@@ -32,6 +32,7 @@ def test_headers_declare_the_boundary():
     inc = os.path.join(ROOT, "include")
     assert declared_functions(os.path.join(inc, "pa.h")) == sorted([
         "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
+        "pa_multi_query",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
         "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
@@ -146,3 +147,21 @@ def test_fp8_host_validation(lib):
     base = [16, 16, 16, 16, 16, 4, 16, 2, 8, 2, 128, 10, 16, c(0.1)]
     assert d(*base, c(1.0), c(1.0), 0, None, None, None) == 2                         # f32 query unsupported
     assert d(*base, c(-1.0), c(1.0), 1, None, None, None) == 1                        # negative scale
+
+
+def test_multi_query_host_validation(lib):
+    f = lib.pa_multi_query
+    c = ctypes.c_float
+    ok = [16, 16, 16, 16, 16, 4, 16, 16]            # out, query, caches, tables, max_blocks, lens, starts
+    shape = [8, 2, 128, 10, 16]                      # H_q, H_kv, head_size, num_blocks, block_size
+    assert f(*ok, 0, 5, *shape, c(0.1), 1, None, None) == 0              # no sequences: nothing launched
+    assert f(*ok, 3, 0, *shape, c(0.1), 1, None, None) == 0              # no new tokens: nothing launched
+    assert f(*ok, 3, 5, *shape, c(-0.1), 1, None, None) == 1             # scale must be > 0
+    assert f(*ok, 3, 5, *shape, c(float("inf")), 1, None, None) == 1
+    assert f(*ok, 3, -1, *shape, c(0.1), 1, None, None) == 1             # negative token count
+    assert f(*ok[:7], None, 3, 5, *shape, c(0.1), 1, None, None) == 1    # no query_start_loc
+    assert f(16, 8, *ok[2:], 3, 5, *shape, c(0.1), 1, None, None) == 1   # misaligned query
+    assert f(*ok, 3, 5, 8, 2, 96, 10, 16, c(0.1), 1, None, None) == 2    # head size
+    assert f(*ok, 3, 5, 8, 3, 128, 10, 16, c(0.1), 1, None, None) == 1   # H_q % H_kv
+    assert f(*ok, 3, 5, 64, 2, 128, 10, 16, c(0.1), 1, None, None) == 2  # group above 16
+    assert f(*ok, 3, 5, *shape, c(0.1), 2, None, None) == 1              # dtype

@@ -391,6 +391,136 @@ def unique_kv_bytes(inp: PagedInputs) -> int:
     return total_tokens * 2 * cfg.num_kv_heads * cfg.head_size * cfg.kv_elem_bytes
 
 
+# ---------------------------------------------------------------- several new tokens per sequence
+@dataclass(frozen=True)
+class MultiQueryConfig:
+    """One step in which sequences may process more than one new token.
+
+    ``base`` gives the head shape, pool and drawn context lengths (the stored
+    tokens after the step, new ones included). ``new_tokens`` is
+    ("fixed", q): every sequence has q new tokens (a speculative step verifying
+    q - 1 draft tokens, llm-stack-book 7.3, "Speculative decoding support"), or
+    ("chunk", m, c, n): the first m sequences run a c-token prompt chunk that
+    ends at context length n, the others one decode token each (one forward
+    pass mixing a prefill slice with decodes, same page, "Prefill, decode, and
+    chunked prefill").
+    """
+
+    name: str
+    base: PagedConfig
+    new_tokens: tuple
+    description: str = ""
+
+
+MQ_CONFIGS: list[MultiQueryConfig] = [
+    MultiQueryConfig(
+        name="llama3_8b_b64_spec4", base=CONFIGS[1], new_tokens=("fixed", 5),
+        description="Speculative verify on the batch-64 Llama-3-8B-shaped decode: k = 4 draft tokens, "
+                    "5 new positions per sequence, ctx U{512..2048}"),
+    MultiQueryConfig(
+        name="llama3_8b_b256_chunk1024", base=CONFIGS[2], new_tokens=("chunk", 1, 1024, 2048),
+        description="The batch-256 decode step with one sequence running a 1024-token prompt chunk "
+                    "(tokens 1024..2047 of its prompt) in the same pass"),
+]
+
+MQ_CONFIG_BY_NAME = {c.name: c for c in MQ_CONFIGS}
+
+
+@dataclass
+class MultiQueryInputs:
+    """Host arrays of one multi-query step. ``paged`` holds the caches with every
+    context complete (new tokens included), the tables and the lengths; the
+    new tokens of sequence i are rows query_start_loc[i] .. query_start_loc[i+1]
+    of ``query`` and positions n_i - q_i .. n_i - 1 of its context."""
+
+    cfg: MultiQueryConfig
+    paged: PagedInputs
+    query_lens: np.ndarray        # int32 [S]
+    query_start_loc: np.ndarray   # int32 [S + 1]
+    query: np.ndarray             # [T, H_q, d_h]
+    slot_mapping: np.ndarray      # int64 [T], -1 for a token with no position
+    new_key: np.ndarray           # [T, H_kv, d_h] (rows of the caches at the slots)
+    new_value: np.ndarray
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+
+def make_multi_inputs(cfg: MultiQueryConfig, mode: str = "parity", seed: int | None = None,
+                      context_lens: np.ndarray | None = None, query_lens: np.ndarray | None = None
+                      ) -> MultiQueryInputs:
+    """Draw one multi-query step: the base workload's inputs (make_inputs, same
+    draws) with the lengths adjusted as ``new_tokens`` says, then the new
+    tokens' queries from a second stream. ``context_lens``/``query_lens``
+    override the lengths."""
+    base = cfg.base
+    s = base.seed if seed is None else seed
+    n = draw_context_lens(base, s) if context_lens is None else np.asarray(context_lens, np.int32).copy()
+    S = n.shape[0]
+    kind = cfg.new_tokens[0]
+    if query_lens is not None:
+        q = np.asarray(query_lens, np.int32).copy()
+    elif kind == "fixed":
+        q = np.full(S, cfg.new_tokens[1], np.int32)
+        n = np.maximum(n, q)
+    elif kind == "chunk":
+        _, m, c, ctx = cfg.new_tokens
+        q = np.ones(S, np.int32)
+        q[:m] = c
+        if context_lens is None:
+            n[:m] = ctx
+    else:
+        raise ValueError(kind)
+    inp = make_inputs(base, mode, seed=s, context_lens=n)
+    loc = np.concatenate([[0], np.cumsum(q, dtype=np.int64)]).astype(np.int32)
+    T = int(loc[-1])
+    rng = np.random.default_rng([s, 101])
+    query = _values(rng, (T, base.num_heads, base.head_size), base.dtype)
+    bs = base.block_size
+    slots = np.full(T, -1, np.int64)
+    for i in range(S):
+        for j in range(int(q[i])):
+            p = int(n[i]) - int(q[i]) + j
+            if p >= 0:
+                slots[loc[i] + j] = int(inp.block_tables[i, p // bs]) * bs + p % bs
+    rows = base.num_blocks * bs
+    ok = slots >= 0
+    shape = (T, base.num_kv_heads, base.head_size)
+    new_key = np.zeros(shape, inp.key_cache.dtype)
+    new_value = np.zeros(shape, inp.value_cache.dtype)
+    new_key[ok] = inp.key_cache.reshape(rows, *shape[1:])[slots[ok]]
+    new_value[ok] = inp.value_cache.reshape(rows, *shape[1:])[slots[ok]]
+    return MultiQueryInputs(cfg=cfg, paged=inp, query_lens=q, query_start_loc=loc, query=query,
+                            slot_mapping=slots, new_key=new_key, new_value=new_value)
+
+
+def multi_caches_before_write(mq: MultiQueryInputs):
+    """The caches before this step's new tokens are written: their rows poisoned."""
+    base = mq.cfg.base
+    rows = base.num_blocks * base.block_size
+    kc, vc = mq.paged.key_cache.copy(), mq.paged.value_cache.copy()
+    ok = mq.slot_mapping >= 0
+    fill = poison_value(base.cache_dtype)
+    kc.reshape(rows, base.num_kv_heads, base.head_size)[mq.slot_mapping[ok]] = fill
+    vc.reshape(rows, base.num_kv_heads, base.head_size)[mq.slot_mapping[ok]] = fill
+    return kc, vc
+
+
+def multi_query_flops(mq: MultiQueryInputs) -> int:
+    """Multiply-adds x 2 of the step's attention: for each new token and query
+    head, 2 d_h flops for its score and 2 d_h for its P*V term per visible key."""
+    base = mq.cfg.base
+    vis = 0
+    for i in range(mq.query_lens.shape[0]):
+        n, q = int(mq.paged.context_lens[i]), int(mq.query_lens[i])
+        first = max(n - q + 1, 0)          # visible keys of the first new token
+        last = max(n, 0)
+        k = max(0, last - first + 1)       # tokens with at least one visible key
+        vis += (first + last) * k // 2
+    return 4 * base.num_heads * base.head_size * vis
+
+
 def small_case(name: str, num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
                dtype: str, ctx: tuple, seed: int, num_blocks: int, partition_size: int = 64,
                kv_dtype: str = "", k_scale: float = 1.0, v_scale: float = 1.0) -> PagedConfig:
