@@ -28,27 +28,31 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 DEFAULT_WORKLOAD = "llama3_8b_b256"
-KERNEL_SOURCES = ["paged_kv_cache_150_amd/csrc/paged_decode.hip", "paged_kv_cache_150_amd/csrc/pa_device.h"]
+KERNEL_SOURCES = ["paged_kv_cache_150_amd/csrc/paged_decode.hip", "paged_kv_cache_150_amd/csrc/pa_device.h",
+                  "paged_kv_cache_150_amd/csrc/pa_tiles.h"]
+MQ_KERNEL_SOURCES = ["paged_kv_cache_150_amd/csrc/multi_query.hip", "paged_kv_cache_150_amd/csrc/pa_device.h",
+                     "paged_kv_cache_150_amd/csrc/pa_tiles.h"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, vendor figure
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, decode: str):
+def stored_traffic(workload: str, decode: str, prefix: str = "paged_decode", sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"paged_decode_{decode}_{workload}_pmc.md")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{decode}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -59,7 +63,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD, help="workload name (see workloads.CONFIGS)")
-    ap.add_argument("--decode", choices=["fused", "split"], default="fused",
+    ap.add_argument("--decode", choices=["fused", "split", "prefix"], default="fused",
                     help="fused: pa_decode (one pass); split: pa_decode_split (partitions + LSE merge)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--order", choices=["longest", "natural"], default="longest",
@@ -68,7 +72,7 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 20 times (counter calibration) and exit")
-    ap.add_argument("--op", choices=["step", "copy_blocks"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "multi_query"], default="step",
                     help="step: reshape + decode (the headline); copy_blocks: pa_copy_blocks on the "
                          "workload's pool (copy-on-write copies), one JSON line of its own")
     ap.add_argument("--pairs", type=int, default=4096, help="copy_blocks: block pairs per launch")
@@ -116,6 +120,129 @@ def bench_copy_blocks(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "pa::copy_blocks_kernel", "algorithmic_bytes_per_launch": moved}}))
+
+
+def bench_multi_query(args):
+    """One multi-query step: reshape_and_cache of every new token, then
+    pa_multi_query over the whole batch (prompt chunks, speculative positions
+    and one-token decodes together). Two pool copies alternate between steps."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_150_amd as pa
+    import workloads as W
+    pa.load_library()
+    name = args.config if args.config in W.MQ_CONFIG_BY_NAME else "llama3_8b_b64_spec4"
+    cfg = W.MQ_CONFIG_BY_NAME[name]
+    base = cfg.base
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    mq = W.make_multi_inputs(cfg, mode="perf")
+    inp = mq.paged
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    pools = [(up(inp.key_cache), up(inp.value_cache)) for _ in range(2)]
+    q, bt, cl, loc = up(mq.query), up(inp.block_tables), up(inp.context_lens), up(mq.query_start_loc)
+    new_k, new_v, slots = up(mq.new_key), up(mq.new_value), up(mq.slot_mapping)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def attend(kc, vc):
+        pa.pa_multi_query(out, q, kc, vc, bt, cl, loc, base.scale, stream=stream)
+
+    print(f"[bench] warmup {args.warmup}, timed {args.steps} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        kc, vc = pools[i & 1]
+        pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+        attend(kc, vc)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_begin.record(stream)
+    for i in range(args.steps):
+        kc, vc = pools[i & 1]
+        pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
+        ev[i][0].record(stream)
+        attend(kc, vc)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    att = [a.elapsed_time(b) for a, b in ev]
+    att_avg = statistics.fmean(att)
+    kv_bytes = W.algorithmic_kv_bytes(base, inp.context_lens)
+    flops = W.multi_query_flops(mq)
+    t_hbm = kv_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    att_gbs = kv_bytes / (att_avg * 1e-3) / 1e9
+    att_tflops = flops / (att_avg * 1e-3) / 1e12
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(att_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": stored_traffic(cfg.name, "mq", "paged_multi_query", MQ_KERNEL_SOURCES),
+                 "kernel": "paged_multi_query_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+                 "algorithmic_flops_per_launch": flops, "achieved_tflops": round(att_tflops, 2),
+                 "kernel_source_hash": kernel_source_hash(MQ_KERNEL_SOURCES)})
+    T = mq.num_tokens
+    rec = {
+        "metric": "multi-query paged attention effective KV GB/s (% of HBM peak), 1 GPU",
+        "value": round(step_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": base.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "description": cfg.description, "num_seqs": base.num_seqs,
+                   "new_tokens": T, "num_heads": base.num_heads, "num_kv_heads": base.num_kv_heads,
+                   "head_size": base.head_size, "block_size": base.block_size, "num_blocks": base.num_blocks,
+                   "mean_context": float(inp.context_lens.mean()),
+                   "step": "pa_reshape_and_cache + pa_multi_query"},
+        "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes, "attention_ms_avg": round(att_avg, 5),
+        "attention_ms_median": round(statistics.median(att), 5),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_multi(mq, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_multi(mq, budget_s: float):
+    """The fp64 oracle's multi-query attention, sequence by sequence in batch
+    order until ~budget_s: KV bytes of the sequences done over the time."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    base, inp = mq.cfg.base, mq.paged
+    loc = mq.query_start_loc
+    order = np.argsort(-mq.query_lens, kind="stable")  # prompt chunks first, then decodes
+    done, t0 = [], time.perf_counter()
+    for i in order:
+        sl = slice(int(loc[i]), int(loc[i + 1]))
+        oracle.paged_multi_query(mq.query[sl], inp.key_cache, inp.value_cache, inp.block_tables[i:i + 1],
+                                 inp.context_lens[i:i + 1], np.array([0, loc[i + 1] - loc[i]]), base.scale,
+                                 base.dtype)
+        done.append(int(i))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    kv = W.algorithmic_kv_bytes(base, inp.context_lens[done])
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, {len(done)} of {base.num_seqs} sequences "
+                      f"({int(mq.query_lens[done].sum())} new tokens) in {dt:.1f} s",
+            "tokens_per_s": float(mq.query_lens[done].sum()) / dt}
 
 
 def copy_calibration(mib: int):
@@ -182,6 +309,9 @@ def main():
     if args.op == "copy_blocks":
         bench_copy_blocks(args)
         return
+    if args.op == "multi_query":
+        bench_multi_query(args)
+        return
 
     import paged_kv_cache_150_amd as pa
     import workloads as W
@@ -218,8 +348,11 @@ def main():
     order = up(np.argsort(-inp.context_lens, kind="stable").astype(np.int32)) if args.order == "longest" else None
     S, Hq, d = cfg.num_seqs, cfg.num_heads, cfg.head_size
     mcl = inp.max_context_len
-    ws = torch.empty(max(256, pa.pa_decode_split_workspace_bytes(S, Hq, d, mcl, P)), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(256, pa.pa_decode_split_workspace_bytes(S, Hq, d, mcl, P),
+                         pa.pa_decode_prefix_workspace_bytes(S, Hq, d)), dtype=torch.uint8, device=dev)
+    if args.decode == "prefix" and inp.shared_prefix_blocks == 0:
+        print(f"bench.py: {cfg.name} has no shared prefix (--decode prefix needs one)", file=sys.stderr)
+        sys.exit(2)
     stream = torch.cuda.current_stream()
 
     def decode(kc, vc):
@@ -228,6 +361,9 @@ def main():
                              stream=stream)
         elif args.decode == "fused":
             pa.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, seq_order=order, stream=stream)
+        elif args.decode == "prefix":
+            pa.pa_decode_prefix(out, q, kc, vc, bt, cl, cfg.scale, inp.shared_prefix_blocks, ws, seq_order=order,
+                                stream=stream)
         else:
             pa.pa_decode_split(out, q, kc, vc, bt, cl, cfg.scale, mcl, P, ws, stream=stream)
 
@@ -272,7 +408,10 @@ def main():
 
     kv_bytes = W.algorithmic_kv_bytes(cfg, inp.context_lens)
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
+    # The shared-prefix decode must read each distinct slot once: its
+    # roofline is priced on the unique bytes.
+    roof_bytes = W.unique_kv_bytes(inp) if args.decode == "prefix" else kv_bytes
+    dec_gbs = roof_bytes / (dec_avg * 1e-3) / 1e9
     traffic = stored_traffic(cfg.name, args.decode)
     rec = {
         "metric": "paged decode attention effective KV GB/s (% of HBM peak) + seqs/sec, 1 GPU",
@@ -291,11 +430,12 @@ def main():
                    "num_kv_heads": cfg.num_kv_heads, "head_size": d, "block_size": cfg.block_size,
                    "num_blocks": cfg.num_blocks, "mean_context": float(inp.context_lens.mean()),
                    "decode": args.decode, "partition_size": P if args.decode == "split" else None,
-                   "seq_order": args.order if args.decode == "fused" else None,
+                   "seq_order": args.order if args.decode in ("fused", "prefix") else None,
+                   "prefix_blocks": inp.shared_prefix_blocks if args.decode == "prefix" else None,
                    "kv_cache": cfg.cache_dtype,
                    "step": ("pa_reshape_and_cache_fp8 + pa_decode_fp8" if fp8 else
-                            "pa_reshape_and_cache + " + ("pa_decode" if args.decode == "fused" else
-                                                         "pa_decode_split"))},
+                            "pa_reshape_and_cache + " + {"fused": "pa_decode", "split": "pa_decode_split",
+                                                         "prefix": "pa_decode_prefix"}[args.decode])},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
@@ -304,9 +444,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_decode_kernel" + ("" if args.decode == "fused" else
-                                                        " + merge_partitions_kernel"),
-                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "kernel": {"fused": "paged_decode_kernel",
+                                "split": "paged_decode_split_kernel + merge_pieces_kernel",
+                                "prefix": "paged_multi_query_kernel (shared prefix) + paged_decode_kernel"
+                                }[args.decode],
+                     "algorithmic_bytes_per_launch": roof_bytes,
                      "kernel_source_hash": kernel_source_hash()},
         "wall_s_timed": round(wall, 4),
     }

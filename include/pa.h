@@ -194,6 +194,47 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               float scale, int32_t dtype, float* lse_out, const int32_t* seq_order, void* stream);
 
 /*
+ * pa_decode_prefix_workspace_bytes - workspace pa_decode_prefix needs: float32
+ * [num_seqs, num_heads, head_size] outputs and float32 [num_seqs, num_heads]
+ * log-sum-exps of the prefix pass, each at a 256-byte aligned offset.
+ * Returns 0 for invalid arguments.
+ */
+size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size);
+
+/*
+ * pa_decode_prefix - pa_decode for a batch whose sequences share a prefix.
+ *
+ * Sequences forked from one prompt (parallel sampling, beam search) or served
+ * from one cached system prompt point their first block-table entries at the
+ * same physical blocks (llm-stack-book 7.3, sections "Copy-on-write for shared
+ * blocks" and "Automatic prefix caching"; modernaiengineering.com lesson
+ * 13.15, "How PagedAttention shares memory"). This call reads those shared
+ * blocks once for the whole batch instead of once per sequence: a first pass
+ * attends every sequence's query over the shared blocks (one context, all
+ * queries at once, on the matrix cores), a second pass attends each sequence
+ * over its own remaining blocks and merges the two parts exactly with their
+ * log-sum-exps. The result is the pa_decode result.
+ *
+ *   prefix_blocks     the number of leading block-table entries shared by every
+ *                     sequence: entries [0, prefix_blocks) of every row must
+ *                     equal row 0's (caller contract; the shared part is read
+ *                     through row 0). A sequence with n_i < prefix_blocks *
+ *                     block_size sees its first n_i keys. 0 runs pa_decode.
+ *   workspace         device memory of at least
+ *                     pa_decode_prefix_workspace_bytes(...) bytes, 256-byte
+ *                     aligned, owned by the caller.
+ * Other arguments as pa_decode. Two kernels are queued on `stream`.
+ * Returns PA_OK or an error status (PA_ERR_WORKSPACE for a short or misaligned
+ * workspace).
+ */
+int pa_decode_prefix(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                     int64_t num_blocks, int32_t block_size, float scale, int32_t dtype, int32_t prefix_blocks,
+                     void* workspace, size_t workspace_bytes, float* lse_out, const int32_t* seq_order,
+                     void* stream);
+
+/*
  * pa_multi_query - paged attention for several new tokens per sequence.
  *
  * One step may give a sequence more than one new token: a slice of a long

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
-    "pa_multi_query", "pa_decode_split_workspace_bytes", "pa_decode_split",
+    "pa_multi_query", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix", "pa_decode_split_workspace_bytes", "pa_decode_split",
     "pa_merge_partitions", "pa_status_string",
 ]
 
@@ -69,6 +69,11 @@ def load_library() -> ctypes.CDLL:
     lib.pa_multi_query.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f, c_i32, c_p, c_p]
     lib.pa_multi_query.restype = c_int
+    lib.pa_decode_prefix_workspace_bytes.argtypes = [c_i32, c_i32, c_i32]
+    lib.pa_decode_prefix_workspace_bytes.restype = c_sz
+    lib.pa_decode_prefix.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
+                                     c_f, c_i32, c_i32, c_p, c_sz, c_p, c_p, c_p]
+    lib.pa_decode_prefix.restype = c_int
     lib.pa_decode_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_split_workspace_bytes.restype = c_sz
     lib.pa_decode_split.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
@@ -245,6 +250,31 @@ def pa_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tens
                             _dev(query_start_loc, "query_start_loc", torch.int32, 1), S, T, Hq, Hkv, d, NB, bs,
                             float(scale), _dtype_code(query), lse_ptr, _stream(stream))
     _check(st, "pa_multi_query")
+
+
+def pa_decode_prefix_workspace_bytes(num_seqs: int, num_heads: int, head_size: int) -> int:
+    return int(load_library().pa_decode_prefix_workspace_bytes(num_seqs, num_heads, head_size))
+
+
+def pa_decode_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                     block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, prefix_blocks: int,
+                     workspace: torch.Tensor, lse_out: torch.Tensor | None = None,
+                     seq_order: torch.Tensor | None = None, stream=None) -> None:
+    """pa_decode for sequences whose first ``prefix_blocks`` block-table entries
+    are shared (equal to row 0's): the shared blocks are read once for the batch."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out)
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.shape != (S,):
+            raise ValueError("seq_order must be [num_seqs]")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
+    ws = _dev(workspace, "workspace")
+    lib = load_library()
+    st = lib.pa_decode_prefix(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
+                              float(scale), _dtype_code(query), int(prefix_blocks), ws,
+                              workspace.numel() * workspace.element_size(), p["lse"], order_ptr, _stream(stream))
+    _check(st, "pa_decode_prefix")
 
 
 def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

@@ -30,14 +30,16 @@
 //  * Probabilities enter the bf16 MFMA rounded to bf16 (relative error at
 //    most 2^-9 per weight); the normaliser and the log-sum-exp use the fp32
 //    values. fp32 caches use the fp32 MFMA and keep fp32 probabilities.
-//  * Online softmax in base 2, per column; a column with no visible key yet
-//    keeps weight 0 (its running maximum stays -inf).
+//  * Online softmax in base 2, per column, with a reference point that moves
+//    only when a chunk's maximum exceeds it by more than 2^8 in weight; a
+//    column with no visible key yet keeps weight 0.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 
 #include "pa.h"
 #include "pa_device.h"
+#include "pa_internal.h"
 #include "pa_tiles.h"
 
 namespace pa {
@@ -67,6 +69,14 @@ struct MultiArgs {
   int32_t tile_tokens;  // new tokens per tile: 16 * NT / group
   int32_t num_slots;    // tile slots: num_tokens / tile_tokens + num_seqs
   float scale_log2;     // scale * log2(e)
+  // Shared-prefix pass (prefix_keys > 0): one context, the first
+  // prefix_keys / 16 blocks of block table row 0, attended by num_tokens
+  // queries, query row t being sequence t's decode query; column (t, h) sees
+  // min(context_lens[t], prefix_keys) keys. Normalised float32 outputs and
+  // log-sum-exps go to part_o [num_tokens, num_heads, D] / part_lse.
+  int32_t prefix_keys;
+  float* part_o;
+  float* part_lse;
 };
 
 // Tile slots: sequence i owns slots [B_i, B_{i+1}) with
@@ -121,9 +131,10 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int w = 0; w < S::kVDw; ++w) vz[i][r][w] = f.v[i][r][w];
+  // Raw scores <q, K>; scale*log2(e) is applied inside the exponent.
   float s[NT][CB][4];
 #pragma unroll
-  for (int p = 0; p < NT; ++p) qk_chunk<T, D, 16, CB>(s[p], f, q[p], scale_log2);
+  for (int p = 0; p < NT; ++p) qk_chunk<T, D, 16, CB>(s[p], f, q[p], 1.0f);
   if (mask) {
     // Keys at or past the tile's last position: weight 0 for every column,
     // and their V rows (possibly stale or poisoned) are replaced by 0.
@@ -139,7 +150,14 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
         for (int w = 0; w < S::kVDw; ++w) vz[i][r][w] = live ? vz[i][r][w] : 0u;
       }
   }
-  float pw[NT][CB][4];
+  // Online softmax with a lazily moved reference point: a column's reference
+  // m only moves (and its partial sums are rescaled) when the chunk maximum
+  // exceeds it by more than kLazy (base-2 units), so weights stay below
+  // 2^kLazy and most chunks skip the rescaling of the accumulators. A
+  // column with no visible key yet keeps m = -inf and weight 0.
+  constexpr float kLazy = 8.0f;
+  float alpha[NT];
+  bool any = false;
 #pragma unroll
   for (int p = 0; p < NT; ++p) {
     float mx = s[p][0][0];
@@ -147,27 +165,35 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
     for (int i = 0; i < CB; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[p][i][r]);
-    mx = rows_max(mx);
-    const float m_new = fmaxf(st.m[p], mx);
-    // With no visible key yet the reference point is 0: every weight is then
-    // exp2(-inf) = 0 and the (zero) partial sums stay zero.
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = fast_exp2(st.m[p] - m_use);
-    st.m[p] = m_new;
+    mx = rows_max(mx) * scale_log2;
+    const bool move = mx > st.m[p] + kLazy;
+    alpha[p] = move ? fast_exp2(st.m[p] - mx) : 1.f;
+    st.m[p] = move ? mx : st.m[p];
+    any = any || move;
+  }
+  if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
-    for (int i = 0; i < CB; ++i)
+    for (int p = 0; p < NT; ++p) {
+      st.l[p] *= alpha[p];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pw[p][i][r] = fast_exp2(s[p][i][r] - m_use);
+      for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.acc[p][t][r] *= alpha[p];
+    }
+  }
+  float pw[NT][CB][4];
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    const float neg_m = st.m[p] == -__builtin_inff() ? 0.f : -st.m[p];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < CB; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) psum += pw[p][i][r];
-    st.l[p] = st.l[p] * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.acc[p][t][r] *= alpha;
+      for (int r = 0; r < 4; ++r) {
+        pw[p][i][r] = fast_exp2(fmaf(s[p][i][r], scale_log2, neg_m));
+        psum += pw[p][i][r];
+      }
+    st.l[p] += psum;
   }
 
   if constexpr (sizeof(T) == 2) {
@@ -277,32 +303,54 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   int slot, kvh;
   wg_to_slot_head(blockIdx.x, a.num_kv_heads, slot, kvh);
   if (slot >= a.num_slots) return;
-  const int seq = __builtin_amdgcn_readfirstlane(slot_owner(a, slot, lane));
-  if (seq >= a.num_seqs) return;
-  const int q0 = clamp_loc(a.query_start_loc[seq], a.num_tokens);
-  const int q1 = clamp_loc(a.query_start_loc[seq + 1], a.num_tokens);
-  const int ql = q1 - q0;
-  if (ql <= 0) return;
-  const int ntiles = (ql + a.tile_tokens - 1) / a.tile_tokens;
-  const int r = slot - (q0 / a.tile_tokens + seq);
-  if (r < 0 || r >= ntiles) return;
-  // Later tiles see longer contexts: they take the lower slots of the sequence.
-  const int tile = ntiles - 1 - r;
-  const int tok0 = tile * a.tile_tokens;                     // first new token of the tile
-  const int ntok = min(a.tile_tokens, ql - tok0);
-  const int ncols = ntok * g;
-
   const int max_tokens = a.max_blocks * kBlockTokens;
-  const int n_raw = a.context_lens[seq];
-  const int n = n_raw < 0 ? 0 : (n_raw > max_tokens ? max_tokens : n_raw);
-  const int pos0 = n - ql + tok0;                            // position of the tile's first token
-  const int key_end = max(0, pos0 + ntok);                   // keys [0, key_end) are read
+  auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > max_tokens ? max_tokens : v); };
+  int seq, q0, tok0, ntok, key_end, min_lim;
   int lim[NT];
+  if (a.prefix_keys > 0) {
+    // Shared-prefix pass: tile `slot` of the queries, all over row 0's prefix.
+    seq = 0;
+    q0 = 0;
+    tok0 = slot * a.tile_tokens;
+    if (tok0 >= a.num_tokens) return;
+    ntok = min(a.tile_tokens, a.num_tokens - tok0);
+    key_end = 0;
+    min_lim = a.prefix_keys;
+    for (int t = 0; t < ntok; ++t) {
+      const int k = min(clamp_len(a.context_lens[tok0 + t]), a.prefix_keys);
+      key_end = max(key_end, k);
+      min_lim = min(min_lim, k);
+    }
 #pragma unroll
-  for (int p = 0; p < NT; ++p) {
-    const int c = 16 * p + (lane & 15);
-    lim[p] = c < ncols ? pos0 + c / g + 1 : 0;
+    for (int p = 0; p < NT; ++p) {
+      const int c = 16 * p + (lane & 15);
+      lim[p] = c < ntok * g ? min(clamp_len(a.context_lens[tok0 + c / g]), a.prefix_keys) : 0;
+    }
+  } else {
+    seq = __builtin_amdgcn_readfirstlane(slot_owner(a, slot, lane));
+    if (seq >= a.num_seqs) return;
+    q0 = clamp_loc(a.query_start_loc[seq], a.num_tokens);
+    const int q1 = clamp_loc(a.query_start_loc[seq + 1], a.num_tokens);
+    const int ql = q1 - q0;
+    if (ql <= 0) return;
+    const int ntiles = (ql + a.tile_tokens - 1) / a.tile_tokens;
+    const int r = slot - (q0 / a.tile_tokens + seq);
+    if (r < 0 || r >= ntiles) return;
+    // Later tiles see longer contexts: they take the lower slots of the sequence.
+    const int tile = ntiles - 1 - r;
+    tok0 = tile * a.tile_tokens;                               // first new token of the tile
+    ntok = min(a.tile_tokens, ql - tok0);
+    const int n = clamp_len(a.context_lens[seq]);
+    const int pos0 = n - ql + tok0;                            // position of the tile's first token
+    key_end = max(0, pos0 + ntok);                             // keys [0, key_end) are read
+    min_lim = pos0 + 1;
+#pragma unroll
+    for (int p = 0; p < NT; ++p) {
+      const int c = 16 * p + (lane & 15);
+      lim[p] = c < ntok * g ? pos0 + c / g + 1 : 0;
+    }
   }
+  const int ncols = ntok * g;
 
   const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
   const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
@@ -313,9 +361,9 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   const int blk_end = (key_end + kBlockTokens - 1) / kBlockTokens;
   const int nchunk = (blk_end + CB - 1) / CB;
   const int blk_last = blk_end - 1;
-  // Chunks from mask_from on reach past the first token's position.
+  // Chunks from mask_from on reach past some column's last visible key.
   constexpr int kChunkTokens = CB * kBlockTokens;
-  const int mask_from = max(pos0 + 1, 0) / kChunkTokens;
+  const int mask_from = max(min_lim, 0) / kChunkTokens;
   const int mine = wave < nchunk ? (nchunk - wave + kMqWaves - 1) / kMqWaves : 0;
   auto blk_of = [&](int i) { return (wave + i * kMqWaves) * CB; };
   auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
@@ -334,7 +382,9 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   }
 
   // Register double buffer with unconditional steady-state loads and a peeled
-  // tail, as in the decode kernel; only a wave's last chunk can need a mask.
+  // tail, as in the decode kernel. For new tokens of one sequence only a
+  // wave's last chunk can need a mask; in the shared-prefix pass columns may
+  // stop anywhere, so every chunk checks.
   Chunk<T, D, 16, CB> fa, fb;
   if (mine > 0) {
     load_chunk<T, D, 16, CB>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
@@ -344,12 +394,12 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
       load_chunk<T, D, 16, CB>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
                                head_off, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, false, lane);
+      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       __builtin_amdgcn_sched_barrier(0);
       load_chunk<T, D, 16, CB>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride, blk_stride,
                                head_off, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, false, lane);
+      mq_chunk<T, D, CB, NT>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
@@ -400,9 +450,14 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
     }
     const int tok = c / g;
     const int64_t row = (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
-    store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
-    if (a.lse_out != nullptr && d == 0)
-      a.lse_out[row] = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
+    const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
+    if (a.part_o != nullptr) {
+      a.part_o[row * D + d] = o;
+      if (d == 0) a.part_lse[row] = lse;
+    } else {
+      store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
+      if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
+    }
   }
 }
 
@@ -445,6 +500,43 @@ int pick_tiles(int num_tokens, int num_seqs, int group) {
 }
 
 }  // namespace
+
+int pa::launch_prefix_pass(const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                           int64_t num_blocks, int32_t prefix_blocks, float scale, int32_t dtype, float* part_o,
+                           float* part_lse, hipStream_t stream) {
+  const int g = num_heads / num_kv_heads;
+  const int NT = (dtype == PA_DTYPE_F32 && head_size == 128) ? 1 : pick_tiles(num_seqs, 1, g);
+  MultiKernel k = pick_multi(dtype, head_size, NT);
+  MultiArgs a{};
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = nullptr;
+  a.out = nullptr;
+  a.lse_out = nullptr;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = 1;
+  a.num_tokens = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = g;
+  a.tile_tokens = 16 * NT / g;
+  const int64_t slots = (static_cast<int64_t>(num_seqs) + a.tile_tokens - 1) / a.tile_tokens;
+  const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
+  if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  a.num_slots = static_cast<int32_t>(slots);
+  a.scale_log2 = scale * kLog2e;
+  a.prefix_keys = prefix_blocks * kBlockTokens;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
 
 extern "C" int pa_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
                               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -493,6 +585,9 @@ extern "C" int pa_multi_query(void* out, const void* query, const void* key_cach
   if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
   a.num_slots = static_cast<int32_t>(slots);
   a.scale_log2 = scale * kLog2e;
+  a.prefix_keys = 0;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;

@@ -38,6 +38,7 @@
 
 #include "pa.h"
 #include "pa_device.h"
+#include "pa_internal.h"
 #include "pa_tiles.h"
 
 namespace pa {
@@ -60,6 +61,13 @@ struct DecodeArgs {
   int32_t num_jobs;     // job ids: ceil(num_seqs / 8) * 8 * num_kv_heads
   float scale_log2;     // scale * log2(e) (times k_scale for FP8 caches)
   float v_scale;        // multiplies the normalised output: v_scale for FP8 caches, else 1
+  // Suffix pass of the shared-prefix decode: keys of blocks < skip_blocks were
+  // attended by the prefix pass, whose normalised float32 output and
+  // log-sum-exp per (sequence, query head) join the final merge. Zero / null
+  // for a plain decode.
+  int32_t skip_blocks;
+  const float* prefix_o;    // [num_seqs, num_heads, D]
+  const float* prefix_lse;  // [num_seqs, num_heads]
 };
 
 // Workgroup -> (sequence, kv head). Consecutive workgroups are dispatched to
@@ -243,16 +251,18 @@ struct JobPlan {
   int mask_chunk;  // the chunk that reaches past the context end, or -1
 };
 
+// Chunk c of a job starts at block skip_blocks + c * CB.
+
 template <int EB, int D, int CB>  // EB: bytes per cache element
 __device__ __forceinline__ JobPlan plan_job(const DecodeArgs& a, const DecodeJob& j, int wave, int nwaves) {
   JobPlan p;
   p.bt_row = a.block_tables + static_cast<int64_t>(j.seq < 0 ? 0 : j.seq) * a.max_blocks;
   p.head_off = static_cast<int64_t>(j.kvh) * D * EB;
   const int blk_end = (j.n + kBlockTokens - 1) / kBlockTokens;
-  const int nchunk = (blk_end + CB - 1) / CB;
+  const int nchunk = blk_end > a.skip_blocks ? (blk_end - a.skip_blocks + CB - 1) / CB : 0;
   p.blk_last = blk_end - 1;
   p.mine = (j.seq >= 0 && wave < nchunk) ? (nchunk - wave + nwaves - 1) / nwaves : 0;
-  p.mask_chunk = (nchunk * CB * kBlockTokens > j.n) ? nchunk - 1 : -1;
+  p.mask_chunk = ((a.skip_blocks + nchunk * CB) * kBlockTokens > j.n) ? nchunk - 1 : -1;
   return p;
 }
 
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(Deco
   if (id0 < a.num_jobs) cur = decode_job(a, id0);
   JobPlan pc = plan_job<S::kElemBytes, D, CB>(a, cur, wave, nwaves);
   // Block of this wave's i-th chunk of a job.
-  auto blk_of = [&](int i) { return (wave + i * nwaves) * CB; };
+  auto blk_of = [&](int i) { return a.skip_blocks + (wave + i * nwaves) * CB; };
 
   u32x4_t q[S::kQSeg];
   Chunk<T, D, G, CB, F8> fa;
@@ -391,13 +401,20 @@ __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(Deco
     __syncthreads();
 
     if (cur.seq >= 0) {
-      // Merge the waves: weights 2^(m_w - M).
+      // Merge the waves: weights 2^(m_w - M). A prefix-pass result joins as
+      // one more part with l = 1, acc = its output and m = its lse in base 2.
       const int head0 = cur.kvh * g;
       for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
         const int h = idx / D;
         const int d = idx - h * D;
+        const int64_t row = static_cast<int64_t>(cur.seq) * a.num_heads + head0 + h;
         float M = -__builtin_inff();
         for (int v = 0; v < nwaves; ++v) M = fmaxf(M, s_m[v][h]);
+        float pm = -__builtin_inff();
+        if (a.prefix_o != nullptr) {
+          pm = a.prefix_lse[row] * kLog2e;
+          M = fmaxf(M, pm);
+        }
         float o = 0.f, L = 0.f;
         if (M != -__builtin_inff()) {
           for (int v = 0; v < nwaves; ++v) {
@@ -405,10 +422,14 @@ __global__ __launch_bounds__(256, G >= 16 ? 1 : 2) void paged_decode_kernel(Deco
             L = fmaf(wt, s_l[v][h], L);
             o = fmaf(wt, s_acc[(v * G + h) * D + d], o);
           }
+          if (pm != -__builtin_inff()) {
+            const float wt = fast_exp2(pm - M);
+            L += wt;
+            o = fmaf(wt, a.prefix_o[row * D + d], o);
+          }
           o = o / L * a.v_scale;
         }
         const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
-        const int64_t row = static_cast<int64_t>(cur.seq) * a.num_heads + head0 + h;
         store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
         if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
       }
@@ -1063,6 +1084,62 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   args.scale_log2 = scale * kLog2e;
   args.v_scale = 1.0f;
   return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
+  return align256(rows * head_size * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+extern "C" int pa_decode_prefix(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
+                                float scale, int32_t dtype, int32_t prefix_blocks, void* workspace,
+                                size_t workspace_bytes, float* lse_out, const int32_t* seq_order, void* stream) {
+  int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq) return PA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (prefix_blocks == 0)
+    return pa_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_size, num_blocks, block_size, scale, dtype, lse_out, seq_order,
+                     stream);
+  const size_t need = pa_decode_prefix_workspace_bytes(num_seqs, num_heads, head_size);
+  if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return PA_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * head_size * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_prefix_pass(query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                          num_heads, num_kv_heads, head_size, num_blocks, prefix_blocks, scale, dtype, part_o,
+                          part_lse, s);
+  if (st != PA_OK) return st;
+  DecodeArgs args{};
+  args.query = query;
+  args.key_cache = key_cache;
+  args.value_cache = value_cache;
+  args.block_tables = block_tables;
+  args.context_lens = context_lens;
+  args.out = out;
+  args.lse_out = lse_out;
+  args.seq_order = seq_order;
+  args.num_blocks = num_blocks;
+  args.max_blocks = max_blocks_per_seq;
+  args.num_seqs = num_seqs;
+  args.num_heads = num_heads;
+  args.num_kv_heads = num_kv_heads;
+  args.group = num_heads / num_kv_heads;
+  args.scale_log2 = scale * kLog2e;
+  args.v_scale = 1.0f;
+  args.skip_blocks = prefix_blocks;
+  args.prefix_o = part_o;
+  args.prefix_lse = part_lse;
+  return launch_decode(args, num_seqs, dtype, head_size, s);
 }
 
 extern "C" int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,

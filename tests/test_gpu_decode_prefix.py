@@ -1,0 +1,120 @@
+"""GPU parity for pa_decode_prefix (shared-prefix decode: one pass over the
+shared blocks for all queries, one over each sequence's own blocks, exact
+log-sum-exp merge) against the oracle's decode."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import LSE_TOL, TOL, Dev, bits, ensure_built, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    return ensure_built()
+
+
+def _prefix_decode(pa, dev, prefix_blocks, lse=True, order=None):
+    S, Hq, d = dev.q.shape
+    ws = torch.empty(pa.pa_decode_prefix_workspace_bytes(S, Hq, d), dtype=torch.uint8, device="cuda")
+    out = torch.full_like(dev.q, float("nan"))
+    lse_t = torch.full((S, Hq), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    pa.pa_decode_prefix(out, dev.q, dev.kc, dev.vc, dev.bt, dev.cl, dev.cfg.scale, prefix_blocks, ws,
+                        lse_out=lse_t, seq_order=order)
+    torch.cuda.synchronize()
+    return out, lse_t
+
+
+def _check(inp, out, lse):
+    ref, ref_lse = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                                       inp.context_lens, inp.cfg.scale, inp.cfg.dtype)
+    dt = inp.cfg.dtype
+    assert np.abs(f64(out) - ref).max() <= TOL[dt]
+    assert np.abs(f64(lse) - ref_lse).max() <= LSE_TOL[dt]
+
+
+CASES = [(d, Hq, Hkv, dt, P) for dt in ("bf16", "f32") for d in (64, 128)
+         for Hq, Hkv in ((64, 8), (8, 2), (16, 16), (12, 4)) for P in (1, 3)]
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,dtype,P", CASES, ids=lambda v: str(v))
+def test_prefix_decode_matches_the_oracle(pa, d, Hq, Hkv, dtype, P):
+    lens = P * 16 + np.array([0, 1, 15, 16, 17, 100, 3, 64, 0, 250, 33], np.int32)
+    cfg = W.small_case("prefix", len(lens), Hq, Hkv, d, dtype, ("prefix", P * 16, 0, 1), seed=41, num_blocks=140)
+    inp = W.make_inputs(cfg, context_lens=lens)
+    out, lse = _prefix_decode(pa, Dev(inp), P)
+    _check(inp, out, lse)
+
+
+def test_sequences_shorter_than_the_prefix(pa):
+    """Contexts that end inside the shared blocks see only their own tokens."""
+    lens = np.array([48, 5, 16, 31, 47, 60, 1], np.int32)
+    cfg = W.small_case("prefix", len(lens), 32, 8, 128, "bf16", ("prefix", 48, 0, 1), seed=42, num_blocks=60)
+    inp = W.make_inputs(cfg, mode="perf", context_lens=np.maximum(lens, 48))
+    inp.context_lens = lens
+    out, lse = _prefix_decode(pa, Dev(inp), 3)
+    _check(inp, out, lse)
+
+
+def test_zero_prefix_is_pa_decode(pa):
+    cfg = W.small_case("prefix", 9, 32, 8, 128, "bf16", ("prefix", 32, 1, 200), seed=43, num_blocks=140)
+    dev = Dev(W.make_inputs(cfg))
+    a, la = _prefix_decode(pa, dev, 0)
+    b, lb = dev.decode(pa, lse=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(a), bits(b))
+    np.testing.assert_array_equal(bits(la), bits(lb))
+
+
+def test_schedule_and_placement_do_not_change_bits(pa):
+    cfg = W.small_case("prefix", 20, 64, 8, 128, "bf16", ("prefix", 64, 1, 300), seed=44, num_blocks=300)
+    inp = W.make_inputs(cfg)
+    dev = Dev(inp)
+    a, la = _prefix_decode(pa, dev, 4)
+    order = to_dev(np.argsort(-inp.context_lens, kind="stable").astype(np.int32))
+    b, lb = _prefix_decode(pa, dev, 4, order=order)
+    np.testing.assert_array_equal(bits(a), bits(b))
+    np.testing.assert_array_equal(bits(la), bits(lb))
+    perm = np.random.default_rng(3).permutation(cfg.num_blocks)
+    inv = np.argsort(perm)
+    moved = W.make_inputs(cfg)
+    moved.key_cache, moved.value_cache = inp.key_cache[perm], inp.value_cache[perm]
+    moved.block_tables = np.where(inp.block_tables >= 0, inv[np.maximum(inp.block_tables, 0)], -1).astype(np.int32)
+    c, lc = _prefix_decode(pa, Dev(moved), 4)
+    np.testing.assert_array_equal(bits(a), bits(c))
+    np.testing.assert_array_equal(bits(la), bits(lc))
+
+
+def test_workspace_and_argument_errors(pa):
+    cfg = W.small_case("prefix", 3, 8, 2, 64, "bf16", ("prefix", 32, 1, 20), seed=45, num_blocks=40)
+    dev = Dev(W.make_inputs(cfg))
+    S, Hq, d = dev.q.shape
+    out = torch.empty_like(dev.q)
+    small = torch.empty(pa.pa_decode_prefix_workspace_bytes(S, Hq, d) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_prefix(out, dev.q, dev.kc, dev.vc, dev.bt, dev.cl, cfg.scale, 2, small)
+    assert e.value.status == 3
+    ws = torch.empty(pa.pa_decode_prefix_workspace_bytes(S, Hq, d), dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PaError):
+        pa.pa_decode_prefix(out, dev.q, dev.kc, dev.vc, dev.bt, dev.cl, cfg.scale, dev.bt.shape[1] + 1, ws)
+
+
+def test_prefix_70b_full_size(pa):
+    """The 70B-shaped shared-prefix workload at full size: the shared-prefix
+    decode against pa_decode everywhere and against the oracle on a sample."""
+    cfg = W.CONFIG_BY_NAME["prefix_70b"]
+    inp = W.make_inputs(cfg)
+    dev = Dev(inp)
+    out, lse = _prefix_decode(pa, dev, inp.shared_prefix_blocks)
+    ref_out, ref_lse = dev.decode(pa, lse=True)
+    torch.cuda.synchronize()
+    assert np.abs(f64(out) - f64(ref_out)).max() <= TOL["bf16"]
+    assert np.abs(f64(lse) - f64(ref_lse)).max() <= LSE_TOL["bf16"]
+    rows = np.random.default_rng(2).choice(cfg.num_seqs, 10, replace=False)
+    ref, rl = oracle.paged_decode(inp.query[rows], inp.key_cache, inp.value_cache, inp.block_tables[rows],
+                                  inp.context_lens[rows], cfg.scale, "bf16")
+    assert np.abs(f64(out)[rows] - ref).max() <= TOL["bf16"]
+    assert np.abs(f64(lse)[rows] - rl).max() <= LSE_TOL["bf16"]
