@@ -14,13 +14,15 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import torch
 
 __all__ = [
-    "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library",
+    "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library", "prepared",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
-    "pa_multi_query", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix", "pa_decode_split_workspace_bytes", "pa_decode_split",
+    "pa_multi_query", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
+    "pa_decode_split_workspace_bytes", "pa_decode_split",
     "pa_merge_partitions", "pa_status_string",
 ]
 
@@ -122,6 +124,38 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+_capture = threading.local()
+
+
+def _invoke(fn, where: str, *args) -> None:
+    """One library call with its status checked, or, inside prepared(), the
+    call recorded for replay."""
+    rec = getattr(_capture, "calls", None)
+    if rec is not None:
+        rec.append((fn, args, where))
+        return
+    _check(fn(*args), where)
+
+
+def prepared(fn, *args, **kwargs):
+    """Validate the arguments of binding function ``fn`` once and return a
+    zero-argument callable that repeats exactly the same library call(s)
+    (same tensors, sizes and stream) with only the ctypes call per launch.
+    For launch loops where the per-call checks would cost more than the
+    kernel; the tensors must stay alive and unchanged in shape."""
+    _capture.calls = []
+    try:
+        fn(*args, **kwargs)
+        calls = _capture.calls
+    finally:
+        _capture.calls = None
+
+    def run():
+        for f, a, where in calls:
+            _check(f(*a), where)
+    return run
+
+
 def _check(status: int, where: str) -> None:
     if status != 0:
         raise PaError(status, where)
@@ -148,11 +182,10 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [num_tokens]")
     lib = load_library()
-    st = lib.pa_reshape_and_cache(_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
-                                  _dev(value_cache, "value_cache"),
-                                  _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d,
-                                  _dtype_code(key_cache), _stream(stream))
-    _check(st, "pa_reshape_and_cache")
+    _invoke(lib.pa_reshape_and_cache, "pa_reshape_and_cache", _dev(key, "key"), _dev(value, "value"),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d, _dtype_code(key_cache),
+            _stream(stream))
 
 
 def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mapping: torch.Tensor,
@@ -162,10 +195,9 @@ def pa_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_map
     if block_mapping.dim() != 2 or int(block_mapping.shape[1]) != 2:
         raise ValueError("block_mapping must be [num_pairs, 2]")
     lib = load_library()
-    st = lib.pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
-                            _dev(block_mapping, "block_mapping", torch.int64, 2), int(block_mapping.shape[0]), NB,
-                            bs, Hkv, d, _dtype_code(key_cache), _stream(stream))
-    _check(st, "pa_copy_blocks")
+    _invoke(lib.pa_copy_blocks, "pa_copy_blocks", _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(block_mapping, "block_mapping", torch.int64, 2), int(block_mapping.shape[0]), NB, bs, Hkv, d,
+            _dtype_code(key_cache), _stream(stream))
 
 
 def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens, lse_out, fp8=False):
@@ -213,9 +245,8 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
             raise ValueError("seq_order must be [num_seqs]")
         order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
     lib = load_library()
-    st = lib.pa_decode(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
-                       float(scale), _dtype_code(query), p["lse"], order_ptr, _stream(stream))
-    _check(st, "pa_decode")
+    _invoke(lib.pa_decode, "pa_decode", p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d,
+            NB, bs, float(scale), _dtype_code(query), p["lse"], order_ptr, _stream(stream))
 
 
 def pa_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
@@ -244,12 +275,12 @@ def pa_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tens
             raise ValueError("lse_out must be [num_tokens, num_heads]")
         lse_ptr = _dev(lse_out, "lse_out", torch.float32)
     lib = load_library()
-    st = lib.pa_multi_query(_dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
-                            _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32, 2),
-                            int(block_tables.shape[1]), _dev(context_lens, "context_lens", torch.int32, 1),
-                            _dev(query_start_loc, "query_start_loc", torch.int32, 1), S, T, Hq, Hkv, d, NB, bs,
-                            float(scale), _dtype_code(query), lse_ptr, _stream(stream))
-    _check(st, "pa_multi_query")
+    _invoke(lib.pa_multi_query, "pa_multi_query", _dev(out, "out"), _dev(query, "query"),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(block_tables, "block_tables", torch.int32, 2), int(block_tables.shape[1]),
+            _dev(context_lens, "context_lens", torch.int32, 1),
+            _dev(query_start_loc, "query_start_loc", torch.int32, 1), S, T, Hq, Hkv, d, NB, bs, float(scale),
+            _dtype_code(query), lse_ptr, _stream(stream))
 
 
 def pa_decode_prefix_workspace_bytes(num_seqs: int, num_heads: int, head_size: int) -> int:
@@ -271,10 +302,9 @@ def pa_decode_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Te
         order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
     ws = _dev(workspace, "workspace")
     lib = load_library()
-    st = lib.pa_decode_prefix(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
-                              float(scale), _dtype_code(query), int(prefix_blocks), ws,
-                              workspace.numel() * workspace.element_size(), p["lse"], order_ptr, _stream(stream))
-    _check(st, "pa_decode_prefix")
+    _invoke(lib.pa_decode_prefix, "pa_decode_prefix", p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"],
+            S, Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), int(prefix_blocks), ws,
+            workspace.numel() * workspace.element_size(), p["lse"], order_ptr, _stream(stream))
 
 
 def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
@@ -290,11 +320,10 @@ def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: 
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [num_tokens]")
     lib = load_library()
-    st = lib.pa_reshape_and_cache_fp8(_dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
-                                      _dev(value_cache, "value_cache"),
-                                      _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d,
-                                      _dtype_code(key), float(k_scale), float(v_scale), _stream(stream))
-    _check(st, "pa_reshape_and_cache_fp8")
+    _invoke(lib.pa_reshape_and_cache_fp8, "pa_reshape_and_cache_fp8", _dev(key, "key"), _dev(value, "value"),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, bs, Hkv, d, _dtype_code(key), float(k_scale),
+            float(v_scale), _stream(stream))
 
 
 def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
@@ -310,10 +339,9 @@ def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tenso
             raise ValueError("seq_order must be [num_seqs]")
         order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
     lib = load_library()
-    st = lib.pa_decode_fp8(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
-                           float(scale), float(k_scale), float(v_scale), _dtype_code(query), p["lse"], order_ptr,
-                           _stream(stream))
-    _check(st, "pa_decode_fp8")
+    _invoke(lib.pa_decode_fp8, "pa_decode_fp8", p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq,
+            Hkv, d, NB, bs, float(scale), float(k_scale), float(v_scale), _dtype_code(query), p["lse"], order_ptr,
+            _stream(stream))
 
 
 def pa_decode_split_workspace_bytes(num_seqs: int, num_heads: int, head_size: int, max_context_len: int,
@@ -332,10 +360,9 @@ def pa_decode_split(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Ten
     ws = _dev(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
     lib = load_library()
-    st = lib.pa_decode_split(p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S, Hq, Hkv, d, NB, bs,
-                             float(scale), _dtype_code(query), int(max_context_len), int(partition_size), ws,
-                             nbytes, p["lse"], _stream(stream))
-    _check(st, "pa_decode_split")
+    _invoke(lib.pa_decode_split, "pa_decode_split", p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S,
+            Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), int(max_context_len), int(partition_size), ws,
+            nbytes, p["lse"], _stream(stream))
 
 
 def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head_size: int,
@@ -373,7 +400,6 @@ def pa_merge_partitions(out: torch.Tensor, o_parts: torch.Tensor, lse_parts: tor
             raise ValueError("lse_out must be [S, H]")
         lse_ptr = _dev(lse_out, "lse_out", torch.float32)
     lib = load_library()
-    st = lib.pa_merge_partitions(_dev(out, "out"), lse_ptr, _dev(o_parts, "o_parts", torch.float32),
-                                 _dev(lse_parts, "lse_parts", torch.float32), S, H, P, d, _dtype_code(out),
-                                 _stream(stream))
-    _check(st, "pa_merge_partitions")
+    _invoke(lib.pa_merge_partitions, "pa_merge_partitions", _dev(out, "out"), lse_ptr,
+            _dev(o_parts, "o_parts", torch.float32), _dev(lse_parts, "lse_parts", torch.float32), S, H, P, d,
+            _dtype_code(out), _stream(stream))

@@ -37,26 +37,38 @@ def _check(inp, out, lse):
 
 
 CASES = [(d, Hq, Hkv, dt, P) for dt in ("bf16", "f32") for d in (64, 128)
-         for Hq, Hkv in ((64, 8), (8, 2), (16, 16), (12, 4)) for P in (1, 3)]
+         for Hq, Hkv in ((64, 8), (8, 2), (16, 16), (12, 4)) for P in (1, 3, 9)]
 
 
 @pytest.mark.parametrize("d,Hq,Hkv,dtype,P", CASES, ids=lambda v: str(v))
 def test_prefix_decode_matches_the_oracle(pa, d, Hq, Hkv, dtype, P):
     lens = P * 16 + np.array([0, 1, 15, 16, 17, 100, 3, 64, 0, 250, 33], np.int32)
-    cfg = W.small_case("prefix", len(lens), Hq, Hkv, d, dtype, ("prefix", P * 16, 0, 1), seed=41, num_blocks=140)
+    cfg = W.small_case("prefix", len(lens), Hq, Hkv, d, dtype, ("prefix", P * 16, 0, 1), seed=41, num_blocks=160)
     inp = W.make_inputs(cfg, context_lens=lens)
     out, lse = _prefix_decode(pa, Dev(inp), P)
     _check(inp, out, lse)
 
 
-def test_sequences_shorter_than_the_prefix(pa):
-    """Contexts that end inside the shared blocks see only their own tokens."""
-    lens = np.array([48, 5, 16, 31, 47, 60, 1], np.int32)
-    cfg = W.small_case("prefix", len(lens), 32, 8, 128, "bf16", ("prefix", 48, 0, 1), seed=42, num_blocks=60)
-    inp = W.make_inputs(cfg, mode="perf", context_lens=np.maximum(lens, 48))
+@pytest.mark.parametrize("P", [3, 9, 16])
+def test_sequences_shorter_than_the_prefix(pa, P):
+    """Contexts that end inside the shared blocks (in any of its key ranges)
+    see only their own tokens."""
+    k = P * 16
+    lens = np.array([k, 5, 16, 31, k - 1, k + 12, 1, k // 2, k // 2 + 1, 80, 81, 0], np.int32)
+    cfg = W.small_case("prefix", len(lens), 32, 8, 128, "bf16", ("prefix", k, 0, 1), seed=42, num_blocks=60)
+    inp = W.make_inputs(cfg, mode="perf", context_lens=np.maximum(lens, k))
     inp.context_lens = lens
-    out, lse = _prefix_decode(pa, Dev(inp), 3)
-    _check(inp, out, lse)
+    out, lse = _prefix_decode(pa, Dev(inp), P)
+    _check_allow_empty(inp, out, lse)
+
+
+def _check_allow_empty(inp, out, lse):
+    ref, ref_lse = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables,
+                                       inp.context_lens, inp.cfg.scale, inp.cfg.dtype)
+    dead = inp.context_lens == 0
+    assert (f64(out)[dead] == 0).all() and np.isneginf(f64(lse)[dead]).all()
+    assert np.abs(f64(out)[~dead] - ref[~dead]).max() <= TOL["bf16"]
+    assert np.abs(f64(lse)[~dead] - ref_lse[~dead]).max() <= LSE_TOL["bf16"]
 
 
 def test_zero_prefix_is_pa_decode(pa):
