@@ -109,11 +109,11 @@ struct MqState {
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{a, b}, bf16x2v_t));
 }
-// Element t of a lane's bf16 piece, taken from two rows, packed (row a low).
+// Element t of a lane's bf16 piece, taken from two rows, packed (row a low):
+// one byte permute (bytes 0-3 of x, 4-7 of y).
 template <int T_>
 __device__ __forceinline__ uint32_t pick_bf16(const uint32_t* ra, const uint32_t* rb) {
-  const uint32_t x = ra[T_ / 2], y = rb[T_ / 2];
-  return (T_ & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+  return __builtin_amdgcn_perm(rb[T_ / 2], ra[T_ / 2], (T_ & 1) ? 0x07060302u : 0x05040100u);
 }
 
 template <typename T, int D, int CB, int NT>
@@ -167,13 +167,14 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[p][i][r]);
     mx = rows_max(mx) * scale_log2;
     const bool move = mx > st.m[p] + kLazy;
-    alpha[p] = move ? fast_exp2(st.m[p] - mx) : 1.f;
+    alpha[p] = move ? st.m[p] - mx : 0.f;  // log2 of the rescale factor
     st.m[p] = move ? mx : st.m[p];
     any = any || move;
   }
   if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
     for (int p = 0; p < NT; ++p) {
+      alpha[p] = fast_exp2(alpha[p]);
       st.l[p] *= alpha[p];
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
