@@ -100,20 +100,15 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
 }
 
 // Eight FP8 codes (two dwords) to eight bf16 values, the MFMA operand. Every
-// E4M3 value is exact in bfloat16 (3 mantissa bits, exponents 2^-9 .. 2^8), so
-// keeping the upper half of the float32 is exact.
+// E4M3 value is exact in bfloat16 (3 mantissa bits, exponents 2^-9 .. 2^8);
+// gfx950 converts two codes straight to two bf16 (scale 1, exact).
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  uint32_t out[4];
-  const uint32_t w[2] = {w0, w1};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float a, b, c, d;
-    fp8x2_to_f32<false>(w[i], a, b);
-    fp8x2_to_f32<true>(w[i], c, d);
-    out[2 * i] = (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u) | (__builtin_bit_cast(uint32_t, a) >> 16);
-    out[2 * i + 1] = (__builtin_bit_cast(uint32_t, d) & 0xFFFF0000u) | (__builtin_bit_cast(uint32_t, c) >> 16);
-  }
-  return __builtin_bit_cast(bf16x8_t, u32x4_t{out[0], out[1], out[2], out[3]});
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{fp8x2_to_bf16x2(w0, false), fp8x2_to_bf16x2(w0, true),
+                                              fp8x2_to_bf16x2(w1, false), fp8x2_to_bf16x2(w1, true)});
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
