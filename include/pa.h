@@ -194,6 +194,18 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               float scale, int32_t dtype, float* lse_out, const int32_t* seq_order, void* stream);
 
 /*
+ * pa_multi_query_fp8 - pa_multi_query over FP8 (E4M3) caches: attention on
+ * value(code) * scale, bf16 query and out (dtype PA_DTYPE_BF16, anything else
+ * is PA_ERR_UNSUPPORTED), k_scale folded into the scores and v_scale into the
+ * normalised output, as in pa_decode_fp8. Other arguments as pa_multi_query.
+ */
+int pa_multi_query_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size, float scale,
+                       float k_scale, float v_scale, int32_t dtype, float* lse_out, void* stream);
+
+/*
  * pa_decode_prefix_workspace_bytes - workspace pa_decode_prefix needs: float32
  * [num_seqs, num_heads, head_size] outputs and float32 [num_seqs, num_heads]
  * log-sum-exps of the prefix pass, each at a 256-byte aligned offset.

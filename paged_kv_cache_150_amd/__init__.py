@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library", "prepared",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
-    "pa_multi_query", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
+    "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
     "pa_decode_split_workspace_bytes", "pa_decode_split",
     "pa_merge_partitions", "pa_status_string",
 ]
@@ -71,6 +71,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_multi_query.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f, c_i32, c_p, c_p]
     lib.pa_multi_query.restype = c_int
+    lib.pa_multi_query_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                       c_i64, c_i32, c_f, c_f, c_f, c_i32, c_p, c_p]
+    lib.pa_multi_query_fp8.restype = c_int
     lib.pa_decode_prefix_workspace_bytes.argtypes = [c_i32, c_i32, c_i32]
     lib.pa_decode_prefix_workspace_bytes.restype = c_sz
     lib.pa_decode_prefix.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
@@ -249,20 +252,18 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
             NB, bs, float(scale), _dtype_code(query), p["lse"], order_ptr, _stream(stream))
 
 
-def pa_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                   block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
-                   scale: float, lse_out: torch.Tensor | None = None, stream=None) -> None:
-    """Paged attention for several new tokens per sequence (prompt chunks, speculative positions).
-
-    ``query``/``out`` are [num_tokens, num_heads, head_size]; sequence i's new
-    tokens are rows ``query_start_loc[i] .. query_start_loc[i+1]`` (int32
-    [num_seqs + 1]) and are the last of its ``context_lens[i]`` stored tokens.
-    """
+def _multi_common(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc, lse_out,
+                  fp8=False):
     NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
     if query.dim() != 3 or int(query.shape[2]) != d:
         raise ValueError("query must be [num_tokens, num_heads, head_size]")
     T, Hq = int(query.shape[0]), int(query.shape[1])
-    if out.shape != query.shape or out.dtype != query.dtype or query.dtype != key_cache.dtype:
+    if fp8:
+        if key_cache.dtype != torch.uint8:
+            raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+        if out.shape != query.shape or out.dtype != query.dtype:
+            raise ValueError("out must match query's shape and dtype")
+    elif out.shape != query.shape or out.dtype != query.dtype or query.dtype != key_cache.dtype:
         raise ValueError("out must match query's shape; query, out and caches share one dtype")
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
@@ -274,12 +275,37 @@ def pa_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tens
         if lse_out.shape != (T, Hq):
             raise ValueError("lse_out must be [num_tokens, num_heads]")
         lse_ptr = _dev(lse_out, "lse_out", torch.float32)
-    lib = load_library()
-    _invoke(lib.pa_multi_query, "pa_multi_query", _dev(out, "out"), _dev(query, "query"),
-            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+    ptrs = (_dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
             _dev(block_tables, "block_tables", torch.int32, 2), int(block_tables.shape[1]),
             _dev(context_lens, "context_lens", torch.int32, 1),
-            _dev(query_start_loc, "query_start_loc", torch.int32, 1), S, T, Hq, Hkv, d, NB, bs, float(scale),
+            _dev(query_start_loc, "query_start_loc", torch.int32, 1), S, T, Hq, Hkv, d, NB, bs)
+    return ptrs, lse_ptr
+
+
+def pa_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                   scale: float, lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """Paged attention for several new tokens per sequence (prompt chunks, speculative positions).
+
+    ``query``/``out`` are [num_tokens, num_heads, head_size]; sequence i's new
+    tokens are rows ``query_start_loc[i] .. query_start_loc[i+1]`` (int32
+    [num_seqs + 1]) and are the last of its ``context_lens[i]`` stored tokens.
+    """
+    ptrs, lse_ptr = _multi_common(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                                  lse_out)
+    lib = load_library()
+    _invoke(lib.pa_multi_query, "pa_multi_query", *ptrs, float(scale), _dtype_code(query), lse_ptr, _stream(stream))
+
+
+def pa_multi_query_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                       scale: float, k_scale: float, v_scale: float, lse_out: torch.Tensor | None = None,
+                       stream=None) -> None:
+    """pa_multi_query over FP8 (E4M3 code) caches with scales k_scale, v_scale; bf16 query/out."""
+    ptrs, lse_ptr = _multi_common(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                                  lse_out, fp8=True)
+    lib = load_library()
+    _invoke(lib.pa_multi_query_fp8, "pa_multi_query_fp8", *ptrs, float(scale), float(k_scale), float(v_scale),
             _dtype_code(query), lse_ptr, _stream(stream))
 
 

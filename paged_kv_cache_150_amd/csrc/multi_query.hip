@@ -56,7 +56,9 @@ struct MultiArgs {
   const void* value_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;    // tokens stored per sequence, new ones included
-  const int32_t* query_start_loc; // [num_seqs + 1]: sequence i's new tokens are rows [loc[i], loc[i+1])
+  const int32_t* query_start_loc; // [num_seqs + 1]: sequence i's new tokens are rows [loc[i], loc[i+1]);
+                                  // null: one new token per sequence, row i (decode)
+  const int32_t* seq_order;       // decode only, optional: slot i takes sequence seq_order[i]
   void* out;                      // [num_tokens, num_heads, D]
   float* lse_out;                 // optional [num_tokens, num_heads]
   int64_t num_blocks;
@@ -68,7 +70,8 @@ struct MultiArgs {
   int32_t group;        // H_q / H_kv
   int32_t tile_tokens;  // new tokens per tile: 16 * NT / group
   int32_t num_slots;    // tile slots: num_tokens / tile_tokens + num_seqs
-  float scale_log2;     // scale * log2(e)
+  float scale_log2;     // scale * log2(e) (times k_scale for FP8 caches)
+  float v_scale;        // multiplies the normalised output: v_scale for FP8 caches, else 1
   // Shared-prefix pass (prefix_keys > 0): one context, the first
   // prefix_keys / 16 blocks of block table row 0, attended by num_tokens
   // queries, query row t being sequence t's decode query; column (t, h) sees
@@ -77,6 +80,12 @@ struct MultiArgs {
   int32_t prefix_keys;
   float* part_o;
   float* part_lse;
+  // Decode mode as the suffix pass of the shared-prefix decode: keys of
+  // blocks < skip_blocks were attended by the prefix pass, whose normalised
+  // output and log-sum-exp per (sequence, query head) join the final merge.
+  int32_t skip_blocks;
+  const float* prefix_o;    // [num_seqs, num_heads, D]
+  const float* prefix_lse;  // [num_seqs, num_heads]
 };
 
 // Tile slots: sequence i owns slots [B_i, B_{i+1}) with
@@ -116,12 +125,12 @@ __device__ __forceinline__ uint32_t pick_bf16(const uint32_t* ra, const uint32_t
   return __builtin_amdgcn_perm(rb[T_ / 2], ra[T_ / 2], (T_ & 1) ? 0x07060302u : 0x05040100u);
 }
 
-template <typename T, int D, int CB, int NT>
-__device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<T, D, 16, CB>& f,
-                                         const u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB>::kQSeg],
+template <typename T, int D, int CB, int NT, bool F8>
+__device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<T, D, 16, CB, F8>& f,
+                                         const u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB, F8>::kQSeg],
                                          float scale_log2, int tok0, const int (&lim)[NT], int key_end,
                                          bool mask, int lane) {
-  using S = DecodeShape<T, D, 16, CB>;
+  using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kTiles = D / 16;
   const int rg = lane >> 4;
   uint32_t vz[CB][4][S::kVDw];
@@ -134,7 +143,7 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
   // Raw scores <q, K>; scale*log2(e) is applied inside the exponent.
   float s[NT][CB][4];
 #pragma unroll
-  for (int p = 0; p < NT; ++p) qk_chunk<T, D, 16, CB>(s[p], f, q[p], 1.0f);
+  for (int p = 0; p < NT; ++p) qk_chunk<T, D, 16, CB, F8>(s[p], f, q[p], 1.0f);
   if (mask) {
     // Keys at or past the tile's last position: weight 0 for every column,
     // and their V rows (possibly stale or poisoned) are replaced by 0.
@@ -199,7 +208,21 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
 
   if constexpr (sizeof(T) == 2) {
     // bf16: probabilities rounded to bf16, contracted with V over 8 keys of
-    // two blocks per MFMA, or 4 keys of the odd block out.
+    // two blocks per MFMA, or 4 keys of the odd block out. FP8 V codes are
+    // first converted to bf16 (exact), giving the same per-lane rows.
+    constexpr int kBW = D / 32;  // bf16 dwords of a lane's piece of one row
+    uint32_t vb[CB][4][kBW];
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int w = 0; w < kBW; ++w) {
+          if constexpr (F8)
+            vb[i][r][w] = fp8x2_to_bf16x2(vz[i][r][w / 2], (w & 1) != 0);
+          else
+            vb[i][r][w] = vz[i][r][w];
+        }
 #pragma unroll
     for (int i = 0; i < CB; i += 2) {
       if (i + 1 < CB) {
@@ -211,8 +234,8 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
         }
         static_for<kTiles>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          const u32x4_t av = {pick_bf16<t>(vz[i][0], vz[i][1]), pick_bf16<t>(vz[i][2], vz[i][3]),
-                              pick_bf16<t>(vz[i + 1][0], vz[i + 1][1]), pick_bf16<t>(vz[i + 1][2], vz[i + 1][3])};
+          const u32x4_t av = {pick_bf16<t>(vb[i][0], vb[i][1]), pick_bf16<t>(vb[i][2], vb[i][3]),
+                              pick_bf16<t>(vb[i + 1][0], vb[i + 1][1]), pick_bf16<t>(vb[i + 1][2], vb[i + 1][3])};
 #pragma unroll
           for (int p = 0; p < NT; ++p)
             st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
@@ -227,7 +250,7 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
         }
         static_for<kTiles>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          const u32x2_t av = {pick_bf16<t>(vz[i][0], vz[i][1]), pick_bf16<t>(vz[i][2], vz[i][3])};
+          const u32x2_t av = {pick_bf16<t>(vb[i][0], vb[i][1]), pick_bf16<t>(vb[i][2], vb[i][3])};
 #pragma unroll
           for (int p = 0; p < NT; ++p)
             st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, av),
@@ -264,11 +287,11 @@ __device__ __forceinline__ void wg_to_slot_head(int id, int num_kv_heads, int& s
 // Query fragments of a tile's columns: column c = 16 p + (lane % 16) is new
 // token c / g (row `row0` + c / g) and head head0 + c % g; columns past the
 // tile's `ncols` get zeros. Same d order as the K operand of qk_chunk.
-template <typename T, int D, int CB, int NT>
+template <typename T, int D, int CB, int NT, bool F8>
 __device__ __forceinline__ void load_query_cols(const void* query, int64_t row0, int num_heads, int head0, int g,
                                                 int ncols, int lane,
-                                                u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB>::kQSeg]) {
-  using S = DecodeShape<T, D, 16, CB>;
+                                                u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB, F8>::kQSeg]) {
+  using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kQBytes = static_cast<int>(sizeof(T));
   const int j = lane >> 4;
   const gchar_t* qb = uniform_ptr(static_cast<const char*>(query) + (row0 * num_heads + head0) * D * kQBytes);
@@ -280,7 +303,10 @@ __device__ __forceinline__ void load_query_cols(const void* query, int64_t row0,
     const uint32_t qoff = valid ? static_cast<uint32_t>((tok * num_heads + c - tok * g) * D * kQBytes) : 0u;
 #pragma unroll
     for (int sg = 0; sg < S::kQSeg; ++sg) {
-      u32x4_t v = gload16(qb + sg * 64 + j * 16 + qoff);
+      // The K operand's d order: 32 sg + 8 j + e for bf16/fp32 caches; for
+      // FP8 caches (16 codes per lane per load) 64 (sg/2) + 16 j + 8 (sg%2) + e.
+      const uint32_t off = F8 ? 128 * (sg / 2) + 32 * j + 16 * (sg % 2) : sg * 64 + j * 16;
+      u32x4_t v = gload16(qb + off + qoff);
       q[p][sg] = valid ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
@@ -288,9 +314,9 @@ __device__ __forceinline__ void load_query_cols(const void* query, int64_t row0,
 
 // One workgroup per (tile slot, kv head); slot ids follow the decode kernel's
 // XCD-aware order (id % 8 names the XCD; the kv heads of a slot share it).
-template <typename T, int D, int CB, int NT>
+template <typename T, int D, int CB, int NT, bool F8>
 __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(MultiArgs a) {
-  using S = DecodeShape<T, D, 16, CB>;
+  using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kCols = 16 * NT;
   constexpr int kRow = D + 1;  // LDS row stride in floats (spreads the 16 columns over banks)
   __shared__ float s_acc[kMqWaves][kCols][kRow];
@@ -306,7 +332,9 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   if (slot >= a.num_slots) return;
   const int max_tokens = a.max_blocks * kBlockTokens;
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > max_tokens ? max_tokens : v); };
-  int seq, q0, tok0, ntok, key_end, min_lim;
+  // The tile reads keys [16 * blk_begin, key_end); column p of this lane sees
+  // keys below lim[p]; min_lim is the smallest limit of the tile's columns.
+  int seq, q0, tok0, ntok, key_end, min_lim, blk_begin = 0;
   int lim[NT];
   if (a.prefix_keys > 0) {
     // Shared-prefix pass: tile `slot` of the queries, all over row 0's prefix.
@@ -328,14 +356,30 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
       lim[p] = c < ntok * g ? min(clamp_len(a.context_lens[tok0 + c / g]), a.prefix_keys) : 0;
     }
   } else {
-    seq = __builtin_amdgcn_readfirstlane(slot_owner(a, slot, lane));
-    if (seq >= a.num_seqs) return;
-    q0 = clamp_loc(a.query_start_loc[seq], a.num_tokens);
-    const int q1 = clamp_loc(a.query_start_loc[seq + 1], a.num_tokens);
+    int q1, r;
+    if (a.query_start_loc == nullptr) {
+      // One new token per sequence (decode): slot i is sequence i (or
+      // seq_order[i], clamped), query row = sequence.
+      if (slot >= a.num_seqs) return;
+      seq = slot;
+      if (a.seq_order != nullptr) {
+        const uint32_t o = static_cast<uint32_t>(a.seq_order[slot]);
+        seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
+      }
+      blk_begin = a.skip_blocks;
+      q0 = seq;
+      q1 = seq + 1;
+      r = 0;
+    } else {
+      seq = __builtin_amdgcn_readfirstlane(slot_owner(a, slot, lane));
+      if (seq >= a.num_seqs) return;
+      q0 = clamp_loc(a.query_start_loc[seq], a.num_tokens);
+      q1 = clamp_loc(a.query_start_loc[seq + 1], a.num_tokens);
+      r = slot - (q0 / a.tile_tokens + seq);
+    }
     const int ql = q1 - q0;
     if (ql <= 0) return;
     const int ntiles = (ql + a.tile_tokens - 1) / a.tile_tokens;
-    const int r = slot - (q0 / a.tile_tokens + seq);
     if (r < 0 || r >= ntiles) return;
     // Later tiles see longer contexts: they take the lower slots of the sequence.
     const int tile = ntiles - 1 - r;
@@ -360,18 +404,18 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   const char* vc = static_cast<const char*>(a.value_cache);
   const int32_t* bt_row = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
   const int blk_end = (key_end + kBlockTokens - 1) / kBlockTokens;
-  const int nchunk = (blk_end + CB - 1) / CB;
+  const int nchunk = blk_end > blk_begin ? (blk_end - blk_begin + CB - 1) / CB : 0;
   const int blk_last = blk_end - 1;
   // Chunks from mask_from on reach past some column's last visible key.
   constexpr int kChunkTokens = CB * kBlockTokens;
-  const int mask_from = max(min_lim, 0) / kChunkTokens;
+  const int mask_from = max(min_lim - blk_begin * kBlockTokens, 0) / kChunkTokens;
   const int mine = wave < nchunk ? (nchunk - wave + kMqWaves - 1) / kMqWaves : 0;
-  auto blk_of = [&](int i) { return (wave + i * kMqWaves) * CB; };
+  auto blk_of = [&](int i) { return blk_begin + (wave + i * kMqWaves) * CB; };
   auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
   auto is_mask = [&](int i) { return wave + i * kMqWaves >= mask_from; };
 
   u32x4_t q[NT][S::kQSeg];
-  load_query_cols<T, D, CB, NT>(a.query, q0 + tok0, a.num_heads, kvh * g, g, ncols, lane, q);
+  load_query_cols<T, D, CB, NT, F8>(a.query, q0 + tok0, a.num_heads, kvh * g, g, ncols, lane, q);
 
   MqState<T, D, CB, NT> st;
 #pragma unroll
@@ -386,31 +430,31 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   // tail, as in the decode kernel. For new tokens of one sequence only a
   // wave's last chunk can need a mask; in the shared-prefix pass columns may
   // stop anywhere, so every chunk checks.
-  Chunk<T, D, 16, CB> fa, fb;
+  Chunk<T, D, 16, CB, F8> fa, fb;
   if (mine > 0) {
-    load_chunk<T, D, 16, CB>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
+    load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
                              head_off, lane);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
-      load_chunk<T, D, 16, CB>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
+      load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
                                head_off, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk<T, D, 16, CB>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride, blk_stride,
+      load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride, blk_stride,
                                head_off, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
+      mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
-      load_chunk<T, D, 16, CB>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
+      load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
                                head_off, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
-      mq_chunk<T, D, CB, NT>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
+      mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
     } else {
-      mq_chunk<T, D, CB, NT>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
     }
   }
 
@@ -436,9 +480,15 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   for (int idx = threadIdx.x; idx < ncols * D; idx += kMqWaves * kWave) {
     const int c = idx / D;
     const int d = idx - c * D;
+    const int tok = c / g;
+    const int64_t row = (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
     float M = -__builtin_inff();
 #pragma unroll
     for (int v = 0; v < kMqWaves; ++v) M = fmaxf(M, s_m[v][c]);
+    // A prefix-pass result joins as one more part: l = 1, acc = its output,
+    // m = its log-sum-exp in base 2.
+    const float pm = a.prefix_o != nullptr ? a.prefix_lse[row] * kLog2e : -__builtin_inff();
+    M = fmaxf(M, pm);
     float o = 0.f, L = 0.f;
     if (M != -__builtin_inff()) {
 #pragma unroll
@@ -447,10 +497,13 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
         L = fmaf(wt, s_l[v][c], L);
         o = fmaf(wt, s_acc[v][c][d], o);
       }
-      o = o / L;
+      if (pm != -__builtin_inff()) {
+        const float wt = fast_exp2(pm - M);
+        L += wt;
+        o = fmaf(wt, a.prefix_o[row * D + d], o);
+      }
+      o = o / L * a.v_scale;
     }
-    const int tok = c / g;
-    const int64_t row = (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
     const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
     if (a.part_o != nullptr) {
       a.part_o[row * D + d] = o;
@@ -471,21 +524,29 @@ using namespace pa;
 
 typedef void (*MultiKernel)(MultiArgs);
 
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, bool F8>
 MultiKernel multi_kernel_for() {
-  constexpr int kRegsPerBlock = D * static_cast<int>(sizeof(T)) / 8;  // K + V dwords per lane
+  constexpr int kElem = F8 ? 1 : static_cast<int>(sizeof(T));
+  constexpr int kRegsPerBlock = D * kElem / 8;  // K + V dwords per lane
   constexpr int CB = (kRegsPerBlock <= 32 && NT == 1) ? 2 : 1;
-  return paged_multi_query_kernel<T, D, CB, NT>;
+  return paged_multi_query_kernel<T, D, CB, NT, F8>;
 }
 
-MultiKernel pick_multi(int dtype, int D, int NT) {
-  if (dtype == PA_DTYPE_BF16) {
-    if (D == 128) return NT == 1 ? multi_kernel_for<bf16_t, 128, 1>() : multi_kernel_for<bf16_t, 128, 2>();
-    return NT == 1 ? multi_kernel_for<bf16_t, 64, 1>() : multi_kernel_for<bf16_t, 64, 2>();
-  }
-  if (D == 128) return multi_kernel_for<float, 128, 1>();
-  return NT == 1 ? multi_kernel_for<float, 64, 1>() : multi_kernel_for<float, 64, 2>();
+template <typename T, bool F8>
+MultiKernel pick_multi_t(int D, int NT) {
+  if (D == 128) return NT == 1 ? multi_kernel_for<T, 128, 1, F8>() : multi_kernel_for<T, 128, 2, F8>();
+  return NT == 1 ? multi_kernel_for<T, 64, 1, F8>() : multi_kernel_for<T, 64, 2, F8>();
 }
+
+// fp32 caches with 128-element heads keep 16-column tiles (32 would spill).
+MultiKernel pick_multi(int dtype, int D, int NT, bool fp8_cache) {
+  if (fp8_cache) return pick_multi_t<bf16_t, true>(D, NT);
+  if (dtype == PA_DTYPE_BF16) return pick_multi_t<bf16_t, false>(D, NT);
+  if (D == 128) return multi_kernel_for<float, 128, 1, false>();
+  return NT == 1 ? multi_kernel_for<float, 64, 1, false>() : multi_kernel_for<float, 64, 2, false>();
+}
+
+int max_tiles(int dtype, int D) { return (dtype == PA_DTYPE_F32 && D == 128) ? 1 : 2; }
 
 inline bool aligned16_mq(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -500,6 +561,72 @@ int pick_tiles(int num_tokens, int num_seqs, int group) {
   return static_cast<int64_t>(num_tokens) * group > static_cast<int64_t>(num_seqs) * 16 ? 2 : 1;
 }
 
+// Shared host checks of the multi-query entry points.
+int check_multi(const void* out, const void* query, const void* key_cache, const void* value_cache,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                int64_t num_blocks, int32_t block_size, float scale, int32_t dtype) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned16_mq(out) || !aligned16_mq(query) || !aligned16_mq(key_cache) || !aligned16_mq(value_cache))
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// One multi-query launch. query_start_loc == nullptr: one new token per
+// sequence (query row i is sequence i's), 16-column tiles.
+int launch_multi(void* out, const void* query, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                 const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                 int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, float scale_log2, float v_scale,
+                 int32_t dtype, bool fp8_cache, float* lse_out, const int32_t* seq_order, hipStream_t stream,
+                 int32_t skip_blocks = 0, const float* prefix_o = nullptr, const float* prefix_lse = nullptr) {
+  const int g = num_heads / num_kv_heads;
+  int NT = query_start_loc == nullptr ? 1 : pick_tiles(num_tokens, num_seqs, g);
+  NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
+  MultiKernel k = pick_multi(dtype, head_size, NT, fp8_cache);
+  MultiArgs a{};
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.seq_order = query_start_loc == nullptr ? seq_order : nullptr;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = g;
+  a.tile_tokens = 16 * NT / g;
+  const int64_t slots =
+      query_start_loc == nullptr ? num_seqs : static_cast<int64_t>(num_tokens) / a.tile_tokens + num_seqs;
+  const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
+  if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  a.num_slots = static_cast<int32_t>(slots);
+  a.scale_log2 = scale_log2;
+  a.v_scale = v_scale;
+  a.skip_blocks = skip_blocks;
+  a.prefix_o = prefix_o;
+  a.prefix_lse = prefix_lse;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 int pa::launch_prefix_pass(const void* query, const void* key_cache, const void* value_cache,
@@ -508,17 +635,15 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
                            int64_t num_blocks, int32_t prefix_blocks, float scale, int32_t dtype, float* part_o,
                            float* part_lse, hipStream_t stream) {
   const int g = num_heads / num_kv_heads;
-  const int NT = (dtype == PA_DTYPE_F32 && head_size == 128) ? 1 : pick_tiles(num_seqs, 1, g);
-  MultiKernel k = pick_multi(dtype, head_size, NT);
+  int NT = pick_tiles(num_seqs, 1, g);
+  NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
+  MultiKernel k = pick_multi(dtype, head_size, NT, false);
   MultiArgs a{};
   a.query = query;
   a.key_cache = key_cache;
   a.value_cache = value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.query_start_loc = nullptr;
-  a.out = nullptr;
-  a.lse_out = nullptr;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = 1;
@@ -532,6 +657,7 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
   if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
   a.num_slots = static_cast<int32_t>(slots);
   a.scale_log2 = scale * kLog2e;
+  a.v_scale = 1.0f;
   a.prefix_keys = prefix_blocks * kBlockTokens;
   a.part_o = part_o;
   a.part_lse = part_lse;
@@ -539,57 +665,46 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int pa::launch_decode_multi(void* out, const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int64_t num_blocks, float scale_log2, float v_scale, int32_t dtype, bool fp8_cache,
+                            float* lse_out, const int32_t* seq_order, int32_t skip_blocks, const float* prefix_o,
+                            const float* prefix_lse, hipStream_t stream) {
+  return launch_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, nullptr,
+                      num_seqs, num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale_log2, v_scale,
+                      dtype, fp8_cache, lse_out, seq_order, stream, skip_blocks, prefix_o, prefix_lse);
+}
+
 extern "C" int pa_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
                               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                               const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
                               int32_t block_size, float scale, int32_t dtype, float* lse_out, void* stream) {
-  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0)
-    return PA_ERR_INVALID_ARG;
-  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
-  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
-  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || scale == __builtin_inff()) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens || !query_start_loc)
-    return PA_ERR_INVALID_ARG;
-  if (!aligned16_mq(out) || !aligned16_mq(query) || !aligned16_mq(key_cache) || !aligned16_mq(value_cache))
-    return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+  int st = check_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_tokens, num_heads, num_kv_heads, head_size, num_blocks, block_size, scale, dtype);
+  if (st != PA_OK || num_seqs == 0 || num_tokens == 0) return st;
+  if (!query_start_loc) return PA_ERR_INVALID_ARG;
+  return launch_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                      query_start_loc, num_seqs, num_tokens, num_heads, num_kv_heads, head_size, num_blocks,
+                      scale * kLog2e, 1.0f, dtype, false, lse_out, nullptr, static_cast<hipStream_t>(stream));
+}
 
-  const int g = num_heads / num_kv_heads;
-  // fp32 caches with 128-element heads keep 16-column tiles (32 would spill).
-  const int NT = (dtype == PA_DTYPE_F32 && head_size == 128) ? 1 : pick_tiles(num_tokens, num_seqs, g);
-  MultiKernel k = pick_multi(dtype, head_size, NT);
-  MultiArgs a;
-  a.query = query;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.query_start_loc = query_start_loc;
-  a.out = out;
-  a.lse_out = lse_out;
-  a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_tokens = num_tokens;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = g;
-  a.tile_tokens = 16 * NT / g;
-  const int64_t slots = static_cast<int64_t>(num_tokens) / a.tile_tokens + num_seqs;
-  const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
-  if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
-  a.num_slots = static_cast<int32_t>(slots);
-  a.scale_log2 = scale * kLog2e;
-  a.prefix_keys = 0;
-  a.part_o = nullptr;
-  a.part_lse = nullptr;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+extern "C" int pa_multi_query_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                                  int32_t dtype, float* lse_out, void* stream) {
+  int st = check_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_tokens, num_heads, num_kv_heads, head_size, num_blocks, block_size, scale, dtype);
+  if (st != PA_OK || num_seqs == 0 || num_tokens == 0) return st;
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
+    return PA_ERR_INVALID_ARG;
+  if (!query_start_loc) return PA_ERR_INVALID_ARG;
+  return launch_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                      query_start_loc, num_seqs, num_tokens, num_heads, num_kv_heads, head_size, num_blocks,
+                      scale * k_scale * kLog2e, v_scale, dtype, true, lse_out, nullptr,
+                      static_cast<hipStream_t>(stream));
 }

@@ -18,4 +18,17 @@ int launch_prefix_pass(const void* query, const void* key_cache, const void* val
                        int64_t num_blocks, int32_t prefix_blocks, float scale, int32_t dtype, float* part_o,
                        float* part_lse, hipStream_t stream);
 
+// One-token-per-sequence decode through the multi-query kernel (P*V on the
+// matrix cores; one workgroup per (sequence, kv head), dispatched in
+// seq_order): scale_log2 = scale * log2(e), times k_scale for FP8 caches.
+// With skip_blocks > 0 it is the suffix pass of the shared-prefix decode
+// (prefix_o / prefix_lse as the decode kernel's). Arguments are validated by
+// the caller.
+int launch_decode_multi(void* out, const void* query, const void* key_cache, const void* value_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                        int64_t num_blocks, float scale_log2, float v_scale, int32_t dtype, bool fp8_cache,
+                        float* lse_out, const int32_t* seq_order, int32_t skip_blocks, const float* prefix_o,
+                        const float* prefix_lse, hipStream_t stream);
+
 }  // namespace pa

@@ -939,6 +939,27 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
+// Which kernel serves a decode step. The tile kernel (the multi-query kernel
+// with one token per sequence: P*V on the matrix cores, one workgroup per
+// (sequence, kv head) handed out by the hardware in seq_order) is the faster
+// one except when every resident workgroup would get at most one job; then
+// the persistent kernel with 8-wave workgroups splits each job more finely.
+// PA_DECODE_KERNEL=persistent|tiles forces one (the tests run both).
+bool decode_by_tiles(int num_seqs, int num_kv_heads, int group, int dtype, int head_size, bool fp8_cache) {
+  if (const char* e = getenv("PA_DECODE_KERNEL")) {
+    if (e[0] == 'p') return false;
+    if (e[0] == 't') return true;
+  }
+  const int G = next_pow2_group(group);
+  DecodeKernel k = fp8_cache ? (head_size == 128 ? pick_group_fp8<128>(G) : pick_group_fp8<64>(G))
+                             : pick_decode(dtype, head_size, G);
+  if (!k || G >= 16) return true;
+  const int64_t jobs = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * num_kv_heads;
+  const int64_t resident4 = resident_groups(reinterpret_cast<const void*>(k), 4 * kWave,
+                                            static_cast<size_t>(4) * G * head_size * sizeof(float));
+  return !(resident4 > 0 && jobs <= resident4);
+}
+
 int launch_decode(DecodeArgs args, int num_seqs, int dtype, int head_size, hipStream_t stream,
                   bool fp8_cache = false) {
   const int G = next_pow2_group(args.group);
@@ -1080,6 +1101,11 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                         num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
   if (st != PA_OK || num_seqs == 0) return st;
+  if (decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, false))
+    return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                               num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
+                               dtype, false, lse_out, seq_order, 0, nullptr, nullptr,
+                               static_cast<hipStream_t>(stream));
   DecodeArgs args{};
   args.query = query;
   args.key_cache = key_cache;
@@ -1133,6 +1159,10 @@ extern "C" int pa_decode_prefix(void* out, const void* query, const void* key_ca
                           num_heads, num_kv_heads, head_size, num_blocks, prefix_blocks, scale, dtype, part_o,
                           part_lse, s);
   if (st != PA_OK) return st;
+  if (decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, false))
+    return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                               num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
+                               dtype, false, lse_out, seq_order, prefix_blocks, part_o, part_lse, s);
   DecodeArgs args{};
   args.query = query;
   args.key_cache = key_cache;
@@ -1168,6 +1198,11 @@ extern "C" int pa_decode_fp8(void* out, const void* query, const uint8_t* key_ca
   if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
     return PA_ERR_INVALID_ARG;
+  if (decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, true))
+    return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                               num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * k_scale * kLog2e,
+                               v_scale, dtype, true, lse_out, seq_order, 0, nullptr, nullptr,
+                               static_cast<hipStream_t>(stream));
   DecodeArgs args{};
   args.query = query;
   args.key_cache = key_cache;

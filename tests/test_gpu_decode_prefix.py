@@ -17,6 +17,14 @@ def pa():
     return ensure_built()
 
 
+@pytest.fixture(autouse=True, params=["persistent", "tiles"])
+def decode_kernel(request, monkeypatch):
+    """Run every test here with each decode kernel (the library picks one by
+    batch size; both must give the oracle's answers)."""
+    monkeypatch.setenv("PA_DECODE_KERNEL", request.param)
+    return request.param
+
+
 def _prefix_decode(pa, dev, prefix_blocks, lse=True, order=None):
     S, Hq, d = dev.q.shape
     ws = torch.empty(pa.pa_decode_prefix_workspace_bytes(S, Hq, d), dtype=torch.uint8, device="cuda")

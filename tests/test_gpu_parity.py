@@ -22,6 +22,14 @@ def pa():
     return ensure_built()
 
 
+@pytest.fixture(autouse=True, params=["persistent", "tiles"])
+def decode_kernel(request, monkeypatch):
+    """Run every test here with each decode kernel (the library picks one by
+    batch size; both must give the oracle's answers)."""
+    monkeypatch.setenv("PA_DECODE_KERNEL", request.param)
+    return request.param
+
+
 def _say(msg):
     print(msg, flush=True)
 
