@@ -432,6 +432,11 @@ def main():
     roof_bytes = W.unique_kv_bytes(inp) if args.decode == "prefix" else kv_bytes
     dec_gbs = roof_bytes / (dec_avg * 1e-3) / 1e9
     traffic = stored_traffic(cfg.name, args.decode)
+    tiles = pa.pa_decode_uses_tiles(S, Hq, cfg.num_kv_heads, d, pa.PA_DTYPE_BF16 if cfg.dtype == "bf16"
+                                    else pa.PA_DTYPE_F32, fp8)
+    one = "paged_multi_query_kernel (one token per sequence)" if tiles else "paged_decode_kernel (persistent)"
+    kernel_label = {"fused": one, "split": "paged_decode_split_kernel + merge_pieces_kernel",
+                    "prefix": "paged_multi_query_kernel (shared prefix) + " + one}[args.decode]
     rec = {
         "metric": "paged decode attention effective KV GB/s (% of HBM peak) + seqs/sec, 1 GPU",
         "value": round(step_gbs, 1),
@@ -463,10 +468,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": {"fused": "paged_decode_kernel",
-                                "split": "paged_decode_split_kernel + merge_pieces_kernel",
-                                "prefix": "paged_multi_query_kernel (shared prefix) + paged_decode_kernel"
-                                }[args.decode],
+                     "kernel": kernel_label,
                      "algorithmic_bytes_per_launch": roof_bytes,
                      "kernel_source_hash": kernel_source_hash()},
         "wall_s_timed": round(wall, 4),  # includes the spin kernel queued ahead of the timed steps

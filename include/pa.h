@@ -171,8 +171,14 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapp
  * softmax is evaluated online over the streamed blocks (stanleyjacob.dev
  * "vLLM", Part IV "Stage 6: The forward pass").
  *
- * Work is cut into jobs of one (sequence, kv head) each, taken by persistent
- * workgroups (as many as fit on the GPU at once) in a fixed order.
+ * Work is cut into jobs of one (sequence, kv head) each. Two kernels serve
+ * them: the tile kernel (the multi-query kernel with one new token per
+ * sequence: one workgroup per job, handed out by the hardware in seq_order,
+ * P*V on the matrix cores) and a persistent kernel (workgroups that walk jobs
+ * in a fixed order). The persistent kernel, with 8-wave workgroups, is used
+ * when every resident workgroup would get at most one job; the tile kernel
+ * otherwise (pa_decode_uses_tiles tells which). Results differ between the two
+ * only by rounding order.
  *
  *   out               [num_seqs, num_heads, head_size], written (dtype).
  *   lse_out           optional float32 [num_seqs, num_heads]: ln sum_t exp(s_t).
@@ -282,6 +288,18 @@ int pa_multi_query(void* out, const void* query, const void* key_cache, const vo
                    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                    int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size, float scale,
                    int32_t dtype, float* lse_out, void* stream);
+
+/*
+ * pa_decode_uses_tiles - which kernel pa_decode / pa_decode_fp8 /
+ * pa_decode_prefix would run for this shape on the current device: 1 for the
+ * tile kernel (the multi-query kernel with one new token per sequence), 0 for
+ * the persistent decode kernel, -1 for invalid arguments. The choice follows
+ * the rule documented with pa_decode; the environment variable
+ * PA_DECODE_KERNEL=persistent|tiles overrides it. Queries the device's
+ * occupancy, launches nothing.
+ */
+int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t dtype, int32_t fp8_cache);
 
 /*
  * pa_decode_split_workspace_bytes - workspace pa_decode_split needs.

@@ -22,7 +22,7 @@ __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library", "prepared",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
     "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
-    "pa_decode_split_workspace_bytes", "pa_decode_split",
+    "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles",
     "pa_merge_partitions", "pa_status_string",
 ]
 
@@ -71,6 +71,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_multi_query.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f, c_i32, c_p, c_p]
     lib.pa_multi_query.restype = c_int
+    lib.pa_decode_uses_tiles.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]
+    lib.pa_decode_uses_tiles.restype = c_int
     lib.pa_multi_query_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                        c_i64, c_i32, c_f, c_f, c_f, c_i32, c_p, c_p]
     lib.pa_multi_query_fp8.restype = c_int
@@ -307,6 +309,15 @@ def pa_multi_query_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
     lib = load_library()
     _invoke(lib.pa_multi_query_fp8, "pa_multi_query_fp8", *ptrs, float(scale), float(k_scale), float(v_scale),
             _dtype_code(query), lse_ptr, _stream(stream))
+
+
+def pa_decode_uses_tiles(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int, dtype: int = PA_DTYPE_BF16,
+                         fp8_cache: bool = False) -> bool:
+    """Whether pa_decode (and the FP8 / shared-prefix variants) runs the tile kernel for this shape."""
+    r = load_library().pa_decode_uses_tiles(num_seqs, num_heads, num_kv_heads, head_size, dtype, int(fp8_cache))
+    if r < 0:
+        raise ValueError("invalid decode shape")
+    return bool(r)
 
 
 def pa_decode_prefix_workspace_bytes(num_seqs: int, num_heads: int, head_size: int) -> int:

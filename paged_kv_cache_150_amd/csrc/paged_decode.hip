@@ -1126,6 +1126,14 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
 }
 
+extern "C" int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                    int32_t dtype, int32_t fp8_cache) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
+  if (num_heads / num_kv_heads > 16 || (head_size != 64 && head_size != 128)) return -1;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return -1;
+  return decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, fp8_cache != 0) ? 1 : 0;
+}
+
 extern "C" size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size) {
   if (num_seqs < 0 || num_heads <= 0 || head_size <= 0) return 0;
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
