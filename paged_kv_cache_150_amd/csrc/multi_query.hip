@@ -318,8 +318,8 @@ template <typename T, int D, int CB, int NT, bool F8>
 __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(MultiArgs a) {
   using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kCols = 16 * NT;
-  constexpr int kRow = D + 1;  // LDS row stride in floats (spreads the 16 columns over banks)
-  __shared__ float s_acc[kMqWaves][kCols][kRow];
+  constexpr int kRow = D + 4;  // LDS row stride in floats: 16-byte rows, the 16 columns on distinct banks
+  __shared__ __attribute__((aligned(16))) float s_acc[kMqWaves][kCols][kRow];
   __shared__ float s_m[kMqWaves][kCols];
   __shared__ float s_l[kMqWaves][kCols];
 
@@ -469,10 +469,15 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
       s_m[wave][c] = st.m[p];
       s_l[wave][c] = l;
     }
+    // Columns past the tile's last (token, head) pair are never read back.
+    if (c < ncols) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
+      for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) s_acc[wave][c][(D / 16) * (4 * j + rr) + t] = st.acc[p][t][rr];
+        for (int t0 = 0; t0 < D / 16; t0 += 4)
+          *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][(D / 16) * (4 * j + rr) + t0]) =
+              f32x4_t{st.acc[p][t0][rr], st.acc[p][t0 + 1][rr], st.acc[p][t0 + 2][rr], st.acc[p][t0 + 3][rr]};
+    }
   }
   __syncthreads();
 
