@@ -243,20 +243,26 @@ def cpu_baseline_multi(mq, budget_s: float):
     base, inp = mq.cfg.base, mq.paged
     loc = mq.query_start_loc
     order = np.argsort(-mq.query_lens, kind="stable")  # prompt chunks first, then decodes
-    done, t0 = [], time.perf_counter()
-    for i in order:
-        sl = slice(int(loc[i]), int(loc[i + 1]))
-        oracle.paged_multi_query(mq.query[sl], inp.key_cache, inp.value_cache, inp.block_tables[i:i + 1],
-                                 inp.context_lens[i:i + 1], np.array([0, loc[i + 1] - loc[i]]), base.scale,
-                                 base.dtype)
-        done.append(int(i))
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    done, passes, t0 = [], 0, time.perf_counter()
+    while True:
+        for i in order:
+            sl = slice(int(loc[i]), int(loc[i + 1]))
+            oracle.paged_multi_query(mq.query[sl], inp.key_cache, inp.value_cache, inp.block_tables[i:i + 1],
+                                     inp.context_lens[i:i + 1], np.array([0, loc[i + 1] - loc[i]]), base.scale,
+                                     base.dtype)
+            done.append(int(i))
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            passes += 1
+            continue
+        break
     dt = time.perf_counter() - t0
     kv = W.algorithmic_kv_bytes(base, inp.context_lens[done])
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, {len(done)} of {base.num_seqs} sequences "
-                      f"({int(mq.query_lens[done].sum())} new tokens) in {dt:.1f} s",
+            "sample": f"fp64 numpy oracle, {passes} whole passes over the {base.num_seqs} sequences and "
+                      f"{len(done) - passes * base.num_seqs} more ({int(mq.query_lens[done].sum())} new tokens) "
+                      f"in {dt:.1f} s",
             "tokens_per_s": float(mq.query_lens[done].sum()) / dt}
 
 
