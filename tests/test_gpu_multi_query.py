@@ -148,3 +148,13 @@ def test_full_size_workloads_sampled(pa, name):
     loc = mq.query_start_loc
     rows = np.unique(np.concatenate([loc[:-1][:8], loc[1:][:8] - 1, rng.choice(mq.num_tokens, 24, replace=False)]))
     _check(mq, out, lse, rows=rows)
+
+
+def test_decode_kernel_choice(pa):
+    """The batch-256 shape runs on the tile kernel, the batch-64 shape (one job
+    per resident workgroup) on the persistent kernel, and the override wins."""
+    assert pa.pa_decode_uses_tiles(256, 32, 8, 128)
+    assert not pa.pa_decode_uses_tiles(64, 32, 8, 128)
+    assert pa.pa_decode_uses_tiles(256, 32, 8, 128, fp8_cache=True)
+    with pytest.raises(ValueError):
+        pa.pa_decode_uses_tiles(4, 30, 8, 128)
