@@ -75,6 +75,9 @@ def parse_args():
     ap.add_argument("--config", default=DEFAULT_WORKLOAD, help="workload name (see workloads.CONFIGS)")
     ap.add_argument("--decode", choices=["fused", "split", "prefix"], default="fused",
                     help="fused: pa_decode (one pass); split: pa_decode_split (partitions + LSE merge)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="fused decode: launch pa_reshape_and_cache and pa_decode separately instead of the "
+                         "one-launch pa_reshape_and_decode")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--order", choices=["longest", "natural"], default="longest",
                     help="seq_order schedule hint for pa_decode: longest context first (default) or none")
@@ -175,18 +178,25 @@ def bench_multi_query(args):
         reshape_p[i & 1]()
         attend_p[i & 1]()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Step rate from a pass with events only at its ends; per-launch durations
+    # from a second pass with events around each attention launch.
     t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     hold_gpu(stream)
     t_begin.record(stream)
     for i in range(args.steps):
         reshape_p[i & 1]()
-        ev[i][0].record(stream)
         attend_p[i & 1]()
-        ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    hold_gpu(stream)
+    for i in range(args.steps):
+        reshape_p[i & 1]()
+        ev[i][0].record(stream)
+        attend_p[i & 1]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
     att = [a.elapsed_time(b) for a, b in ev]
     att_avg = statistics.fmean(att)
     kv_bytes = W.algorithmic_kv_bytes(base, inp.context_lens)
@@ -396,8 +406,18 @@ def main():
 
     # The binding's checks run once here; the loops below repeat the bare
     # library calls (one ctypes call per launch).
-    reshape_p = [pa.prepared(reshape, *pools[k]) for k in range(2)]
-    decode_p = [pa.prepared(decode, *pools[k]) for k in range(2)]
+    # The plain decode step runs as one launch (pa_reshape_and_decode: the
+    # new tokens' write folded into the decode) unless asked otherwise.
+    one_launch = args.decode == "fused" and not fp8 and not args.separate_write
+    if one_launch:
+        def fused_step(kc, vc):
+            pa.pa_reshape_and_decode(out, q, new_k, new_v, slots, kc, vc, bt, cl, cfg.scale, seq_order=order,
+                                     stream=stream)
+        reshape_p = [lambda: None, lambda: None]
+        decode_p = [pa.prepared(fused_step, *pools[k]) for k in range(2)]
+    else:
+        reshape_p = [pa.prepared(reshape, *pools[k]) for k in range(2)]
+        decode_p = [pa.prepared(decode, *pools[k]) for k in range(2)]
 
     def step(i):
         reshape_p[i & 1]()
@@ -408,9 +428,11 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Per-launch events around the decode call inside the timed region, on the
-    # stream the kernels run on.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Two timed passes of `steps` steps each. The step rate comes from a pass
+    # with events only at its two ends (an event between kernels costs GPU
+    # time of its own); the per-launch duration of the decode call (with the
+    # write folded in, for the one-launch step) comes from a second pass with
+    # events around each launch, on the stream the kernels run on.
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -418,15 +440,21 @@ def main():
     hold_gpu(stream)
     t_begin.record(stream)
     for i in range(args.steps):
-        reshape_p[i & 1]()
-        ev[i][0].record(stream)
-        decode_p[i & 1]()
-        ev[i][1].record(stream)
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    hold_gpu(stream)
+    for i in range(args.steps):
+        reshape_p[i & 1]()
+        ev[i][0].record(stream)
+        decode_p[i & 1]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in ev]
     dec_avg = statistics.fmean(dec_ms)
     dec_med = statistics.median(dec_ms)
@@ -436,11 +464,16 @@ def main():
     # The shared-prefix decode must read each distinct slot once: its
     # roofline is priced on the unique bytes.
     roof_bytes = W.unique_kv_bytes(inp) if args.decode == "prefix" else kv_bytes
+    if one_launch:
+        # The launch also reads the new tokens' K/V and writes them to their slots.
+        roof_bytes += 4 * int(np.count_nonzero(inp.slot_mapping >= 0)) * cfg.num_kv_heads * d * cfg.kv_elem_bytes
     dec_gbs = roof_bytes / (dec_avg * 1e-3) / 1e9
-    traffic = stored_traffic(cfg.name, args.decode)
-    tiles = pa.pa_decode_uses_tiles(S, Hq, cfg.num_kv_heads, d, pa.PA_DTYPE_BF16 if cfg.dtype == "bf16"
-                                    else pa.PA_DTYPE_F32, fp8)
+    traffic = stored_traffic(cfg.name, args.decode + ("_separate" if args.separate_write else ""))
+    tiles = one_launch or pa.pa_decode_uses_tiles(S, Hq, cfg.num_kv_heads, d, pa.PA_DTYPE_BF16
+                                                  if cfg.dtype == "bf16" else pa.PA_DTYPE_F32, fp8)
     one = "paged_multi_query_kernel (one token per sequence)" if tiles else "paged_decode_kernel (persistent)"
+    if one_launch:
+        one += " with the new-token write"
     kernel_label = {"fused": one, "split": "paged_decode_split_kernel + merge_pieces_kernel",
                     "prefix": "paged_multi_query_kernel (shared prefix) + " + one}[args.decode]
     rec = {
@@ -464,6 +497,7 @@ def main():
                    "prefix_blocks": inp.shared_prefix_blocks if args.decode == "prefix" else None,
                    "kv_cache": cfg.cache_dtype,
                    "step": ("pa_reshape_and_cache_fp8 + pa_decode_fp8" if fp8 else
+                            "pa_reshape_and_decode (one launch)" if one_launch else
                             "pa_reshape_and_cache + " + {"fused": "pa_decode", "split": "pa_decode_split",
                                                          "prefix": "pa_decode_prefix"}[args.decode])},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),

@@ -253,6 +253,32 @@ int pa_decode_prefix(void* out, const void* query, const void* key_cache, const 
                      void* stream);
 
 /*
+ * pa_reshape_and_decode - pa_reshape_and_cache of one decode step's new
+ * tokens followed by pa_decode, in one launch.
+ *
+ * Token i is sequence i's new token: its K/V (key, value [num_seqs, H_kv,
+ * head_size]) are written to slot_mapping[i] and the step's attention is
+ * computed as pa_decode computes it (the forward step of llm-stack-book 7.3,
+ * "The forward step in detail": scatter the new K/V, then attend). Each
+ * workgroup writes its sequence's slice for its kv head with the very lanes
+ * that later read that slot back, so the write needs no extra pass or fence.
+ *
+ *   slot_mapping      int64 [num_seqs]: the slot of position context_lens[i]-1
+ *                     of sequence i (the usual decode step), or negative for
+ *                     no write. A slot elsewhere is still written, but its
+ *                     order against other sequences' reads is unspecified.
+ * Runs on the tile kernel for every batch size. Other arguments as pa_decode
+ * and pa_reshape_and_cache (same dtype for key, value, query, out and caches).
+ * Returns PA_OK or an error status.
+ */
+int pa_reshape_and_decode(void* out, const void* query, const void* key, const void* value,
+                          const int64_t* slot_mapping, void* key_cache, void* value_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                          int64_t num_blocks, int32_t block_size, float scale, int32_t dtype, float* lse_out,
+                          const int32_t* seq_order, void* stream);
+
+/*
  * pa_multi_query - paged attention for several new tokens per sequence.
  *
  * One step may give a sequence more than one new token: a slice of a long

@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library", "prepared",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
+    "pa_reshape_and_decode",
     "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
     "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles",
     "pa_merge_partitions", "pa_status_string",
@@ -71,6 +72,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_multi_query.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_f, c_i32, c_p, c_p]
     lib.pa_multi_query.restype = c_int
+    lib.pa_reshape_and_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32,
+                                          c_i32, c_i64, c_i32, c_f, c_i32, c_p, c_p, c_p]
+    lib.pa_reshape_and_decode.restype = c_int
     lib.pa_decode_uses_tiles.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_uses_tiles.restype = c_int
     lib.pa_multi_query_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -342,6 +346,32 @@ def pa_decode_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Te
     _invoke(lib.pa_decode_prefix, "pa_decode_prefix", p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"],
             S, Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), int(prefix_blocks), ws,
             workspace.numel() * workspace.element_size(), p["lse"], order_ptr, _stream(stream))
+
+
+def pa_reshape_and_decode(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                          slot_mapping: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                          lse_out: torch.Tensor | None = None, seq_order: torch.Tensor | None = None,
+                          stream=None) -> None:
+    """One decode step in one launch: write sequence i's new key[i]/value[i] to
+    slot_mapping[i] (the slot of its last position), then pa_decode."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out)
+    if key.shape != (S, Hkv, d) or value.shape != (S, Hkv, d) or key.dtype != key_cache.dtype \
+            or value.dtype != key_cache.dtype:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_size] in the cache dtype")
+    if slot_mapping.shape != (S,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.shape != (S,):
+            raise ValueError("seq_order must be [num_seqs]")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
+    lib = load_library()
+    _invoke(lib.pa_reshape_and_decode, "pa_reshape_and_decode", p["out"], p["query"], _dev(key, "key"),
+            _dev(value, "value"), _dev(slot_mapping, "slot_mapping", torch.int64, 1), p["kc"], p["vc"], p["bt"],
+            MB, p["cl"], S, Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), p["lse"], order_ptr,
+            _stream(stream))
 
 
 def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

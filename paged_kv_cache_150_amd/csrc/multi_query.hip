@@ -86,6 +86,12 @@ struct MultiArgs {
   int32_t skip_blocks;
   const float* prefix_o;    // [num_seqs, num_heads, D]
   const float* prefix_lse;  // [num_seqs, num_heads]
+  // Decode mode with the new tokens' write folded in: sequence i's new K/V
+  // (new_key/new_value row i, [num_seqs, H_kv, D]) go to slot_mapping[i]
+  // first. Null: the caches already hold them.
+  const void* new_key;
+  const void* new_value;
+  const int64_t* slot_mapping;
 };
 
 // Tile slots: sequence i owns slots [B_i, B_{i+1}) with
@@ -414,6 +420,57 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
   auto is_mask = [&](int i) { return wave + i * kMqWaves >= mask_from; };
 
+  // Decode with the new token's write folded in: every lane loads its pieces
+  // of the new K/V row up front (no dependence on anything else); the wave
+  // whose last chunk holds position n - 1 swaps them into that chunk's
+  // registers before using it, and stores them to the slot once its chunks
+  // are done. Nothing in this launch reads the slot from memory after the
+  // store, so no ordering is needed.
+  // (Decode mode always runs 16-column tiles; the 32-column instantiations
+  // leave this out.)
+  constexpr bool kFusedWrite = !F8 && NT == 1;
+  u32x4_t kn[S::kKSeg];
+  uint32_t vn[S::kVDw];
+  bool own_new = false;
+  int new_ib = 0, new_r0 = 0;
+  int64_t new_slot = -1;
+  if constexpr (kFusedWrite) {
+    if (a.slot_mapping != nullptr && key_end > 0) {
+      new_slot = a.slot_mapping[seq];
+      const int pos = key_end - 1;
+      if (new_slot >= 0 && new_slot < a.num_blocks * kBlockTokens) {
+        const int64_t src_off = (static_cast<int64_t>(seq) * a.num_kv_heads + kvh) * D * S::kElemBytes;
+        const gchar_t* ksrc = uniform_ptr(static_cast<const char*>(a.new_key) + src_off);
+        const gchar_t* vsrc = uniform_ptr(static_cast<const char*>(a.new_value) + src_off);
+#pragma unroll
+        for (int sg = 0; sg < S::kKSeg; ++sg) kn[sg] = gload16(ksrc + sg * 64 + (lane >> 4) * 16);
+        load_dwords<S::kVDw>(vn, vsrc + (lane & 15) * (S::kVDw * 4));
+        const int c_last = (pos / kBlockTokens) / CB;
+        own_new = c_last % kMqWaves == wave;
+        new_ib = pos / kBlockTokens - c_last * CB;
+        new_r0 = pos % kBlockTokens;
+      }
+    }
+  }
+  // K row new_r0 of block new_ib lives in lanes with lane % 16 == new_r0; V row
+  // new_r0 in lanes with lane / 16 == new_r0 / 4, register row new_r0 % 4.
+  auto patch_new = [&](Chunk<T, D, 16, CB, F8>& f) {
+    const bool krow = (lane & 15) == new_r0;
+    const bool vrow = (lane >> 4) == new_r0 / 4;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      if (i != new_ib) continue;
+#pragma unroll
+      for (int sg = 0; sg < S::kKSeg; ++sg) f.k[i][sg] = krow ? kn[sg] : f.k[i][sg];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r != new_r0 % 4) continue;
+#pragma unroll
+        for (int w = 0; w < S::kVDw; ++w) f.v[i][r][w] = vrow ? vn[w] : f.v[i][r][w];
+      }
+    }
+  };
+
   u32x4_t q[NT][S::kQSeg];
   load_query_cols<T, D, CB, NT, F8>(a.query, q0 + tok0, a.num_heads, kvh * g, g, ncols, lane, q);
 
@@ -452,9 +509,32 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
                                head_off, lane);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      if constexpr (kFusedWrite) {
+        if (own_new) patch_new(fb);
+      }
       mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
     } else {
+      if constexpr (kFusedWrite) {
+        if (own_new) patch_new(fa);
+      }
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+    }
+  }
+  if (kFusedWrite && own_new) {
+    // The new token's slice to its slot (the lanes that hold it).
+    typedef __attribute__((address_space(1))) char gwchar_t;
+    const int64_t dst_off = (new_slot / kBlockTokens) * blk_stride + (new_slot % kBlockTokens) * tok_stride + head_off;
+    gwchar_t* kdst = reinterpret_cast<gwchar_t*>(reinterpret_cast<uintptr_t>(kc + dst_off));
+    gwchar_t* vdst = reinterpret_cast<gwchar_t*>(reinterpret_cast<uintptr_t>(vc + dst_off));
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int sg = 0; sg < S::kKSeg; ++sg)
+        *reinterpret_cast<__attribute__((address_space(1))) u32x4_t*>(kdst + sg * 64 + (lane >> 4) * 16) = kn[sg];
+    }
+    if ((lane >> 4) == 0) {
+#pragma unroll
+      for (int w = 0; w < S::kVDw; ++w)
+        reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(vdst + (lane & 15) * (S::kVDw * 4))[w] = vn[w];
     }
   }
 
@@ -595,7 +675,9 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
                  const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                  int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, float scale_log2, float v_scale,
                  int32_t dtype, bool fp8_cache, float* lse_out, const int32_t* seq_order, hipStream_t stream,
-                 int32_t skip_blocks = 0, const float* prefix_o = nullptr, const float* prefix_lse = nullptr) {
+                 int32_t skip_blocks = 0, const float* prefix_o = nullptr, const float* prefix_lse = nullptr,
+                 const void* new_key = nullptr, const void* new_value = nullptr,
+                 const int64_t* slot_mapping = nullptr) {
   const int g = num_heads / num_kv_heads;
   int NT = query_start_loc == nullptr ? 1 : pick_tiles(num_tokens, num_seqs, g);
   NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
@@ -628,6 +710,9 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
   a.skip_blocks = skip_blocks;
   a.prefix_o = prefix_o;
   a.prefix_lse = prefix_lse;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.slot_mapping = slot_mapping;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -712,4 +797,22 @@ extern "C" int pa_multi_query_fp8(void* out, const void* query, const uint8_t* k
                       query_start_loc, num_seqs, num_tokens, num_heads, num_kv_heads, head_size, num_blocks,
                       scale * k_scale * kLog2e, v_scale, dtype, true, lse_out, nullptr,
                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pa_reshape_and_decode(void* out, const void* query, const void* key, const void* value,
+                                     const int64_t* slot_mapping, void* key_cache, void* value_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
+                                     float scale, int32_t dtype, float* lse_out, const int32_t* seq_order,
+                                     void* stream) {
+  int st = check_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, scale, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!key || !value || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned16_mq(key) || !aligned16_mq(value)) return PA_ERR_INVALID_ARG;
+  return launch_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, nullptr,
+                      num_seqs, num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
+                      dtype, false, lse_out, seq_order, static_cast<hipStream_t>(stream), 0, nullptr, nullptr, key,
+                      value, slot_mapping);
 }
