@@ -281,15 +281,6 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
 }
 
 
-// Workgroup -> (tile slot, kv head): consecutive workgroups go to the 8 XCDs
-// in turn; the kv heads of one slot share an XCD.
-__device__ __forceinline__ void wg_to_slot_head(int id, int num_kv_heads, int& slot, int& kvh) {
-  const int xcd = id & 7;
-  const int k = id >> 3;
-  kvh = k % num_kv_heads;
-  slot = (k / num_kv_heads) * 8 + xcd;
-}
-
 // Query fragments of a tile's columns: column c = 16 p + (lane % 16) is new
 // token c / g (row `row0` + c / g) and head head0 + c % g; columns past the
 // tile's `ncols` get zeros. Same d order as the K operand of qk_chunk.
@@ -334,7 +325,7 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   const int g = a.group;
 
   int slot, kvh;
-  wg_to_slot_head(blockIdx.x, a.num_kv_heads, slot, kvh);
+  slot_and_head(blockIdx.x, a.num_kv_heads, slot, kvh);
   if (slot >= a.num_slots) return;
   const int max_tokens = a.max_blocks * kBlockTokens;
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > max_tokens ? max_tokens : v); };

@@ -150,4 +150,24 @@ __device__ __forceinline__ void load_dwords(uint32_t (&dst)[NDW], const gchar_t*
   }
 }
 
+// Workgroup id -> (slot, kv head) for grids of one workgroup per (slot, kv
+// head). Consecutive ids go to the 8 XCDs in turn, and the kv heads of one
+// slot share an XCD (ids x, x+8, x+16, ...), so each XCD reads whole token
+// rows. Within an XCD the dispatcher deals workgroups to its 4 shader engines
+// in turn and strictly in order. With a fixed head per dispatch position each
+// engine would always get the same heads, and heads do not stream at the same
+// rate (their byte offset in the token row decides where their rows fall in
+// the memory system; on the Llama-3-8B layout two of the 8 heads run 15-40%
+// slower). The engine holding the slow heads would then stall the in-order
+// dispatch of its whole XCD, so the heads of consecutive slots are rotated
+// and every engine sees every head.
+__device__ __forceinline__ void slot_and_head(int id, int num_kv_heads, int& slot, int& kvh) {
+  const int xcd = id & 7;
+  const int k = id >> 3;
+  const int group = k / num_kv_heads;
+  const int span = num_kv_heads >= 4 ? 1 : 4 / num_kv_heads;
+  kvh = (k - group * num_kv_heads + group / span) % num_kv_heads;
+  slot = group * 8 + xcd;
+}
+
 }  // namespace pa

@@ -70,17 +70,6 @@ struct DecodeArgs {
   const float* prefix_lse;  // [num_seqs, num_heads]
 };
 
-// Workgroup -> (sequence, kv head). Consecutive workgroups are dispatched to
-// the 8 XCDs in turn; the kv heads of one sequence are placed on the same XCD
-// (workgroups x, x+8, x+16, ...), so each XCD reads whole 2 KiB token rows and
-// all of its L2 channels, and consecutive XCDs take consecutive sequences.
-__device__ __forceinline__ void wg_to_seq_head(int id, int num_kv_heads, int& seq, int& kvh) {
-  const int xcd = id & 7;
-  const int k = id >> 3;
-  kvh = k % num_kv_heads;
-  seq = (k / num_kv_heads) * 8 + xcd;
-}
-
 template <typename T, int D, int G, int CB>
 struct WaveState {
   using S = DecodeShape<T, D, G, CB>;
@@ -203,7 +192,7 @@ __device__ __forceinline__ void load_query(const void* query, int seq, int num_h
 }
 
 // One decode job is one (sequence, kv head); job ids follow the XCD-aware
-// order of wg_to_seq_head (id % 8 names the XCD meant to run it, and all kv
+// order of slot_and_head (id % 8 names the XCD meant to run it, and all kv
 // heads of a sequence share it), and ids past the last sequence are padding.
 struct DecodeJob {
   int seq;  // -1 for a padding id
@@ -214,7 +203,7 @@ struct DecodeJob {
 __device__ __forceinline__ DecodeJob decode_job(const DecodeArgs& a, int id) {
   DecodeJob j;
   int seq, kvh;
-  wg_to_seq_head(id, a.num_kv_heads, seq, kvh);
+  slot_and_head(id, a.num_kv_heads, seq, kvh);
   j.kvh = kvh;
   j.seq = -1;
   j.n = 0;
