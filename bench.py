@@ -116,6 +116,17 @@ def bench_copy_blocks(args):
     for i in range(args.warmup):
         copy_p[i & 1]()
     torch.cuda.synchronize()
+    # One launch per step: the pass timed at its two ends gives the average
+    # launch duration; a second pass with events around each launch is kept
+    # as a cross-check (those events cost GPU time of their own).
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_gpu(stream)
+    t_begin.record(stream)
+    for i in range(args.steps):
+        copy_p[i & 1]()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_begin.elapsed_time(t_end) / args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     hold_gpu(stream)
     for i in range(args.steps):
@@ -123,7 +134,7 @@ def bench_copy_blocks(args):
         copy_p[i & 1]()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_events = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     block_bytes = cfg.block_size * cfg.num_kv_heads * cfg.head_size * (2 if cfg.dtype == "bf16" else 4)
     moved = 2 * 2 * args.pairs * block_bytes  # K and V, read + write
     gbs = moved / (ms * 1e-3) / 1e9
@@ -132,6 +143,7 @@ def bench_copy_blocks(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "pairs": args.pairs, "block_bytes": block_bytes},
+        "launch_ms_events": round(ms_events, 5),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(cfg.name, f"pairs{args.pairs}", "copy_blocks"),
@@ -467,7 +479,13 @@ def main():
     if one_launch:
         # The launch also reads the new tokens' K/V and writes them to their slots.
         roof_bytes += 4 * int(np.count_nonzero(inp.slot_mapping >= 0)) * cfg.num_kv_heads * d * cfg.kv_elem_bytes
-    dec_gbs = roof_bytes / (dec_avg * 1e-3) / 1e9
+    # With one launch per step the first pass, timed at its two ends over
+    # launches queued back to back on the kernel's stream, gives the kernel's
+    # average launch duration directly (any gap between launches counts
+    # against the kernel); the per-launch events add a cost of their own and
+    # are kept as a cross-check.
+    launch_ms = ms_per_step if one_launch else dec_avg
+    dec_gbs = roof_bytes / (launch_ms * 1e-3) / 1e9
     traffic = stored_traffic(cfg.name, args.decode + ("_separate" if args.separate_write else ""))
     tiles = one_launch or pa.pa_decode_uses_tiles(S, Hq, cfg.num_kv_heads, d, pa.PA_DTYPE_BF16
                                                   if cfg.dtype == "bf16" else pa.PA_DTYPE_F32, fp8)
@@ -505,6 +523,9 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "decode_ms_avg": round(dec_avg, 5),
         "decode_ms_median": round(dec_med, 5),
+        "launch_ms": round(launch_ms, 5),
+        "launch_timing": ("timed region / steps (one launch per step)" if one_launch
+                          else "HIP events around each launch"),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
