@@ -492,7 +492,10 @@ def main():
     one = "paged_multi_query_kernel (one token per sequence)" if tiles else "paged_decode_kernel (persistent)"
     if one_launch:
         one += " with the new-token write"
-    kernel_label = {"fused": one, "split": "paged_decode_split_kernel + merge_pieces_kernel",
+    split_label = "paged_decode_split_kernel + merge_pieces_kernel"
+    if args.decode == "split" and pa.pa_decode_split_part_tokens(S, Hq, cfg.num_kv_heads, inp.max_context_len, P):
+        split_label = "paged_multi_query_kernel (context partitions) + merge_parts_kernel"
+    kernel_label = {"fused": one, "split": split_label,
                     "prefix": "paged_multi_query_kernel (shared prefix) + " + one}[args.decode]
     rec = {
         "metric": "paged decode attention effective KV GB/s (% of HBM peak) + seqs/sec, 1 GPU",

@@ -342,38 +342,51 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
 
 /*
  * pa_decode_split - the same result as pa_decode, computed over context
- * pieces spread evenly over the whole GPU and merged exactly.
+ * pieces and merged exactly with the log-sum-exp rule of pa_merge_partitions.
+ * The merge rests on the softmax normaliser identity the pages lean on for
+ * streaming (stanleyjacob.dev "vLLM", Part V "The attention backend dispatch
+ * layer": tiling plus online softmax). The work is cut one of two ways
+ * (pa_decode_split_part_tokens says which):
  *
- * The kv heads are taken in groups of up to 8 (one persistent workgroup has
- * one wave per kv head of its group, all walking the same blocks). Per head
- * group, the blocks of all sequences are laid end to end (sequence i has
- * nb_i = ceil(n_i / block_size) blocks; total_blocks T = groups * sum nb_i,
- * group-major) and cut into num_ranges R equal contiguous ranges, one per
- * workgroup, so long and short contexts share the GPU evenly: range r is
- * blocks [r*T/R, (r+1)*T/R). R is at most the number of resident workgroups
- * and at most T / (partition_size / block_size), so every range spans at least
- * partition_size tokens. The piece of (sequence i, head group) inside range r
- * gets slot r - r0 (r0 the range of the sequence's first block); its
- * normalised output and log-sum-exp go to o_p / lse_p of the query heads of
- * that group. A sequence that one range covers whole is written straight to
- * `out`; a second kernel on the same stream merges the pieces of the others
- * with the log-sum-exp rule of pa_merge_partitions. The merge rests on the
- * softmax normaliser identity the pages lean on for streaming
- * (stanleyjacob.dev "vLLM", Part V "The attention backend dispatch layer":
- * tiling plus online softmax); this way of cutting the work is this library's.
+ * Partitions (group H_q / H_kv <= 16): with P' = k * P tokens
+ * (pa_decode_split_part_tokens: k >= 1 grows with the grid the call would
+ * launch, so every workgroup streams long enough) and C = ceil(max_context_len
+ * / P) * P, partition p of sequence i is its keys [p*P', min((p+1)*P', n_i, C)),
+ * p < ceil(C / P'). One workgroup of the multi-query kernel per (sequence,
+ * partition, kv head), handed out by the hardware dispatcher, writes the
+ * partition's normalised output and log-sum-exp for the group's query heads
+ * to slot p of o_p / lse_p; partitions past n_i write nothing. A second kernel
+ * on the same stream merges the slots of every (sequence, head) that hold a
+ * partition into out. The header is not written.
+ *
+ * Pieces (larger groups, or PA_SPLIT_KERNEL=pieces): the kv heads are taken
+ * in groups of up to 8 (one persistent workgroup has one wave per kv head of
+ * its group, all walking the same blocks). Per head group, the blocks of all
+ * sequences are laid end to end (sequence i has nb_i = ceil(n_i / block_size)
+ * blocks; total_blocks T = groups * sum nb_i, group-major) and cut into
+ * num_ranges R equal contiguous ranges, one per workgroup, so long and short
+ * contexts share the GPU evenly: range r is blocks [r*T/R, (r+1)*T/R). R is at
+ * most the number of resident workgroups and at most T / (partition_size /
+ * block_size), so every range spans at least partition_size tokens. The piece
+ * of (sequence i, head group) inside range r gets slot r - r0 (r0 the range of
+ * the sequence's first block); its normalised output and log-sum-exp go to
+ * o_p / lse_p of the query heads of that group. A sequence that one range
+ * covers whole is written straight to `out`; a second kernel merges the
+ * pieces of the others. The header describes the cut.
  *
  *   max_context_len   host-side upper bound of context_lens (sizes the
- *                     workspace without reading the lengths back). Positions
- *                     past ceil(max_context_len / P) * P are ignored, so it
- *                     must be >= every length.
- *   partition_size    P: multiple of block_size, > 0; the shortest piece.
+ *                     workspace and the grid without reading the lengths
+ *                     back). Positions past ceil(max_context_len / P) * P are
+ *                     ignored, so it must be >= every length.
+ *   partition_size    P: multiple of block_size, > 0.
  *   workspace         device memory of at least
  *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
- *                     aligned, owned by the caller. Slots of sequences
- *                     that are not cut are left untouched.
+ *                     aligned, owned by the caller. Slots that the cut does not
+ *                     use are left untouched.
  *   lse_out           optional float32 [num_seqs, num_heads]; NULL to skip.
- * num_seqs + 1 block counts must fit in 64 KiB of LDS (num_seqs <= 16383).
- * Other arguments as pa_decode. Returns PA_OK or an error status.
+ * The pieces cut keeps num_seqs + 1 block counts in 64 KiB of LDS
+ * (num_seqs <= 16383). Other arguments as pa_decode. Returns PA_OK or an
+ * error status.
  */
 int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -382,6 +395,18 @@ int pa_decode_split(void* out, const void* query, const void* key_cache, const v
                     int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
                     int32_t partition_size, void* workspace, size_t workspace_bytes,
                     float* lse_out, void* stream);
+
+/*
+ * pa_decode_split_part_tokens - the cut pa_decode_split makes for these
+ * arguments on the current device: the partition length P' (a multiple of
+ * partition_size) of the partition cut, 0 for the pieces cut, -1 for invalid
+ * arguments. PA_SPLIT_KERNEL=pieces|tiles overrides the choice of cut (tiles
+ * need H_q / H_kv <= 16) and PA_SPLIT_PART_FACTOR=k the factor P' / P (capped
+ * at ceil(max_context_len / P)). Queries the device's CU count, launches
+ * nothing.
+ */
+int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t max_context_len, int32_t partition_size);
 
 /*
  * pa_merge_partitions - exact log-sum-exp merge of partial attention results.

@@ -23,7 +23,7 @@ __all__ = [
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
     "pa_reshape_and_decode",
     "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
-    "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles",
+    "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles", "pa_decode_split_part_tokens",
     "pa_merge_partitions", "pa_status_string",
 ]
 
@@ -77,6 +77,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_reshape_and_decode.restype = c_int
     lib.pa_decode_uses_tiles.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_uses_tiles.restype = c_int
+    lib.pa_decode_split_part_tokens.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
+    lib.pa_decode_split_part_tokens.restype = c_i32
     lib.pa_multi_query_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                        c_i64, c_i32, c_f, c_f, c_f, c_i32, c_p, c_p]
     lib.pa_multi_query_fp8.restype = c_int
@@ -322,6 +324,16 @@ def pa_decode_uses_tiles(num_seqs: int, num_heads: int, num_kv_heads: int, head_
     if r < 0:
         raise ValueError("invalid decode shape")
     return bool(r)
+
+
+def pa_decode_split_part_tokens(num_seqs: int, num_heads: int, num_kv_heads: int, max_context_len: int,
+                                partition_size: int) -> int:
+    """Partition length of pa_decode_split's partition cut for these arguments, or 0 for its pieces cut."""
+    r = load_library().pa_decode_split_part_tokens(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                                   partition_size)
+    if r < 0:
+        raise ValueError("invalid split arguments")
+    return int(r)
 
 
 def pa_decode_prefix_workspace_bytes(num_seqs: int, num_heads: int, head_size: int) -> int:

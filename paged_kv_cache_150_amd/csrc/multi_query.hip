@@ -28,8 +28,8 @@
 //    probabilities. Lane l ends up owning output elements
 //    d in [(l/16)*D/4, (l/16+1)*D/4) of column l % 16.
 //  * Probabilities enter the bf16 MFMA rounded to bf16 (relative error at
-//    most 2^-9 per weight); the normaliser and the log-sum-exp use the fp32
-//    values. fp32 caches use the fp32 MFMA and keep fp32 probabilities.
+//    most 2^-8 per weight, so an output moves by at most 2^-8 * max |v|);
+//    the normaliser and the log-sum-exp use the fp32 values. fp32 caches use the fp32 MFMA and keep fp32 probabilities.
 //  * Online softmax in base 2, per column, with a reference point that moves
 //    only when a chunk's maximum exceeds it by more than 2^8 in weight; a
 //    column with no visible key yet keeps weight 0.
@@ -92,6 +92,18 @@ struct MultiArgs {
   const void* new_key;
   const void* new_value;
   const int64_t* slot_mapping;
+  // Decode mode cut into context partitions (part_blocks > 0): slot
+  // p * num_seqs + j attends the keys [p * P, min((p + 1) * P, n)) of sequence
+  // i = (j - p) mod num_seqs (P = 16 * part_blocks) and writes the normalised
+  // float32 output and the log-sum-exp of each query head h to part_o /
+  // part_lse row (i * num_heads + h) * parts_stride + p. Partitions past the
+  // context end write nothing. First partitions (full ones) are dispatched
+  // first; the rotation by p moves each sequence to another XCD from one
+  // partition to the next, so every XCD gets a share of every context.
+  int32_t part_blocks;
+  int32_t num_parts;
+  int32_t parts_stride;
+  int32_t part_cap;  // keys at or past this position are ignored
 };
 
 // Tile slots: sequence i owns slots [B_i, B_{i+1}) with
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > max_tokens ? max_tokens : v); };
   // The tile reads keys [16 * blk_begin, key_end); column p of this lane sees
   // keys below lim[p]; min_lim is the smallest limit of the tile's columns.
-  int seq, q0, tok0, ntok, key_end, min_lim, blk_begin = 0;
+  int seq, q0, tok0, ntok, key_end, min_lim, blk_begin = 0, part = -1;
   int lim[NT];
   if (a.prefix_keys > 0) {
     // Shared-prefix pass: tile `slot` of the queries, all over row 0's prefix.
@@ -356,14 +368,23 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
     int q1, r;
     if (a.query_start_loc == nullptr) {
       // One new token per sequence (decode): slot i is sequence i (or
-      // seq_order[i], clamped), query row = sequence.
-      if (slot >= a.num_seqs) return;
-      seq = slot;
-      if (a.seq_order != nullptr) {
-        const uint32_t o = static_cast<uint32_t>(a.seq_order[slot]);
-        seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
+      // seq_order[i], clamped), query row = sequence; with partitions, slot
+      // p * num_seqs + j is partition p of sequence (j - p) mod num_seqs.
+      if (a.part_blocks > 0) {
+        part = slot / a.num_seqs;
+        const int j = slot - part * a.num_seqs;
+        const int rot = part % a.num_seqs;
+        seq = j >= rot ? j - rot : j - rot + a.num_seqs;
+        blk_begin = part * a.part_blocks;
+      } else {
+        if (slot >= a.num_seqs) return;
+        seq = slot;
+        if (a.seq_order != nullptr) {
+          const uint32_t o = static_cast<uint32_t>(a.seq_order[slot]);
+          seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
+        }
+        blk_begin = a.skip_blocks;
       }
-      blk_begin = a.skip_blocks;
       q0 = seq;
       q1 = seq + 1;
       r = 0;
@@ -390,6 +411,15 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
     for (int p = 0; p < NT; ++p) {
       const int c = 16 * p + (lane & 15);
       lim[p] = c < ntok * g ? pos0 + c / g + 1 : 0;
+    }
+    if (part >= 0) {
+      // The partition's keys are all visible to the sequence's one query.
+      key_end = min(key_end, a.part_cap);
+      if (key_end <= blk_begin * kBlockTokens) return;
+      key_end = min(key_end, (blk_begin + a.part_blocks) * kBlockTokens);
+      min_lim = key_end;
+#pragma unroll
+      for (int p = 0; p < NT; ++p) lim[p] = lim[p] > 0 ? key_end : 0;
     }
   }
   const int ncols = ntok * g;
@@ -582,8 +612,9 @@ __global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(
     }
     const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
     if (a.part_o != nullptr) {
-      a.part_o[row * D + d] = o;
-      if (d == 0) a.part_lse[row] = lse;
+      const int64_t orow = part >= 0 ? row * a.parts_stride + part : row;
+      a.part_o[orow * D + d] = o;
+      if (d == 0) a.part_lse[orow] = lse;
     } else {
       store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
       if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
@@ -742,6 +773,45 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
   a.prefix_keys = prefix_blocks * kBlockTokens;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa::launch_split_tiles(const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                           int64_t num_blocks, float scale, int32_t dtype, int32_t part_blocks, int32_t num_parts,
+                           int32_t part_cap, int32_t parts_stride, float* o_parts, float* lse_parts,
+                           hipStream_t stream) {
+  const int g = num_heads / num_kv_heads;
+  if (g > 16 || part_blocks <= 0 || num_parts <= 0 || parts_stride < num_parts) return PA_ERR_UNSUPPORTED;
+  MultiKernel k = pick_multi(dtype, head_size, 1, false);
+  MultiArgs a{};
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = g;
+  a.tile_tokens = 16 / g;
+  const int64_t slots = static_cast<int64_t>(num_seqs) * num_parts;
+  const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
+  if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  a.num_slots = static_cast<int32_t>(slots);
+  a.scale_log2 = scale * kLog2e;
+  a.v_scale = 1.0f;
+  a.part_o = o_parts;
+  a.part_lse = lse_parts;
+  a.part_blocks = part_blocks;
+  a.num_parts = num_parts;
+  a.parts_stride = parts_stride;
+  a.part_cap = part_cap;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -31,4 +31,18 @@ int launch_decode_multi(void* out, const void* query, const void* key_cache, con
                         float* lse_out, const int32_t* seq_order, int32_t skip_blocks, const float* prefix_o,
                         const float* prefix_lse, hipStream_t stream);
 
+// Context partitions of a one-token-per-sequence decode on the multi-query
+// kernel: partition p of sequence i (keys [p * P, min((p + 1) * P, n_i,
+// part_cap)), P = 16 * part_blocks, p < num_parts) writes the normalised
+// float32 output and log-sum-exp of each query head h to o_parts / lse_parts
+// row (i * num_heads + h) * parts_stride + p; partitions past a context's end
+// write nothing. g = num_heads / num_kv_heads must be at most 16. Arguments are
+// validated by the caller.
+int launch_split_tiles(const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                       int64_t num_blocks, float scale, int32_t dtype, int32_t part_blocks, int32_t num_parts,
+                       int32_t part_cap, int32_t parts_stride, float* o_parts, float* lse_parts,
+                       hipStream_t stream);
+
 }  // namespace pa

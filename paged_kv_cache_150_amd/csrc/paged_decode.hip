@@ -722,19 +722,27 @@ __global__ __launch_bounds__(64 * kMaxHeadsPerGroup, 1) void paged_decode_split_
   }
 }
 
-// Log-sum-exp merge of np partials of one (sequence, head) row by one wave:
-// lane p holds lse_p (lanes stride over p when np > 64), the weights
-// 2^(lse_p - M) are broadcast through LDS and every lane accumulates its
-// head_size/64 output elements with eight partial loads in flight.
-// Partitions at -inf get weight 0 and their o_p is never read.
+// Log-sum-exp merge of np partials of one (sequence, head) row by one wave.
+// Lane j owns output elements [j*D/64, (j+1)*D/64); lane p holds lse_p (lanes
+// stride over p when np > 64). The first 32 partials are requested together
+// with the lse values, before the maximum is known, and later ones 32 at a
+// time, so a row costs one or two memory round trips instead of one per
+// eight partials. A partial whose lse_p is -inf has weight 0 and its o_p (which
+// may hold anything) does not enter the sum.
 template <typename T, int D>
 __device__ __forceinline__ void merge_row(T* out, float* lse_out, const float* o_row, const float* lse_row, int np,
                                           int lane) {
   constexpr int kPer = D / kWave;
-  __shared__ float s_w[4][kWave];
-  const int wv = (threadIdx.x >> 6) & 3;
-  float M = -__builtin_inff();
-  for (int p = lane; p < np; p += kWave) M = fmaxf(M, lse_row[p]);
+  constexpr int kBatch = 32;
+  const float lv0 = lane < np ? lse_row[lane] : -__builtin_inff();
+  const float* op = o_row + lane * kPer;
+  float v[kBatch][kPer];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) v[u][e] = u < np ? op[u * D + e] : 0.f;
+  float M = lv0;
+  for (int p = lane + kWave; p < np; p += kWave) M = fmaxf(M, lse_row[p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
   float acc[kPer];
@@ -743,37 +751,29 @@ __device__ __forceinline__ void merge_row(T* out, float* lse_out, const float* o
   float L = 0.f;
   if (M != -__builtin_inff()) {
     for (int p0 = 0; p0 < np; p0 += kWave) {
-      const int p = p0 + lane;
-      const float lv = p < np ? lse_row[p] : -__builtin_inff();
+      const float lv = p0 == 0 ? lv0 : (p0 + lane < np ? lse_row[p0 + lane] : -__builtin_inff());
       const float w = lv == -__builtin_inff() ? 0.f : fast_exp2((lv - M) * kLog2e);
       float wsum = w;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) wsum += xor_shfl(wsum, off);
       L += wsum;
-      s_w[wv][lane] = w;
-      __builtin_amdgcn_wave_barrier();
       const int cnt = min(kWave, np - p0);
-      const float* op = o_row + static_cast<int64_t>(p0) * D + lane * kPer;
-      int i = 0;
-      for (; i + 8 <= cnt; i += 8) {
-        float v[8][kPer];
+      for (int i = 0; i < cnt; i += kBatch) {
+        if (p0 != 0 || i != 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+          for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) v[u][e] = s_w[wv][i + u] > 0.f ? op[(i + u) * D + e] : 0.f;
+            for (int e = 0; e < kPer; ++e) v[u][e] = i + u < cnt ? op[(p0 + i + u) * D + e] : 0.f;
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < kBatch; ++u) {
+          const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i + u));
+          if (wu > 0.f) {
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) acc[e] = fmaf(s_w[wv][i + u], v[u][e], acc[e]);
-      }
-      for (; i < cnt; ++i) {
-        const float wi = s_w[wv][i];
-        if (wi > 0.f) {
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) acc[e] = fmaf(wi, op[i * D + e], acc[e]);
+            for (int e = 0; e < kPer; ++e) acc[e] = fmaf(wu, v[u][e], acc[e]);
+          }
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
   }
   const bool empty = (M == -__builtin_inff());
@@ -826,6 +826,27 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(T* __restrict__ o
   if (row >= num_rows) return;
   merge_row<T, D>(out + row * D, lse_out != nullptr ? lse_out + row : nullptr, o_parts + row * num_parts * D,
                   lse_parts + row * num_parts, num_parts, lane);
+}
+
+// Merge for the partition path: row (sequence, head) combines the
+// min(ceil(n_i / P), num_parts) partitions its sequence was cut into (partial
+// rows spaced `slots` apart); an empty context gives 0 / -inf.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_parts_kernel(T* __restrict__ out, float* __restrict__ lse_out,
+                                                          const float* __restrict__ o_parts,
+                                                          const float* __restrict__ lse_parts,
+                                                          const int32_t* __restrict__ context_lens, int num_seqs,
+                                                          int num_heads, int max_tokens, int part_tokens,
+                                                          int num_parts, int slots) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= static_cast<int64_t>(num_seqs) * num_heads) return;
+  const int seq = static_cast<int>(row / num_heads);
+  int n = context_lens[seq];
+  n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+  const int np = min((n + part_tokens - 1) / part_tokens, num_parts);
+  merge_row<T, D>(out + row * D, lse_out != nullptr ? lse_out + row : nullptr, o_parts + row * slots * D,
+                  lse_parts + row * slots, np, lane);
 }
 
 // ------------------------------------------------------------------ host side
@@ -1072,6 +1093,70 @@ int launch_merge(void* out, float* lse_out, const float* o_parts, const float* l
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int launch_merge_parts(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
+                       const int32_t* context_lens, int num_seqs, int num_heads, int max_tokens, int part_tokens,
+                       int num_parts, int slots, int head_size, int dtype, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
+  if (rows <= 0) return PA_OK;
+  constexpr int kRowsPerBlock = 4;
+  const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
+#define PA_MERGE_PARTS(TT, DD)                                                                                   \
+  hipLaunchKernelGGL((merge_parts_kernel<TT, DD>), g, b, 0, stream, static_cast<TT*>(out), lse_out, o_parts,     \
+                     lse_parts, context_lens, num_seqs, num_heads, max_tokens, part_tokens, num_parts, slots)
+  if (dtype == PA_DTYPE_BF16) {
+    if (head_size == 128) PA_MERGE_PARTS(bf16_t, 128); else PA_MERGE_PARTS(bf16_t, 64);
+  } else {
+    if (head_size == 128) PA_MERGE_PARTS(float, 128); else PA_MERGE_PARTS(float, 64);
+  }
+#undef PA_MERGE_PARTS
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// Compute units of the current device (256 when it cannot be queried).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// pa_decode_split's cut: context partitions on the multi-query kernel (one
+// workgroup per (sequence, partition, kv head), from the hardware
+// dispatcher) when its 16-column tiles hold the group and the batch has at
+// least as many (sequence, kv head) pairs as resident tile workgroups (2 per
+// CU); else pieces on the persistent split kernel, whose workgroups read whole
+// token rows (one wave per kv head), which measured faster for long contexts
+// of a few sequences. PA_SPLIT_KERNEL=pieces|tiles overrides.
+bool split_by_tiles(int group, int num_seqs, int num_kv_heads) {
+  if (group > 16) return false;
+  if (const char* e = getenv("PA_SPLIT_KERNEL")) {
+    if (e[0] == 'p') return false;
+    if (e[0] == 't') return true;
+  }
+  return static_cast<int64_t>(num_seqs) * num_kv_heads >= 2 * static_cast<int64_t>(device_cus());
+}
+
+// Partition length of the partition cut: k * P with k the largest factor
+// that still leaves about three rounds of resident tile workgroups for the
+// longest possible batch (num_seqs contexts of max_context_len tokens), so
+// each workgroup streams long enough to amortise its start; at most the
+// longest context. PA_SPLIT_PART_FACTOR=k overrides k.
+int split_part_tokens(int num_seqs, int num_kv_heads, int max_context_len, int P) {
+  const int64_t n_p = (static_cast<int64_t>(max_context_len) + P - 1) / P;
+  if (n_p <= 1) return P;
+  int64_t k = 0;
+  if (const char* e = getenv("PA_SPLIT_PART_FACTOR")) k = atoi(e);
+  if (k <= 0) {
+    const int64_t target = 3 * 2 * static_cast<int64_t>(device_cus());  // 2 tile workgroups per CU
+    k = static_cast<int64_t>(num_seqs) * n_p * num_kv_heads / target;
+  }
+  k = k < 1 ? 1 : (k > n_p ? n_p : k);
+  return static_cast<int>(k * P);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 
@@ -1121,6 +1206,14 @@ extern "C" int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t
   if (num_heads / num_kv_heads > 16 || (head_size != 64 && head_size != 128)) return -1;
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return -1;
   return decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, fp8_cache != 0) ? 1 : 0;
+}
+
+extern "C" int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
+  if (max_context_len < 0 || partition_size <= 0 || partition_size % kBlockTokens != 0) return -1;
+  if (!split_by_tiles(num_heads / num_kv_heads, num_seqs, num_kv_heads)) return 0;
+  return split_part_tokens(num_seqs, num_kv_heads, max_context_len, partition_size);
 }
 
 extern "C" size_t pa_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_size) {
@@ -1286,6 +1379,24 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
   args.part_tokens = partition_size;
   args.slots = static_cast<int32_t>(L.slots);
   args.scale_log2 = scale * kLog2e;
+  if (split_by_tiles(args.group, num_seqs, num_kv_heads)) {
+    // Partitions of pt = k * P tokens; positions past ceil(max_context_len / P) * P
+    // are ignored, as with the pieces cut.
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int pt = split_part_tokens(num_seqs, num_kv_heads, max_context_len, partition_size);
+    const int64_t cap = min(static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens,
+                            static_cast<int64_t>(partition_size) * (L.slots - 1));
+    const int num_parts = static_cast<int>((cap + pt - 1) / pt);
+    if (num_parts > 0) {
+      st = launch_split_tiles(query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                              num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale, dtype,
+                              pt / kBlockTokens, num_parts, static_cast<int>(cap), args.slots, args.o_parts,
+                              args.lse_parts, s);
+      if (st != PA_OK) return st;
+    }
+    return launch_merge_parts(out, lse_out, args.o_parts, args.lse_parts, context_lens, num_seqs, num_heads,
+                              static_cast<int>(cap), pt, num_parts, args.slots, head_size, dtype, s);
+  }
   return launch_split(args, dtype, head_size, static_cast<hipStream_t>(stream));
 }
 

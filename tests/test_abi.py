@@ -34,7 +34,7 @@ def test_headers_declare_the_boundary():
         "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
         "pa_reshape_and_decode", "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",
-        "pa_decode_uses_tiles"])
+        "pa_decode_uses_tiles", "pa_decode_split_part_tokens"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
         "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
         "pa_pool_allocate", "pa_pool_append_slot", "pa_pool_share", "pa_pool_release",
@@ -166,3 +166,31 @@ def test_multi_query_host_validation(lib):
     assert f(*ok, 3, 5, 8, 3, 128, 10, 16, c(0.1), 1, None, None) == 1   # H_q % H_kv
     assert f(*ok, 3, 5, 64, 2, 128, 10, 16, c(0.1), 1, None, None) == 2  # group above 16
     assert f(*ok, 3, 5, *shape, c(0.1), 2, None, None) == 1              # dtype
+
+
+def test_split_cut_choice(lib, monkeypatch):
+    """pa_decode_split cuts into partitions of k * P tokens (tile kernel) when
+    its 16-column tiles hold the group and the batch has at least as many
+    (sequence, kv head) pairs as resident tile workgroups, else into pieces;
+    the overrides win where they apply. Host-only: with no device the CU count
+    defaults to 256 (512 resident tile workgroups)."""
+    f = lib.pa_decode_split_part_tokens
+    monkeypatch.delenv("PA_SPLIT_KERNEL", raising=False)
+    monkeypatch.setenv("PA_SPLIT_PART_FACTOR", "1")
+    assert f(64, 32, 8, 2048, 512) == 512                 # 512 pairs: partitions
+    assert f(8, 32, 8, 32768, 512) == 0                   # 64 pairs: pieces
+    assert f(256, 64, 2, 4096, 512) == 0                  # group of 32: pieces
+    monkeypatch.setenv("PA_SPLIT_PART_FACTOR", "3")
+    assert f(64, 32, 8, 32768, 512) == 1536
+    assert f(64, 32, 8, 1000, 512) == 1024                # k capped at ceil(1000 / 512)
+    assert f(64, 32, 8, 300, 512) == 512
+    for bad in [(8, 30, 8, 4096, 512), (8, 32, 0, 4096, 512), (8, 32, 8, -1, 512), (8, 32, 8, 4096, 24),
+                (-1, 32, 8, 4096, 512)]:
+        assert f(*bad) == -1
+    monkeypatch.delenv("PA_SPLIT_PART_FACTOR")
+    assert f(64, 32, 8, 2048, 512) == 512                 # 64 * 4 * 8 / 1536 rounds down to k = 1
+    assert f(256, 32, 8, 4096, 512) == 4096               # k = 10, capped at 8 partitions
+    monkeypatch.setenv("PA_SPLIT_KERNEL", "pieces")
+    assert f(64, 32, 8, 2048, 512) == 0
+    monkeypatch.setenv("PA_SPLIT_KERNEL", "tiles")
+    assert f(8, 32, 8, 32768, 512) == 1024 and f(256, 64, 2, 4096, 512) == 0   # k = 8 * 64 * 8 // 1536

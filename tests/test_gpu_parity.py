@@ -25,8 +25,11 @@ def pa():
 @pytest.fixture(autouse=True, params=["persistent", "tiles"])
 def decode_kernel(request, monkeypatch):
     """Run every test here with each decode kernel (the library picks one by
-    batch size; both must give the oracle's answers)."""
+    batch size; both must give the oracle's answers), and pa_decode_split with
+    the matching cut: pieces on the persistent split kernel, or P-token
+    partitions on the tile kernel."""
     monkeypatch.setenv("PA_DECODE_KERNEL", request.param)
+    monkeypatch.setenv("PA_SPLIT_KERNEL", "pieces" if request.param == "persistent" else "tiles")
     return request.param
 
 
@@ -65,7 +68,54 @@ def test_workload_reshape_then_decode(pa, cfg):
 
 
 def check_split_pieces(pa, cfg, inp, kc, vc, ws, P, max_pairs=24):
-    """The workspace pieces of pa_decode_split against the oracle, piece by piece.
+    """The workspace partials of pa_decode_split against the oracle: pieces of
+    the persistent split kernel, or P-token partitions of the tile kernel."""
+    pt = pa.pa_decode_split_part_tokens(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, inp.max_context_len, P)
+    if pt:
+        return check_split_partitions(pa, cfg, inp, kc, vc, ws, P, pt, max_pairs)
+    return check_pieces_cut(pa, cfg, inp, kc, vc, ws, P, max_pairs)
+
+
+def check_split_partitions(pa, cfg, inp, kc, vc, ws, P, pt, max_pairs=24):
+    """Slot p of (sequence i, head h) holds attention over keys
+    [p*pt, min((p+1)*pt, n_i)) (pt = k * P) for every partition of a sequence
+    cut in two or more (the pages' split of one context into partitions,
+    merged by the log-sum-exp rule)."""
+    S, Hq, Hkv, d = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_size
+    g = Hq // Hkv
+    o_parts, lse_parts = pa.workspace_views(ws, S, Hq, d, inp.max_context_len, P)[:2]
+    go, gl = f64(o_parts), f64(lse_parts)
+    q = oracle.decode_values(inp.query, cfg.dtype)
+    n = inp.context_lens.astype(np.int64)
+    checked = 0
+    for i in range(S):
+        np_i = -(-int(n[i]) // pt)
+        if np_i < 2:
+            continue
+        Kc, Vc = oracle.gather_context(kc, vc, inp.block_tables[i], int(n[i]), 16)
+        Kf, Vf = oracle.decode_values(Kc, cfg.dtype), oracle.decode_values(Vc, cfg.dtype)
+        for p in sorted({0, np_i - 1, np_i // 2}):
+            t0, t1 = p * pt, min((p + 1) * pt, int(n[i]))
+            for h in range(Hkv):
+                ro, rl = oracle.attention_contiguous(q[i, h * g:(h + 1) * g], Kf[t0:t1, h:h + 1],
+                                                     Vf[t0:t1, h:h + 1], cfg.scale)
+                # The tile kernel feeds the bf16 matrix cores probabilities
+                # rounded to bf16 (relative error <= 2^-8 each), so a float32
+                # partial may move by up to 2^-8 * max |v| over the partition.
+                tol = PART_TOL[cfg.dtype]
+                if cfg.dtype == "bf16":
+                    tol += 2.0 ** -8 * float(np.abs(Vf[t0:t1, h]).max())
+                assert np.abs(go[i, h * g:(h + 1) * g, p] - ro).max() <= tol
+                assert np.abs(gl[i, h * g:(h + 1) * g, p] - rl).max() <= LSE_TOL[cfg.dtype]
+        checked += 1
+        if checked >= max_pairs:
+            break
+    return checked
+
+
+def check_pieces_cut(pa, cfg, inp, kc, vc, ws, P, max_pairs=24):
+    """The workspace pieces of the persistent split kernel against the oracle,
+    piece by piece.
 
     The header gives the cut (T blocks, R ranges, per-sequence block prefix);
     kv heads go in groups of up to 8, the blocks of all sequences laid end to
@@ -141,8 +191,15 @@ def test_shape_sweep(pa, dtype, d_h, Hq, Hkv):
         assert max_err(l, ref_lse) <= LSE_TOL[dtype]
 
 
+@pytest.mark.parametrize("factor", ["auto", "1", "3"])
 @pytest.mark.parametrize("Hq,Hkv", [(16, 4), (24, 12)])
-def test_split_pieces_long_contexts(pa, Hq, Hkv):
+def test_split_pieces_long_contexts(pa, monkeypatch, decode_kernel, Hq, Hkv, factor):
+    """Long contexts cut in many pieces or partitions; for the partition cut,
+    partitions of P tokens and of k * P (the library's choice, or forced)."""
+    if factor != "auto":
+        if decode_kernel == "persistent":
+            pytest.skip("the factor applies to the partition cut only")
+        monkeypatch.setenv("PA_SPLIT_PART_FACTOR", factor)
     cfg = W.small_case("pieces", 5, Hq, Hkv, 128, "bf16", ("uniform", 900, 3000), seed=31, num_blocks=1200,
                        partition_size=64)
     inp = W.make_inputs(cfg)
