@@ -174,11 +174,12 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapp
  * Work is cut into jobs of one (sequence, kv head) each. Two kernels serve
  * them: the tile kernel (the multi-query kernel with one new token per
  * sequence: one workgroup per job, handed out by the hardware in seq_order,
- * P*V on the matrix cores) and a persistent kernel (workgroups that walk jobs
- * in a fixed order). The persistent kernel, with 8-wave workgroups, is used
- * when every resident workgroup would get at most one job; the tile kernel
- * otherwise (pa_decode_uses_tiles tells which). Results differ between the two
- * only by rounding order.
+ * P*V on the matrix cores; 8-wave workgroups when every resident 4-wave
+ * workgroup would get at most one job, 4-wave ones otherwise), used by
+ * default, and a persistent kernel (workgroups that walk jobs in a fixed
+ * order), kept as the alternative (PA_DECODE_KERNEL=persistent;
+ * pa_decode_uses_tiles tells which runs). Results differ between the two only
+ * by rounding order.
  *
  *   out               [num_seqs, num_heads, head_size], written (dtype).
  *   lse_out           optional float32 [num_seqs, num_heads]: ln sum_t exp(s_t).
@@ -319,10 +320,9 @@ int pa_multi_query(void* out, const void* query, const void* key_cache, const vo
  * pa_decode_uses_tiles - which kernel pa_decode / pa_decode_fp8 /
  * pa_decode_prefix would run for this shape on the current device: 1 for the
  * tile kernel (the multi-query kernel with one new token per sequence), 0 for
- * the persistent decode kernel, -1 for invalid arguments. The choice follows
- * the rule documented with pa_decode; the environment variable
- * PA_DECODE_KERNEL=persistent|tiles overrides it. Queries the device's
- * occupancy, launches nothing.
+ * the persistent decode kernel, -1 for invalid arguments. The tile kernel
+ * runs unless the environment variable PA_DECODE_KERNEL=persistent selects
+ * the other. Launches nothing.
  */
 int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                          int32_t dtype, int32_t fp8_cache);

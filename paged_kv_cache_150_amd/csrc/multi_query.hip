@@ -48,7 +48,9 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4_t;
 
-constexpr int kMqWaves = 4;
+// Waves per workgroup: 4 (two workgroups per CU), or 8 (one per CU) when a
+// launch has at most one job per resident 4-wave workgroup, so that each job
+// is split over twice the waves.
 
 struct MultiArgs {
   const void* query;              // [num_tokens, num_heads, D]
@@ -321,10 +323,12 @@ __device__ __forceinline__ void load_query_cols(const void* query, int64_t row0,
   }
 }
 
-// One workgroup per (tile slot, kv head); slot ids follow the decode kernel's
-// XCD-aware order (id % 8 names the XCD; the kv heads of a slot share it).
-template <typename T, int D, int CB, int NT, bool F8>
-__global__ __launch_bounds__(kMqWaves * kWave, 2) void paged_multi_query_kernel(MultiArgs a) {
+// One workgroup of W waves per (tile slot, kv head); slot ids follow the
+// decode kernel's XCD-aware order (id % 8 names the XCD; the kv heads of a
+// slot share it).
+template <typename T, int D, int CB, int NT, bool F8, int W>
+__global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_kernel(MultiArgs a) {
+  constexpr int kMqWaves = W;
   using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kCols = 16 * NT;
   constexpr int kRow = D + 4;  // LDS row stride in floats: 16-byte rows, the 16 columns on distinct banks
@@ -632,25 +636,49 @@ using namespace pa;
 typedef void (*MultiKernel)(MultiArgs);
 
 template <typename T, int D, int NT, bool F8>
-MultiKernel multi_kernel_for() {
+MultiKernel multi_kernel_for(int W) {
   constexpr int kElem = F8 ? 1 : static_cast<int>(sizeof(T));
   constexpr int kRegsPerBlock = D * kElem / 8;  // K + V dwords per lane
   constexpr int CB = (kRegsPerBlock <= 32 && NT == 1) ? 2 : 1;
-  return paged_multi_query_kernel<T, D, CB, NT, F8>;
+  // 8-wave workgroups for 16-column tiles of 16-bit and FP8 caches; fp32
+  // caches (the small workloads) and 32-column tiles (137 KB of LDS at 8
+  // waves) keep 4.
+  if constexpr (sizeof(T) == 2 && NT == 1) {
+    if (W == 8) return paged_multi_query_kernel<T, D, CB, NT, F8, 8>;
+  }
+  return paged_multi_query_kernel<T, D, CB, NT, F8, 4>;
 }
 
 template <typename T, bool F8>
-MultiKernel pick_multi_t(int D, int NT) {
-  if (D == 128) return NT == 1 ? multi_kernel_for<T, 128, 1, F8>() : multi_kernel_for<T, 128, 2, F8>();
-  return NT == 1 ? multi_kernel_for<T, 64, 1, F8>() : multi_kernel_for<T, 64, 2, F8>();
+MultiKernel pick_multi_t(int D, int NT, int W) {
+  if (D == 128) return NT == 1 ? multi_kernel_for<T, 128, 1, F8>(W) : multi_kernel_for<T, 128, 2, F8>(W);
+  return NT == 1 ? multi_kernel_for<T, 64, 1, F8>(W) : multi_kernel_for<T, 64, 2, F8>(W);
 }
 
 // fp32 caches with 128-element heads keep 16-column tiles (32 would spill).
-MultiKernel pick_multi(int dtype, int D, int NT, bool fp8_cache) {
-  if (fp8_cache) return pick_multi_t<bf16_t, true>(D, NT);
-  if (dtype == PA_DTYPE_BF16) return pick_multi_t<bf16_t, false>(D, NT);
-  if (D == 128) return multi_kernel_for<float, 128, 1, false>();
-  return NT == 1 ? multi_kernel_for<float, 64, 1, false>() : multi_kernel_for<float, 64, 2, false>();
+// Returns the kernel and sets W to the waves per workgroup it was built for.
+MultiKernel pick_multi(int dtype, int D, int NT, bool fp8_cache, int& W) {
+  if ((dtype == PA_DTYPE_F32 && !fp8_cache) || NT != 1) W = 4;
+  if (fp8_cache) return pick_multi_t<bf16_t, true>(D, NT, W);
+  if (dtype == PA_DTYPE_BF16) return pick_multi_t<bf16_t, false>(D, NT, W);
+  if (D == 128) return multi_kernel_for<float, 128, 1, false>(W);
+  return NT == 1 ? multi_kernel_for<float, 64, 1, false>(W) : multi_kernel_for<float, 64, 2, false>(W);
+}
+
+// Waves per workgroup for a launch of `jobs` workgroups: 8 when every
+// resident 4-wave workgroup (two per CU) would get at most one job, else 4.
+// PA_MQ_WAVES=4|8 overrides. (pick_multi keeps 4 where no 8-wave kernel is
+// built.)
+int pick_waves(int64_t jobs) {
+  if (const char* e = getenv("PA_MQ_WAVES")) {
+    const int v = atoi(e);
+    if (v == 4 || v == 8) return v;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    cus = 256;
+  return jobs <= 2 * static_cast<int64_t>(cus) ? 8 : 4;
 }
 
 int max_tiles(int dtype, int D) { return (dtype == PA_DTYPE_F32 && D == 128) ? 1 : 2; }
@@ -703,7 +731,6 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
   const int g = num_heads / num_kv_heads;
   int NT = query_start_loc == nullptr ? 1 : pick_tiles(num_tokens, num_seqs, g);
   NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
-  MultiKernel k = pick_multi(dtype, head_size, NT, fp8_cache);
   MultiArgs a{};
   a.query = query;
   a.key_cache = key_cache;
@@ -726,6 +753,13 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
       query_start_loc == nullptr ? num_seqs : static_cast<int64_t>(num_tokens) / a.tile_tokens + num_seqs;
   const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
   if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  // Jobs that do work: about ceil(mean new tokens per sequence / tile) tiles
+  // per sequence (the slot bound counts one spare slot per sequence).
+  const int64_t per_seq = query_start_loc == nullptr ? 1
+      : (static_cast<int64_t>(num_tokens) + static_cast<int64_t>(num_seqs) * a.tile_tokens - 1) /
+            (static_cast<int64_t>(num_seqs) * a.tile_tokens);
+  int W = pick_waves(static_cast<int64_t>(num_seqs) * per_seq * num_kv_heads);
+  MultiKernel k = pick_multi(dtype, head_size, NT, fp8_cache, W);
   a.num_slots = static_cast<int32_t>(slots);
   a.scale_log2 = scale_log2;
   a.v_scale = v_scale;
@@ -735,7 +769,7 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
   a.new_key = new_key;
   a.new_value = new_value;
   a.slot_mapping = slot_mapping;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -749,7 +783,6 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
   const int g = num_heads / num_kv_heads;
   int NT = pick_tiles(num_seqs, 1, g);
   NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
-  MultiKernel k = pick_multi(dtype, head_size, NT, false);
   MultiArgs a{};
   a.query = query;
   a.key_cache = key_cache;
@@ -767,13 +800,15 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
   const int64_t slots = (static_cast<int64_t>(num_seqs) + a.tile_tokens - 1) / a.tile_tokens;
   const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
   if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  int W = pick_waves(slots * num_kv_heads);
+  MultiKernel k = pick_multi(dtype, head_size, NT, false, W);
   a.num_slots = static_cast<int32_t>(slots);
   a.scale_log2 = scale * kLog2e;
   a.v_scale = 1.0f;
   a.prefix_keys = prefix_blocks * kBlockTokens;
   a.part_o = part_o;
   a.part_lse = part_lse;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -785,7 +820,6 @@ int pa::launch_split_tiles(const void* query, const void* key_cache, const void*
                            hipStream_t stream) {
   const int g = num_heads / num_kv_heads;
   if (g > 16 || part_blocks <= 0 || num_parts <= 0 || parts_stride < num_parts) return PA_ERR_UNSUPPORTED;
-  MultiKernel k = pick_multi(dtype, head_size, 1, false);
   MultiArgs a{};
   a.query = query;
   a.key_cache = key_cache;
@@ -803,6 +837,8 @@ int pa::launch_split_tiles(const void* query, const void* key_cache, const void*
   const int64_t slots = static_cast<int64_t>(num_seqs) * num_parts;
   const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
   if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  int W = pick_waves(slots * num_kv_heads);
+  MultiKernel k = pick_multi(dtype, head_size, 1, false, W);
   a.num_slots = static_cast<int32_t>(slots);
   a.scale_log2 = scale * kLog2e;
   a.v_scale = 1.0f;
@@ -812,7 +848,7 @@ int pa::launch_split_tiles(const void* query, const void* key_cache, const void*
   a.num_parts = num_parts;
   a.parts_stride = parts_stride;
   a.part_cap = part_cap;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(kMqWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -949,25 +949,22 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
-// Which kernel serves a decode step. The tile kernel (the multi-query kernel
+// Which kernel serves a decode step: the tile kernel (the multi-query kernel
 // with one token per sequence: P*V on the matrix cores, one workgroup per
-// (sequence, kv head) handed out by the hardware in seq_order) is the faster
-// one except when every resident workgroup would get at most one job; then
-// the persistent kernel with 8-wave workgroups splits each job more finely.
+// (sequence, kv head) handed out by the hardware in seq_order, with 8-wave
+// workgroups when the grid is a single round) measured faster on every
+// workload; the persistent kernel is kept as the alternative.
 // PA_DECODE_KERNEL=persistent|tiles forces one (the tests run both).
 bool decode_by_tiles(int num_seqs, int num_kv_heads, int group, int dtype, int head_size, bool fp8_cache) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)dtype;
+  (void)head_size;
+  (void)fp8_cache;
   if (const char* e = getenv("PA_DECODE_KERNEL")) {
     if (e[0] == 'p') return false;
-    if (e[0] == 't') return true;
   }
-  const int G = next_pow2_group(group);
-  DecodeKernel k = fp8_cache ? (head_size == 128 ? pick_group_fp8<128>(G) : pick_group_fp8<64>(G))
-                             : pick_decode(dtype, head_size, G);
-  if (!k || G >= 16) return true;
-  const int64_t jobs = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * num_kv_heads;
-  const int64_t resident4 = resident_groups(reinterpret_cast<const void*>(k), 4 * kWave,
-                                            static_cast<size_t>(4) * G * head_size * sizeof(float));
-  return !(resident4 > 0 && jobs <= resident4);
+  return group <= 16;
 }
 
 int launch_decode(DecodeArgs args, int num_seqs, int dtype, int head_size, hipStream_t stream,

@@ -79,11 +79,14 @@ SWEEP = [(d, Hq, Hkv, dt) for dt in ("bf16", "f32") for d in (64, 128)
          for Hq, Hkv in ((8, 8), (8, 4), (8, 2), (16, 4), (16, 2), (16, 1), (6, 2))]
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("columns", ["16", "32", "auto"])
 @pytest.mark.parametrize("d,Hq,Hkv,dtype", SWEEP, ids=lambda v: str(v))
-def test_multi_query_matches_the_oracle(pa, monkeypatch, d, Hq, Hkv, dtype, columns):
+def test_multi_query_matches_the_oracle(pa, monkeypatch, d, Hq, Hkv, dtype, columns, waves):
+    """Both workgroup sizes (fp32 caches and 32-column tiles always run 4 waves)."""
     if columns != "auto":
         monkeypatch.setenv("PA_MQ_TILE_COLUMNS", columns)
+    monkeypatch.setenv("PA_MQ_WAVES", waves)
     mq = _case(d, Hq, Hkv, dtype, QLENS, NLENS)
     out, lse = _run(pa, mq)
     _check(mq, out, lse)
@@ -150,11 +153,14 @@ def test_full_size_workloads_sampled(pa, name):
     _check(mq, out, lse, rows=rows)
 
 
-def test_decode_kernel_choice(pa):
-    """The batch-256 shape runs on the tile kernel, the batch-64 shape (one job
-    per resident workgroup) on the persistent kernel, and the override wins."""
+def test_decode_kernel_choice(pa, monkeypatch):
+    """Decode runs on the tile kernel for every supported shape unless the
+    override asks for the persistent kernel."""
+    monkeypatch.delenv("PA_DECODE_KERNEL", raising=False)
     assert pa.pa_decode_uses_tiles(256, 32, 8, 128)
-    assert not pa.pa_decode_uses_tiles(64, 32, 8, 128)
+    assert pa.pa_decode_uses_tiles(64, 32, 8, 128)
     assert pa.pa_decode_uses_tiles(256, 32, 8, 128, fp8_cache=True)
+    monkeypatch.setenv("PA_DECODE_KERNEL", "persistent")
+    assert not pa.pa_decode_uses_tiles(64, 32, 8, 128)
     with pytest.raises(ValueError):
         pa.pa_decode_uses_tiles(4, 30, 8, 128)

@@ -22,15 +22,19 @@ def pa():
     return ensure_built()
 
 
-@pytest.fixture(autouse=True, params=["persistent", "tiles"])
+@pytest.fixture(autouse=True, params=["persistent", "tiles", "tiles4"])
 def decode_kernel(request, monkeypatch):
     """Run every test here with each decode kernel (the library picks one by
-    batch size; both must give the oracle's answers), and pa_decode_split with
-    the matching cut: pieces on the persistent split kernel, or P-token
-    partitions on the tile kernel."""
-    monkeypatch.setenv("PA_DECODE_KERNEL", request.param)
-    monkeypatch.setenv("PA_SPLIT_KERNEL", "pieces" if request.param == "persistent" else "tiles")
-    return request.param
+    batch size; both must give the oracle's answers) — the tile kernel with
+    its own choice of waves per workgroup (8 on these small grids) and with 4
+    forced — and pa_decode_split with the matching cut: pieces on the
+    persistent split kernel, or partitions on the tile kernel."""
+    kernel = "tiles" if request.param.startswith("tiles") else request.param
+    monkeypatch.setenv("PA_DECODE_KERNEL", kernel)
+    monkeypatch.setenv("PA_SPLIT_KERNEL", "pieces" if kernel == "persistent" else "tiles")
+    if request.param == "tiles4":
+        monkeypatch.setenv("PA_MQ_WAVES", "4")
+    return kernel
 
 
 def _say(msg):
