@@ -674,11 +674,7 @@ int pick_waves(int64_t jobs) {
     const int v = atoi(e);
     if (v == 4 || v == 8) return v;
   }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || cus <= 0)
-    cus = 256;
-  return jobs <= 2 * static_cast<int64_t>(cus) ? 8 : 4;
+  return jobs <= 2 * static_cast<int64_t>(device_cus()) ? 8 : 4;
 }
 
 int max_tiles(int dtype, int D) { return (dtype == PA_DTYPE_F32 && D == 128) ? 1 : 2; }
@@ -810,6 +806,18 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
   a.part_lse = part_lse;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa::device_cus() {
+  // Cached per device (every caller on a device writes the same value).
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  return cus;
 }
 
 int pa::launch_split_tiles(const void* query, const void* key_cache, const void* value_cache,

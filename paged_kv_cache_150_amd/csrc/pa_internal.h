@@ -45,4 +45,7 @@ int launch_split_tiles(const void* query, const void* key_cache, const void* val
                        int32_t part_cap, int32_t parts_stride, float* o_parts, float* lse_parts,
                        hipStream_t stream);
 
+// Compute units of the current device (256 when it cannot be queried).
+int device_cus();
+
 }  // namespace pa

@@ -955,12 +955,7 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
 // workgroups when the grid is a single round) measured faster on every
 // workload; the persistent kernel is kept as the alternative.
 // PA_DECODE_KERNEL=persistent|tiles forces one (the tests run both).
-bool decode_by_tiles(int num_seqs, int num_kv_heads, int group, int dtype, int head_size, bool fp8_cache) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)dtype;
-  (void)head_size;
-  (void)fp8_cache;
+bool decode_by_tiles(int group) {
   if (const char* e = getenv("PA_DECODE_KERNEL")) {
     if (e[0] == 'p') return false;
   }
@@ -1111,15 +1106,6 @@ int launch_merge_parts(void* out, float* lse_out, const float* o_parts, const fl
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// Compute units of the current device (256 when it cannot be queried).
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || cus <= 0)
-    return 256;
-  return cus;
-}
-
 // pa_decode_split's cut: context partitions on the multi-query kernel (one
 // workgroup per (sequence, partition, kv head), from the hardware
 // dispatcher) when its 16-column tiles hold the group and the batch has at
@@ -1172,7 +1158,7 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                         num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
   if (st != PA_OK || num_seqs == 0) return st;
-  if (decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, false))
+  if (decode_by_tiles(num_heads / num_kv_heads))
     return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                                num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
                                dtype, false, lse_out, seq_order, 0, nullptr, nullptr,
@@ -1202,7 +1188,7 @@ extern "C" int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
   if (num_heads / num_kv_heads > 16 || (head_size != 64 && head_size != 128)) return -1;
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return -1;
-  return decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, fp8_cache != 0) ? 1 : 0;
+  return decode_by_tiles(num_heads / num_kv_heads) ? 1 : 0;
 }
 
 extern "C" int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -1246,7 +1232,7 @@ extern "C" int pa_decode_prefix(void* out, const void* query, const void* key_ca
                           num_heads, num_kv_heads, head_size, num_blocks, prefix_blocks, scale, dtype, part_o,
                           part_lse, s);
   if (st != PA_OK) return st;
-  if (decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, false))
+  if (decode_by_tiles(num_heads / num_kv_heads))
     return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                                num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
                                dtype, false, lse_out, seq_order, prefix_blocks, part_o, part_lse, s);
@@ -1285,7 +1271,7 @@ extern "C" int pa_decode_fp8(void* out, const void* query, const uint8_t* key_ca
   if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
     return PA_ERR_INVALID_ARG;
-  if (decode_by_tiles(num_seqs, num_kv_heads, num_heads / num_kv_heads, dtype, head_size, true))
+  if (decode_by_tiles(num_heads / num_kv_heads))
     return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                                num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * k_scale * kLog2e,
                                v_scale, dtype, true, lse_out, seq_order, 0, nullptr, nullptr,
