@@ -37,6 +37,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -809,14 +811,18 @@ int pa::launch_prefix_pass(const void* query, const void* key_cache, const void*
 }
 
 int pa::device_cus() {
-  // Cached per device (every caller on a device writes the same value).
-  static int cached[64] = {};
+  // Cached per device (every caller on a device stores the same value).
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
-  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  if (slot) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
