@@ -17,12 +17,16 @@ def pa():
     return ensure_built()
 
 
-@pytest.fixture(autouse=True, params=["persistent", "tiles"])
+@pytest.fixture(autouse=True, params=["persistent", "tiles", "tiles4"])
 def decode_kernel(request, monkeypatch):
-    """Run every test here with each decode kernel (the library picks one by
-    batch size; both must give the oracle's answers)."""
-    monkeypatch.setenv("PA_DECODE_KERNEL", request.param)
-    return request.param
+    """Run every test here with each decode kernel (both must give the
+    oracle's answers): the tile kernel with its own choice of waves per
+    workgroup (8 on these small grids) and with 4 forced."""
+    kernel = "tiles" if request.param.startswith("tiles") else request.param
+    monkeypatch.setenv("PA_DECODE_KERNEL", kernel)
+    if request.param == "tiles4":
+        monkeypatch.setenv("PA_MQ_WAVES", "4")
+    return kernel
 
 
 def _prefix_decode(pa, dev, prefix_blocks, lse=True, order=None):

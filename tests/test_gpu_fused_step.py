@@ -54,12 +54,14 @@ def test_fused_step_on_every_workload(pa, monkeypatch, cfg):
     assert max_err(lse[torch.from_numpy(rows).cuda()], ref_lse) <= LSE_TOL[cfg.dtype]
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("dtype,d_h,Hq,Hkv", [("bf16", 64, 8, 2), ("f32", 128, 16, 4), ("bf16", 128, 12, 4),
                                               ("f32", 64, 16, 16)])
-def test_fused_step_shapes_padding_and_empty(pa, dtype, d_h, Hq, Hkv):
+def test_fused_step_shapes_padding_and_empty(pa, monkeypatch, dtype, d_h, Hq, Hkv, waves):
     """Ragged contexts (block boundaries, one token, empty), padding slots
     (-1: nothing written, the cache already holds the token) and a slot past
-    the pool (skipped)."""
+    the pool (skipped); 4- and 8-wave workgroups (fp32 caches run 4)."""
+    monkeypatch.setenv("PA_MQ_WAVES", waves)
     lens = np.array([1, 15, 16, 17, 33, 100, 257, 31, 0, 48], np.int32)
     cfg = W.small_case("fused", len(lens), Hq, Hkv, d_h, dtype, ("uniform", 1, 2), seed=61, num_blocks=160)
     inp = W.make_inputs(cfg, context_lens=np.maximum(lens, 1))
