@@ -11,7 +11,9 @@ def test_five_configs_shapes():
     assert [x.name for x in W.CONFIGS] == ["tiny_f32", "llama3_8b_b64", "llama3_8b_b256",
                                           "long_split", "prefix_70b"]
     assert c["tiny_f32"].dtype == "f32" and c["tiny_f32"].scale == 1 / 8
-    for x in W.CONFIGS[1:]:
+    for x in W.CONFIGS:
+        if x.name == "tiny_f32":
+            continue
         assert x.dtype == "bf16" and x.head_size == 128 and x.num_kv_heads == 8
     assert c["prefix_70b"].group == 8 and c["llama3_8b_b256"].group == 4
     assert [x.seed for x in W.CONFIGS] == [0, 1, 2, 3, 4]

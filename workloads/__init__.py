@@ -109,8 +109,10 @@ CONFIGS: list[PagedConfig] = [
 # Beyond the five workloads above: the batch-256 step with an FP8 (E4M3) KV
 # cache. Codes are drawn directly (log-uniform magnitudes); with the scales
 # below, keys and values span about 2^-12 .. 4.
+_BASE_BY_NAME = {c.name: c for c in CONFIGS}
+
 EXTRA_CONFIGS: list[PagedConfig] = [
-    dataclasses.replace(CONFIGS[2], name="llama3_8b_b256_fp8", kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64,
+    dataclasses.replace(_BASE_BY_NAME["llama3_8b_b256"], name="llama3_8b_b256_fp8", kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 64,
                         description="Batch-256 Llama-3-8B-shaped decode over an FP8 E4M3 KV cache "
                                     "(bf16 query/out, k_scale = v_scale = 1/64)"),
 ]
@@ -414,11 +416,11 @@ class MultiQueryConfig:
 
 MQ_CONFIGS: list[MultiQueryConfig] = [
     MultiQueryConfig(
-        name="llama3_8b_b64_spec4", base=CONFIGS[1], new_tokens=("fixed", 5),
+        name="llama3_8b_b64_spec4", base=CONFIG_BY_NAME["llama3_8b_b64"], new_tokens=("fixed", 5),
         description="Speculative verify on the batch-64 Llama-3-8B-shaped decode: k = 4 draft tokens, "
                     "5 new positions per sequence, ctx U{512..2048}"),
     MultiQueryConfig(
-        name="llama3_8b_b256_chunk1024", base=CONFIGS[2], new_tokens=("chunk", 1, 1024, 2048),
+        name="llama3_8b_b256_chunk1024", base=CONFIG_BY_NAME["llama3_8b_b256"], new_tokens=("chunk", 1, 1024, 2048),
         description="The batch-256 decode step with one sequence running a 1024-token prompt chunk "
                     "(tokens 1024..2047 of its prompt) in the same pass"),
 ]
