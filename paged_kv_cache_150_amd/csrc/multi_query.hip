@@ -439,6 +439,7 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   const int blk_end = (key_end + kBlockTokens - 1) / kBlockTokens;
   const int nchunk = blk_end > blk_begin ? (blk_end - blk_begin + CB - 1) / CB : 0;
   const int blk_last = blk_end - 1;
+  const int last_rows = key_end - blk_last * kBlockTokens;  // valid rows of the last block
   // Chunks from mask_from on reach past some column's last visible key.
   constexpr int kChunkTokens = CB * kBlockTokens;
   const int mask_from = max(min_lim - blk_begin * kBlockTokens, 0) / kChunkTokens;
@@ -517,23 +518,23 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   Chunk<T, D, 16, CB, F8> fa, fb;
   if (mine > 0) {
     load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
-                             head_off, lane);
+                             head_off, lane, last_rows);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
       load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
-                               head_off, lane);
+                               head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       __builtin_amdgcn_sched_barrier(0);
       load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride, blk_stride,
-                               head_off, lane);
+                               head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
       load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
-                               head_off, lane);
+                               head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       if constexpr (kFusedWrite) {
