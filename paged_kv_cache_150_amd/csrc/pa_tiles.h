@@ -34,7 +34,8 @@ struct Chunk {
 // are wave-uniform, so each load is a scalar base (block, head, row) plus a
 // 32-bit per-lane offset. Block blk_last holds only last_rows valid rows: its
 // lanes for later rows read the last valid row again (same lines, no extra
-// memory traffic); those rows are masked out by the caller.
+// memory traffic); those rows are masked out by the caller (16-bit and FP8
+// caches).
 template <typename T, int D, int G, int CB, bool F8 = false>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
                                            const int32_t* bt_row, int blk0, int blk_last,
@@ -48,6 +49,7 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
   const uint32_t vcol = tok * (S::kVDw * 4);
   const uint32_t koff = tok * tok_stride_bytes + j * 16;                      // K: row tok, piece j
   const uint32_t koff_last = min(tok, lr) * tok_stride_bytes + j * 16;
+  const uint32_t voff = (4 * j) * tok_stride_bytes + vcol;                   // V: rows 4j.., piece tok
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int b = min(blk0 + i, blk_last);
@@ -59,14 +61,24 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
     const int64_t base = static_cast<int64_t>(phys) * blk_stride_bytes + head_off_bytes;
     const gchar_t* kb = uniform_ptr(kc + base);
     const gchar_t* vb = uniform_ptr(vc + base);
-    const uint32_t ko = last ? koff_last : koff;
+    if constexpr (S::kElemBytes <= 2) {
+      const uint32_t ko = last ? koff_last : koff;
 #pragma unroll
-    for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + ko);
+      for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + ko);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // V: rows 4j + r, piece tok.
-      const int row = last ? min(4 * j + r, lr) : 4 * j + r;
-      load_dwords<S::kVDw>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
+      for (int r = 0; r < 4; ++r) {
+        // V: rows 4j + r, piece tok.
+        const int row = last ? min(4 * j + r, lr) : 4 * j + r;
+        load_dwords<S::kVDw>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
+      }
+    } else {
+      // fp32 caches (the small workloads) read whole blocks: the per-row
+      // offsets would spill registers there.
+#pragma unroll
+      for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + koff);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        load_dwords<S::kVDw>(f.v[i][r], vb + r * tok_stride_bytes + voff);
     }
   }
 }
