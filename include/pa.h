@@ -348,7 +348,7 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * layer": tiling plus online softmax). The work is cut one of two ways
  * (pa_decode_split_part_tokens says which):
  *
- * Partitions (group H_q / H_kv <= 16): with P' = k * P tokens
+ * Partitions (the default for groups H_q / H_kv <= 16): with P' = k * P tokens
  * (pa_decode_split_part_tokens: k >= 1 grows with the grid the call would
  * launch, so every workgroup streams long enough) and C = ceil(max_context_len
  * / P) * P, partition p of sequence i is its keys [p*P', min((p+1)*P', n_i, C)),
@@ -359,7 +359,9 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * on the same stream merges the slots of every (sequence, head) that hold a
  * partition into out. The header is not written.
  *
- * Pieces (larger groups, or PA_SPLIT_KERNEL=pieces): the kv heads are taken
+ * Pieces (groups above 16; groups of at most 4 when num_seqs * H_kv is below
+ * the number of resident tile workgroups, i.e. a few long contexts; or
+ * PA_SPLIT_KERNEL=pieces): the kv heads are taken
  * in groups of up to 8 (one persistent workgroup has one wave per kv head of
  * its group, all walking the same blocks). Per head group, the blocks of all
  * sequences are laid end to end (sequence i has nb_i = ceil(n_i / block_size)

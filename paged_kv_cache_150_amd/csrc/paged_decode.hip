@@ -1108,17 +1108,21 @@ int launch_merge_parts(void* out, float* lse_out, const float* o_parts, const fl
 
 // pa_decode_split's cut: context partitions on the multi-query kernel (one
 // workgroup per (sequence, partition, kv head), from the hardware
-// dispatcher) when its 16-column tiles hold the group and the batch has at
-// least as many (sequence, kv head) pairs as resident tile workgroups (2 per
-// CU); else pieces on the persistent split kernel, whose workgroups read whole
-// token rows (one wave per kv head), which measured faster for long contexts
-// of a few sequences. PA_SPLIT_KERNEL=pieces|tiles overrides.
+// dispatcher) when its 16-column tiles hold the group; pieces on the
+// persistent split kernel, whose workgroups read whole token rows (one wave
+// per kv head), for groups above 16 and for groups of at most 4 when the
+// batch has fewer (sequence, kv head) pairs than resident tile workgroups (2
+// per CU): long contexts of a few sequences, where the pieces measured faster.
+// (Larger groups keep the tiles: the piece kernel's per-lane accumulators
+// spill registers from a group of 8 up.) PA_SPLIT_KERNEL=pieces|tiles
+// overrides.
 bool split_by_tiles(int group, int num_seqs, int num_kv_heads) {
   if (group > 16) return false;
   if (const char* e = getenv("PA_SPLIT_KERNEL")) {
     if (e[0] == 'p') return false;
     if (e[0] == 't') return true;
   }
+  if (group > 4) return true;
   return static_cast<int64_t>(num_seqs) * num_kv_heads >= 2 * static_cast<int64_t>(device_cus());
 }
 

@@ -178,7 +178,8 @@ def test_split_cut_choice(lib, monkeypatch):
     monkeypatch.delenv("PA_SPLIT_KERNEL", raising=False)
     monkeypatch.setenv("PA_SPLIT_PART_FACTOR", "1")
     assert f(64, 32, 8, 2048, 512) == 512                 # 512 pairs: partitions
-    assert f(8, 32, 8, 32768, 512) == 0                   # 64 pairs: pieces
+    assert f(8, 32, 8, 32768, 512) == 0                   # 64 pairs, group 4: pieces
+    assert f(8, 64, 8, 32768, 512) == 512                 # 64 pairs, group 8: partitions
     assert f(256, 64, 2, 4096, 512) == 0                  # group of 32: pieces
     monkeypatch.setenv("PA_SPLIT_PART_FACTOR", "3")
     assert f(64, 32, 8, 32768, 512) == 1536
