@@ -337,6 +337,9 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   __shared__ __attribute__((aligned(16))) float s_acc[kMqWaves][kCols][kRow];
   __shared__ float s_m[kMqWaves][kCols];
   __shared__ float s_l[kMqWaves][kCols];
+  __shared__ float s_w[kMqWaves + 1][kCols];  // merge weights per column (last: the prefix part)
+  __shared__ float s_L[kCols];                // normaliser per column
+  __shared__ float s_lse[kCols];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -589,42 +592,69 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   }
   __syncthreads();
 
-  // Merge the waves with weights 2^(m_w - M) and write each column's row.
-  for (int idx = threadIdx.x; idx < ncols * D; idx += kMqWaves * kWave) {
-    const int c = idx / D;
-    const int d = idx - c * D;
+  // Merge weights per column, once: wave w's part weighs 2^(m_w - M), and
+  // the normaliser is L = sum_w 2^(m_w - M) l_w. A prefix-pass result joins
+  // as one more part: l = 1, acc = its output, m = its log-sum-exp in base 2.
+  auto out_row = [&](int c) {
     const int tok = c / g;
-    const int64_t row = (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
+    return (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
+  };
+  for (int c = threadIdx.x; c < ncols; c += kMqWaves * kWave) {
+    const int64_t row = out_row(c);
     float M = -__builtin_inff();
 #pragma unroll
     for (int v = 0; v < kMqWaves; ++v) M = fmaxf(M, s_m[v][c]);
-    // A prefix-pass result joins as one more part: l = 1, acc = its output,
-    // m = its log-sum-exp in base 2.
     const float pm = a.prefix_o != nullptr ? a.prefix_lse[row] * kLog2e : -__builtin_inff();
     M = fmaxf(M, pm);
-    float o = 0.f, L = 0.f;
-    if (M != -__builtin_inff()) {
+    float L = 0.f;
+    float w[kMqWaves + 1];
+#pragma unroll
+    for (int v = 0; v < kMqWaves; ++v) {
+      w[v] = M == -__builtin_inff() ? 0.f : fast_exp2(s_m[v][c] - M);
+      L = fmaf(w[v], s_l[v][c], L);
+    }
+    w[kMqWaves] = pm == -__builtin_inff() ? 0.f : fast_exp2(pm - M);
+    L += w[kMqWaves];
+#pragma unroll
+    for (int v = 0; v <= kMqWaves; ++v) s_w[v][c] = w[v];
+    s_L[c] = L;
+    s_lse[c] = M == -__builtin_inff() ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
+  }
+  __syncthreads();
+
+  // Each column's row, two elements per thread: out = (sum_w weight_w acc_w) / L
+  // times v_scale (0 for a column with no visible key).
+  for (int idx = 2 * threadIdx.x; idx < ncols * D; idx += 2 * kMqWaves * kWave) {
+    const int c = idx / D;
+    const int d = idx - c * D;
+    const int64_t row = out_row(c);
+    float o0 = 0.f, o1 = 0.f;
+    const float L = s_L[c];
+    if (L != 0.f) {
 #pragma unroll
       for (int v = 0; v < kMqWaves; ++v) {
-        const float wt = fast_exp2(s_m[v][c] - M);
-        L = fmaf(wt, s_l[v][c], L);
-        o = fmaf(wt, s_acc[v][c][d], o);
+        const float wv = s_w[v][c];
+        o0 = fmaf(wv, s_acc[v][c][d], o0);
+        o1 = fmaf(wv, s_acc[v][c][d + 1], o1);
       }
-      if (pm != -__builtin_inff()) {
-        const float wt = fast_exp2(pm - M);
-        L += wt;
-        o = fmaf(wt, a.prefix_o[row * D + d], o);
+      if (a.prefix_o != nullptr) {
+        const float wp = s_w[kMqWaves][c];
+        if (wp != 0.f) {
+          o0 = fmaf(wp, a.prefix_o[row * D + d], o0);
+          o1 = fmaf(wp, a.prefix_o[row * D + d + 1], o1);
+        }
       }
-      o = o / L * a.v_scale;
+      o0 = o0 / L * a.v_scale;
+      o1 = o1 / L * a.v_scale;
     }
-    const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
     if (a.part_o != nullptr) {
       const int64_t orow = part >= 0 ? row * a.parts_stride + part : row;
-      a.part_o[orow * D + d] = o;
-      if (d == 0) a.part_lse[orow] = lse;
+      a.part_o[orow * D + d] = o0;
+      a.part_o[orow * D + d + 1] = o1;
+      if (d == 0) a.part_lse[orow] = s_lse[c];
     } else {
-      store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
-      if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
+      store_pair<T>(static_cast<T*>(a.out) + row * D + d, o0, o1);
+      if (a.lse_out != nullptr && d == 0) a.lse_out[row] = s_lse[c];
     }
   }
 }

@@ -128,6 +128,18 @@ __device__ __forceinline__ void store_elem<float>(float* p, float x) { *p = x; }
 template <>
 __device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, float x) { *p = f32_to_bf16(x); }
 
+// Two consecutive elements (p 4-byte aligned for bf16, 8-byte for float).
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, float x, float y);
+template <>
+__device__ __forceinline__ void store_pair<float>(float* p, float x, float y) {
+  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y)};
+}
+template <>
+__device__ __forceinline__ void store_pair<bf16_t>(bf16_t* p, float x, float y) {
+  *reinterpret_cast<uint32_t*>(p) = static_cast<uint32_t>(f32_to_bf16(x)) | (static_cast<uint32_t>(f32_to_bf16(y)) << 16);
+}
+
 // Load `NDW` dwords (8, 16 or 32 bytes) that are 16-byte (or 8-byte) aligned.
 template <int NDW>
 __device__ __forceinline__ void load_dwords(uint32_t (&dst)[NDW], const gchar_t* src) {
