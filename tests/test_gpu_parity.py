@@ -403,9 +403,12 @@ def test_empty_contexts(pa):
         assert max_err(o, ref) <= 1e-5 and max_err(l, ref_lse) <= 1e-5
 
 
-def test_merge_partitions_alone(pa):
+@pytest.mark.parametrize("P", [9, 40, 70, 130])
+def test_merge_partitions_alone(pa, P):
+    """One batch of partials (9), two (40), the lane-strided log-sum-exps past
+    64 (70, 130)."""
     rng = np.random.default_rng(17)
-    S, H, P, dh = 5, 6, 9, 128
+    S, H, dh = 5, 6, 128
     o = rng.standard_normal((S, H, P, dh)).astype(np.float32)
     lp = (rng.standard_normal((S, H, P)) * 3).astype(np.float32)
     lp[rng.random((S, H, P)) < 0.3] = -np.inf
