@@ -182,8 +182,18 @@ def bench_multi_query(args):
 
     reshape_p = [pa.prepared(pa.pa_reshape_and_cache, new_k, new_v, *pools[k], slots, stream=stream)
                  for k in range(2)]
-    attend_p = [pa.prepared(pa.pa_multi_query, out, q, *pools[k], bt, cl, loc, base.scale, stream=stream)
-                for k in range(2)]
+    split = args.decode == "split"
+    if split:
+        # Every context cut into P-token partitions, then the per-row merge.
+        P = args.partition_size or 2048
+        max_ctx = int(inp.context_lens.max(initial=0))
+        ws = torch.empty(pa.pa_multi_query_split_workspace_bytes(mq.num_tokens, base.num_heads, base.head_size,
+                                                                 max_ctx, P), dtype=torch.uint8, device=dev)
+        attend_p = [pa.prepared(pa.pa_multi_query_split, out, q, *pools[k], bt, cl, loc, base.scale, max_ctx, P, ws,
+                                stream=stream) for k in range(2)]
+    else:
+        attend_p = [pa.prepared(pa.pa_multi_query, out, q, *pools[k], bt, cl, loc, base.scale, stream=stream)
+                    for k in range(2)]
 
     print(f"[bench] warmup {args.warmup}, timed {args.steps} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -224,8 +234,9 @@ def bench_multi_query(args):
     else:
         roof = {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": stored_traffic(cfg.name, "mq", "paged_multi_query"),
-                 "kernel": "paged_multi_query_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+    roof.update({"traffic": stored_traffic(cfg.name, "mq_split" if split else "mq", "paged_multi_query"),
+                 "kernel": "paged_multi_query_kernel (context partitions) + merge_mq_parts_kernel" if split
+                 else "paged_multi_query_kernel", "algorithmic_bytes_per_launch": kv_bytes,
                  "algorithmic_flops_per_launch": flops, "achieved_tflops": round(att_tflops, 2),
                  "kernel_source_hash": kernel_source_hash()})
     T = mq.num_tokens
@@ -238,7 +249,8 @@ def bench_multi_query(args):
                    "new_tokens": T, "num_heads": base.num_heads, "num_kv_heads": base.num_kv_heads,
                    "head_size": base.head_size, "block_size": base.block_size, "num_blocks": base.num_blocks,
                    "mean_context": float(inp.context_lens.mean()),
-                   "step": "pa_reshape_and_cache + pa_multi_query"},
+                   "step": "pa_reshape_and_cache + " + ("pa_multi_query_split" if split else "pa_multi_query"),
+                   "partition_size": P if split else None},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes, "attention_ms_avg": round(att_avg, 5),

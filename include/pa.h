@@ -213,6 +213,47 @@ int pa_multi_query_fp8(void* out, const void* query, const uint8_t* key_cache, c
                        float k_scale, float v_scale, int32_t dtype, float* lse_out, void* stream);
 
 /*
+ * pa_multi_query_split_workspace_bytes - workspace pa_multi_query_split needs:
+ * float32 partials [num_tokens, num_heads, slots, head_size], then float32
+ * log-sum-exps [num_tokens, num_heads, slots], each 256-byte aligned, with
+ * slots = ceil(max_context_len / partition_size). Returns 0 for invalid
+ * arguments.
+ */
+size_t pa_multi_query_split_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_size,
+                                            int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_multi_query_split - the same result as pa_multi_query, with every
+ * context cut into partitions of partition_size tokens (P) merged by the
+ * log-sum-exp rule of pa_merge_partitions: each tile of new tokens (see
+ * pa_multi_query) is one workgroup per (tile, partition, kv head), so long
+ * contexts no longer set the time of a step that has few tiles. Partition p
+ * of a tile covers keys [p*P, (p+1)*P); each of its columns sees those below
+ * its own causal limit, and writes its normalised output and log-sum-exp to
+ * slot p of its (token, head) row in the workspace. A second kernel on the
+ * same stream merges, for the token at position x of its sequence, slots
+ * 0 .. ceil(min(x + 1, C) / P) - 1 into out (C = slots * P, also capped by the
+ * block table: positions past it are ignored); rows of tokens that belong
+ * to no sequence get zeros and a log-sum-exp of -inf. The merge rests on the same
+ * softmax normaliser identity as pa_decode_split (stanleyjacob.dev "vLLM",
+ * Part V "The attention backend dispatch layer").
+ *
+ *   max_context_len   host-side upper bound of context_lens (sizes the grid
+ *                     and the workspace without reading the lengths back).
+ *   partition_size    P: multiple of block_size, > 0.
+ *   workspace         device memory of at least
+ *                     pa_multi_query_split_workspace_bytes(...) bytes,
+ *                     256-byte aligned, owned by the caller.
+ * Other arguments as pa_multi_query. Returns PA_OK or an error status.
+ */
+int pa_multi_query_split(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
+                         float scale, int32_t dtype, int32_t max_context_len, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, float* lse_out, void* stream);
+
+/*
  * pa_decode_prefix_workspace_bytes - workspace pa_decode_prefix needs: float32
  * [num_seqs, num_heads, head_size] outputs and float32 [num_seqs, num_heads]
  * log-sum-exps of the prefix pass, each at a 256-byte aligned offset.

@@ -22,7 +22,8 @@ __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library", "prepared",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
     "pa_reshape_and_decode",
-    "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
+    "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes", "pa_multi_query_split",
+    "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
     "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles", "pa_decode_split_part_tokens",
     "pa_merge_partitions", "pa_status_string",
 ]
@@ -87,6 +88,11 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_prefix.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64, c_i32,
                                      c_f, c_i32, c_i32, c_p, c_sz, c_p, c_p, c_p]
     lib.pa_decode_prefix.restype = c_int
+    lib.pa_multi_query_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
+    lib.pa_multi_query_split_workspace_bytes.restype = c_sz
+    lib.pa_multi_query_split.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                         c_i64, c_i32, c_f, c_i32, c_i32, c_i32, c_p, c_sz, c_p, c_p]
+    lib.pa_multi_query_split.restype = c_int
     lib.pa_decode_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_split_workspace_bytes.restype = c_sz
     lib.pa_decode_split.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
@@ -315,6 +321,27 @@ def pa_multi_query_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
     lib = load_library()
     _invoke(lib.pa_multi_query_fp8, "pa_multi_query_fp8", *ptrs, float(scale), float(k_scale), float(v_scale),
             _dtype_code(query), lse_ptr, _stream(stream))
+
+
+def pa_multi_query_split_workspace_bytes(num_tokens: int, num_heads: int, head_size: int, max_context_len: int,
+                                         partition_size: int) -> int:
+    return int(load_library().pa_multi_query_split_workspace_bytes(num_tokens, num_heads, head_size,
+                                                                   max_context_len, partition_size))
+
+
+def pa_multi_query_split(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                         scale: float, max_context_len: int, partition_size: int, workspace: torch.Tensor,
+                         lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """pa_multi_query with every context cut into partition_size-token partitions and merged by
+    log-sum-exp; ``workspace`` is a uint8 GPU tensor of pa_multi_query_split_workspace_bytes bytes."""
+    ptrs, lse_ptr = _multi_common(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                                  lse_out)
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _invoke(lib.pa_multi_query_split, "pa_multi_query_split", *ptrs, float(scale), _dtype_code(query),
+            int(max_context_len), int(partition_size), ws, nbytes, lse_ptr, _stream(stream))
 
 
 def pa_decode_uses_tiles(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int, dtype: int = PA_DTYPE_BF16,

@@ -108,6 +108,12 @@ struct MultiArgs {
   int32_t num_parts;
   int32_t parts_stride;
   int32_t part_cap;  // keys at or past this position are ignored
+  // Multi-query mode cut into context partitions (part_blocks > 0 with
+  // query_start_loc): slot p * tile_slots + j is partition p of tile slot
+  // (j - p) mod tile_slots; each column sees the partition's keys below its
+  // own limit, and its normalised output and log-sum-exp go to part_o /
+  // part_lse row (token row * num_heads + head) * parts_stride + p.
+  int32_t tile_slots;
 };
 
 // Tile slots: sequence i owns slots [B_i, B_{i+1}) with
@@ -398,11 +404,19 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
       q1 = seq + 1;
       r = 0;
     } else {
-      seq = __builtin_amdgcn_readfirstlane(slot_owner(a, slot, lane));
+      int tslot = slot;
+      if (a.part_blocks > 0) {
+        part = slot / a.tile_slots;
+        const int j = slot - part * a.tile_slots;
+        const int rot = part % a.tile_slots;
+        tslot = j >= rot ? j - rot : j - rot + a.tile_slots;
+        blk_begin = part * a.part_blocks;
+      }
+      seq = __builtin_amdgcn_readfirstlane(slot_owner(a, tslot, lane));
       if (seq >= a.num_seqs) return;
       q0 = clamp_loc(a.query_start_loc[seq], a.num_tokens);
       q1 = clamp_loc(a.query_start_loc[seq + 1], a.num_tokens);
-      r = slot - (q0 / a.tile_tokens + seq);
+      r = tslot - (q0 / a.tile_tokens + seq);
     }
     const int ql = q1 - q0;
     if (ql <= 0) return;
@@ -422,13 +436,13 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
       lim[p] = c < ntok * g ? pos0 + c / g + 1 : 0;
     }
     if (part >= 0) {
-      // The partition's keys are all visible to the sequence's one query.
+      // Keys of the partition, each column up to its own limit.
       key_end = min(key_end, a.part_cap);
       if (key_end <= blk_begin * kBlockTokens) return;
       key_end = min(key_end, (blk_begin + a.part_blocks) * kBlockTokens);
-      min_lim = key_end;
+      min_lim = min(min_lim, key_end);
 #pragma unroll
-      for (int p = 0; p < NT; ++p) lim[p] = lim[p] > 0 ? key_end : 0;
+      for (int p = 0; p < NT; ++p) lim[p] = lim[p] > 0 ? min(lim[p], key_end) : 0;
     }
   }
   const int ncols = ntok * g;
@@ -895,6 +909,105 @@ int pa::launch_split_tiles(const void* query, const void* key_cache, const void*
   a.part_cap = part_cap;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+namespace {
+
+// Workspace of pa_multi_query_split: float32 partials [num_tokens, num_heads,
+// slots, head_size] then float32 log-sum-exps [num_tokens, num_heads, slots],
+// each 256-byte aligned; slots = ceil(max_context_len / partition_size).
+struct MqSplitLayout {
+  int64_t slots = 0;
+  size_t lse_off = 0, total = 0;
+};
+
+bool mq_split_layout(int64_t num_tokens, int64_t num_heads, int64_t head_size, int64_t max_context_len,
+                     int64_t partition_size, MqSplitLayout& L) {
+  if (num_tokens < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0 || partition_size <= 0) return false;
+  L.slots = (max_context_len + partition_size - 1) / partition_size;
+  if (L.slots < 1) L.slots = 1;
+  const size_t rows = static_cast<size_t>(num_tokens) * static_cast<size_t>(num_heads) * static_cast<size_t>(L.slots);
+  auto a256 = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  L.lse_off = a256(rows * static_cast<size_t>(head_size) * sizeof(float));
+  L.total = L.lse_off + a256(rows * sizeof(float));
+  return L.slots <= INT32_MAX;
+}
+
+}  // namespace
+
+extern "C" size_t pa_multi_query_split_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t head_size,
+                                                       int32_t max_context_len, int32_t partition_size) {
+  MqSplitLayout L;
+  return mq_split_layout(num_tokens, num_heads, head_size, max_context_len, partition_size, L) ? L.total : 0;
+}
+
+extern "C" int pa_multi_query_split(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                                    int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                    int64_t num_blocks, int32_t block_size, float scale, int32_t dtype,
+                                    int32_t max_context_len, int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, float* lse_out, void* stream) {
+  int st = check_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_tokens, num_heads, num_kv_heads, head_size, num_blocks, block_size, scale, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % kBlockTokens != 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!query_start_loc) return PA_ERR_INVALID_ARG;
+  MqSplitLayout L;
+  if (!mq_split_layout(num_tokens, num_heads, head_size, max_context_len, partition_size, L))
+    return PA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return PA_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_off);
+  const int num_parts = static_cast<int>(L.slots);
+  const int64_t cap = min(static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens,
+                          static_cast<int64_t>(partition_size) * num_parts);
+  if (cap > INT32_MAX) return PA_ERR_UNSUPPORTED;
+
+  const int g = num_heads / num_kv_heads;
+  int NT = pick_tiles(num_tokens, num_seqs, g);
+  NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
+  MultiArgs a{};
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = g;
+  a.tile_tokens = 16 * NT / g;
+  const int64_t tile_slots = static_cast<int64_t>(num_tokens) / a.tile_tokens + num_seqs;
+  const int64_t slots = tile_slots * num_parts;
+  const int64_t grid = (slots + 7) / 8 * 8 * num_kv_heads;
+  if (tile_slots > INT32_MAX || grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  const int64_t per_seq = (static_cast<int64_t>(num_tokens) + static_cast<int64_t>(num_seqs) * a.tile_tokens - 1) /
+                          (static_cast<int64_t>(num_seqs) * a.tile_tokens);
+  int W = pick_waves(static_cast<int64_t>(num_seqs) * per_seq * num_parts * num_kv_heads);
+  MultiKernel k = pick_multi(dtype, head_size, NT, false, W);
+  a.num_slots = static_cast<int32_t>(slots);
+  a.tile_slots = static_cast<int32_t>(tile_slots);
+  a.scale_log2 = scale * kLog2e;
+  a.v_scale = 1.0f;
+  a.part_o = o_parts;
+  a.part_lse = lse_parts;
+  a.part_blocks = partition_size / kBlockTokens;
+  a.num_parts = num_parts;
+  a.parts_stride = num_parts;
+  a.part_cap = static_cast<int32_t>(cap);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  return launch_merge_mq_parts(out, lse_out, o_parts, lse_parts, query_start_loc, context_lens, num_seqs,
+                               num_tokens, num_heads, static_cast<int>(cap), max_blocks_per_seq, partition_size,
+                               num_parts, head_size, dtype, s);
 }
 
 int pa::launch_decode_multi(void* out, const void* query, const void* key_cache, const void* value_cache,

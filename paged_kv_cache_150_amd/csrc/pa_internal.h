@@ -45,6 +45,16 @@ int launch_split_tiles(const void* query, const void* key_cache, const void* val
                        int32_t part_cap, int32_t parts_stride, float* o_parts, float* lse_parts,
                        hipStream_t stream);
 
+// Merge of pa_multi_query_split: output row (token t, head h) combines the
+// partitions 0 .. ceil(min(position(t) + 1, cap) / partition_size) - 1 of
+// its row in o_parts / lse_parts ([num_tokens, num_heads, num_parts(, D)]);
+// position(t) follows from query_start_loc and context_lens. Arguments are
+// validated by the caller.
+int launch_merge_mq_parts(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
+                          const int32_t* query_start_loc, const int32_t* context_lens, int num_seqs,
+                          int num_tokens, int num_heads, int cap, int max_blocks, int partition_size,
+                          int num_parts, int head_size, int dtype, hipStream_t stream);
+
 // Compute units of the current device (256 when it cannot be queried).
 int device_cus();
 

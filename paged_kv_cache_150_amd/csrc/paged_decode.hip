@@ -849,6 +849,41 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(T* __restrict__ out, f
                   lse_parts + row * slots, np, lane);
 }
 
+// Merge of the multi-query partitions: one wave per (token, head) row. The
+// token's sequence is found by binary search over query_start_loc; the token
+// at position n - q + j of its sequence sees keys below that position + 1,
+// i.e. the first ceil(min(position + 1, cap) / P) partitions.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_mq_parts_kernel(T* __restrict__ out, float* __restrict__ lse_out,
+                                                             const float* __restrict__ o_parts,
+                                                             const float* __restrict__ lse_parts,
+                                                             const int32_t* __restrict__ loc,
+                                                             const int32_t* __restrict__ context_lens, int num_seqs,
+                                                             int num_tokens, int num_heads, int cap, int max_tokens,
+                                                             int part_tokens, int num_parts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= static_cast<int64_t>(num_tokens) * num_heads) return;
+  const int t = static_cast<int>(row / num_heads);
+  auto cl = [&](int v) { return v < 0 ? 0 : (v > num_tokens ? num_tokens : v); };
+  int lo = 0, hi = num_seqs;  // largest seq with loc[seq] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cl(loc[mid]) <= t) lo = mid; else hi = mid;
+  }
+  const int q0 = cl(loc[lo]), q1 = cl(loc[lo + 1]);
+  int np = 0;
+  if (t >= q0 && t < q1) {
+    int n = context_lens[lo];
+    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+    int lim = n - (q1 - q0) + (t - q0) + 1;
+    lim = lim < 0 ? 0 : (lim > cap ? cap : lim);
+    np = min((lim + part_tokens - 1) / part_tokens, num_parts);
+  }
+  merge_row<T, D>(out + row * D, lse_out != nullptr ? lse_out + row : nullptr, o_parts + row * num_parts * D,
+                  lse_parts + row * num_parts, np, lane);
+}
+
 // ------------------------------------------------------------------ host side
 namespace {
 
@@ -1146,10 +1181,32 @@ int split_part_tokens(int num_seqs, int num_kv_heads, int max_context_len, int P
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-
-
-
 }  // namespace
+
+int launch_merge_mq_parts(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
+                              const int32_t* query_start_loc, const int32_t* context_lens, int num_seqs,
+                              int num_tokens, int num_heads, int cap, int max_blocks, int partition_size,
+                              int num_parts, int head_size, int dtype, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_tokens) * num_heads;
+  if (rows <= 0) return PA_OK;
+  constexpr int kRowsPerBlock = 4;
+  const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int max_tokens = max_blocks * kBlockTokens;
+  dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
+#define PA_MERGE_MQ(TT, DD)                                                                                      \
+  hipLaunchKernelGGL((merge_mq_parts_kernel<TT, DD>), g, b, 0, stream, static_cast<TT*>(out), lse_out, o_parts,  \
+                     lse_parts, query_start_loc, context_lens, num_seqs, num_tokens, num_heads, cap, max_tokens,  \
+                     partition_size, num_parts)
+  if (dtype == PA_DTYPE_BF16) {
+    if (head_size == 128) PA_MERGE_MQ(bf16_t, 128); else PA_MERGE_MQ(bf16_t, 64);
+  } else {
+    if (head_size == 128) PA_MERGE_MQ(float, 128); else PA_MERGE_MQ(float, 64);
+  }
+#undef PA_MERGE_MQ
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace pa
 
 using namespace pa;

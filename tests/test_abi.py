@@ -32,7 +32,8 @@ def test_headers_declare_the_boundary():
     inc = os.path.join(ROOT, "include")
     assert declared_functions(os.path.join(inc, "pa.h")) == sorted([
         "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
-        "pa_reshape_and_decode", "pa_multi_query", "pa_multi_query_fp8", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
+        "pa_reshape_and_decode", "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes",
+        "pa_multi_query_split", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",
         "pa_decode_uses_tiles", "pa_decode_split_part_tokens"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
@@ -195,3 +196,23 @@ def test_split_cut_choice(lib, monkeypatch):
     assert f(64, 32, 8, 2048, 512) == 0
     monkeypatch.setenv("PA_SPLIT_KERNEL", "tiles")
     assert f(8, 32, 8, 32768, 512) == 1024 and f(256, 64, 2, 4096, 512) == 0   # k = 8 * 64 * 8 // 1536
+
+
+def test_multi_query_split_host_validation(lib):
+    """Workspace sizing and the host checks of pa_multi_query_split (no GPU work)."""
+    f = lib.pa_multi_query_split_workspace_bytes
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    rows = 10 * 8 * 4                                 # tokens, heads, ceil(2000 / 512) slots
+    assert f(10, 8, 128, 2000, 512) == a256(rows * 128 * 4) + a256(rows * 4)
+    assert f(10, 8, 128, 0, 512) == a256(10 * 8 * 128 * 4) + a256(10 * 8 * 4)   # at least one slot
+    assert f(10, 0, 128, 2000, 512) == 0 and f(10, 8, 128, 2000, 0) == 0 and f(-1, 8, 128, 2000, 512) == 0
+    g = lib.pa_multi_query_split
+    c = ctypes.c_float
+    ok = [16, 16, 16, 16, 16, 4, 16, 16]            # out, query, caches, tables, max_blocks, lens, starts
+    shape = [8, 2, 128, 10, 16]                      # H_q, H_kv, head_size, num_blocks, block_size
+    assert g(*ok, 0, 5, *shape, c(0.1), 1, 64, 16, 256, 1 << 20, None, None) == 0    # no sequences
+    assert g(*ok, 3, 5, *shape, c(0.1), 1, 64, 24, 256, 1 << 20, None, None) == 1    # P not a block multiple
+    assert g(*ok, 3, 5, *shape, c(0.1), 1, 64, 16, None, 1 << 20, None, None) == 1   # no workspace
+    assert g(*ok, 3, 5, *shape, c(0.1), 1, 64, 16, 264, 1 << 20, None, None) == 1    # misaligned workspace
+    assert g(*ok, 3, 5, *shape, c(0.1), 1, 64, 16, 256, 16, None, None) == 3         # workspace too small
+    assert g(*ok[:7], None, 3, 5, *shape, c(0.1), 1, 64, 16, 256, 1 << 20, None, None) == 1  # no query_start_loc

@@ -423,6 +423,10 @@ MQ_CONFIGS: list[MultiQueryConfig] = [
         name="llama3_8b_b256_chunk1024", base=CONFIG_BY_NAME["llama3_8b_b256"], new_tokens=("chunk", 1, 1024, 2048),
         description="The batch-256 decode step with one sequence running a 1024-token prompt chunk "
                     "(tokens 1024..2047 of its prompt) in the same pass"),
+    MultiQueryConfig(
+        name="long_split_spec4", base=CONFIG_BY_NAME["long_split"], new_tokens=("fixed", 5),
+        description="Speculative verify on the long-context batch: 8 sequences, ctx U{16k..32k}, "
+                    "5 new positions each (few tiles over long contexts)"),
 ]
 
 MQ_CONFIG_BY_NAME = {c.name: c for c in MQ_CONFIGS}
