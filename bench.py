@@ -185,8 +185,9 @@ def bench_multi_query(args):
     split = args.decode == "split"
     if split:
         # Every context cut into P-token partitions, then the per-row merge.
-        P = args.partition_size or 2048
         max_ctx = int(inp.context_lens.max(initial=0))
+        P = (args.partition_size or pa.pa_multi_query_split_partition_size(
+            base.num_seqs, mq.num_tokens, base.num_heads, base.num_kv_heads, base.head_size, max_ctx) or 1024)
         ws = torch.empty(pa.pa_multi_query_split_workspace_bytes(mq.num_tokens, base.num_heads, base.head_size,
                                                                  max_ctx, P), dtype=torch.uint8, device=dev)
         attend_p = [pa.prepared(pa.pa_multi_query_split, out, q, *pools[k], bt, cl, loc, base.scale, max_ctx, P, ws,

@@ -223,6 +223,18 @@ size_t pa_multi_query_split_workspace_bytes(int32_t num_tokens, int32_t num_head
                                             int32_t max_context_len, int32_t partition_size);
 
 /*
+ * pa_multi_query_split_partition_size - partition length (tokens, a multiple
+ * of 256) for pa_multi_query_split on this device, or 0 when the plain
+ * pa_multi_query should be used: the step's tiles already give at least one
+ * workgroup per compute unit, or the longest context is not longer than one
+ * partition would be. Cuts to about six workgroups per compute unit
+ * otherwise. Shape arguments as pa_multi_query; returns 0 for invalid ones.
+ */
+int32_t pa_multi_query_split_partition_size(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_size, int32_t dtype,
+                                            int32_t max_context_len);
+
+/*
  * pa_multi_query_split - the same result as pa_multi_query, with every
  * context cut into partitions of partition_size tokens (P) merged by the
  * log-sum-exp rule of pa_merge_partitions: each tile of new tokens (see

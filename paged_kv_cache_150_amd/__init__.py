@@ -23,6 +23,7 @@ __all__ = [
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
     "pa_reshape_and_decode",
     "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes", "pa_multi_query_split",
+    "pa_multi_query_split_partition_size",
     "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
     "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles", "pa_decode_split_part_tokens",
     "pa_merge_partitions", "pa_status_string",
@@ -90,6 +91,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_prefix.restype = c_int
     lib.pa_multi_query_split_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_multi_query_split_workspace_bytes.restype = c_sz
+    lib.pa_multi_query_split_partition_size.argtypes = [c_i32] * 7
+    lib.pa_multi_query_split_partition_size.restype = c_i32
     lib.pa_multi_query_split.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          c_i64, c_i32, c_f, c_i32, c_i32, c_i32, c_p, c_sz, c_p, c_p]
     lib.pa_multi_query_split.restype = c_int
@@ -327,6 +330,13 @@ def pa_multi_query_split_workspace_bytes(num_tokens: int, num_heads: int, head_s
                                          partition_size: int) -> int:
     return int(load_library().pa_multi_query_split_workspace_bytes(num_tokens, num_heads, head_size,
                                                                    max_context_len, partition_size))
+
+
+def pa_multi_query_split_partition_size(num_seqs: int, num_tokens: int, num_heads: int, num_kv_heads: int,
+                                        head_size: int, max_context_len: int, dtype: int = PA_DTYPE_BF16) -> int:
+    """Partition length for pa_multi_query_split, or 0 when pa_multi_query fills the GPU by itself."""
+    return int(load_library().pa_multi_query_split_partition_size(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                                                  head_size, dtype, max_context_len))
 
 
 def pa_multi_query_split(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,

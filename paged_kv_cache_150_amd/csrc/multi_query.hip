@@ -941,6 +941,31 @@ extern "C" size_t pa_multi_query_split_workspace_bytes(int32_t num_tokens, int32
   return mq_split_layout(num_tokens, num_heads, head_size, max_context_len, partition_size, L) ? L.total : 0;
 }
 
+// One round of the plain launch has at most tile_slots * H_kv workgroups,
+// each over a whole context. When that is fewer than the compute units, the
+// contexts are cut so that about three rounds of two resident workgroups per
+// compute unit remain (as for the decode partition cut), in multiples of
+// 256 tokens so that each partition still streams long enough.
+extern "C" int32_t pa_multi_query_split_partition_size(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                                       int32_t num_kv_heads, int32_t head_size, int32_t dtype,
+                                                       int32_t max_context_len) {
+  if (num_seqs <= 0 || num_tokens <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      max_context_len <= 0 || (head_size != 64 && head_size != 128))
+    return 0;
+  const int g = num_heads / num_kv_heads;
+  if (g > 16) return 0;
+  int NT = pick_tiles(num_tokens, num_seqs, g);
+  NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
+  const int64_t tile_tokens = 16 * NT / g;
+  const int64_t jobs = (static_cast<int64_t>(num_tokens) / tile_tokens + num_seqs) * num_kv_heads;
+  const int64_t cus = device_cus();
+  if (jobs >= cus) return 0;
+  const int64_t parts = (3 * 2 * cus + jobs - 1) / jobs;
+  int64_t P = (static_cast<int64_t>(max_context_len) + parts - 1) / parts;
+  P = (P + 255) / 256 * 256;
+  return P >= max_context_len ? 0 : static_cast<int32_t>(P);
+}
+
 extern "C" int pa_multi_query_split(void* out, const void* query, const void* key_cache, const void* value_cache,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                                     const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,

@@ -33,7 +33,8 @@ def test_headers_declare_the_boundary():
     assert declared_functions(os.path.join(inc, "pa.h")) == sorted([
         "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
         "pa_reshape_and_decode", "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes",
-        "pa_multi_query_split", "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
+        "pa_multi_query_split", "pa_multi_query_split_partition_size", "pa_decode_prefix_workspace_bytes",
+        "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",
         "pa_decode_uses_tiles", "pa_decode_split_part_tokens"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
@@ -216,3 +217,17 @@ def test_multi_query_split_host_validation(lib):
     assert g(*ok, 3, 5, *shape, c(0.1), 1, 64, 16, 264, 1 << 20, None, None) == 1    # misaligned workspace
     assert g(*ok, 3, 5, *shape, c(0.1), 1, 64, 16, 256, 16, None, None) == 3         # workspace too small
     assert g(*ok[:7], None, 3, 5, *shape, c(0.1), 1, 64, 16, 256, 1 << 20, None, None) == 1  # no query_start_loc
+
+
+def test_multi_query_split_partition_choice(lib):
+    """Without a GPU the library assumes 256 compute units: a step whose tiles
+    give fewer workgroups than that is cut to about 6 * 256 workgroups."""
+    f = lib.pa_multi_query_split_partition_size
+    # 8 long sequences, 5 verify positions: 32-column tiles of 8 tokens,
+    # (40 / 8 + 8) * 8 = 104 jobs -> ceil(1536 / 104) = 15 parts of 32768.
+    assert f(8, 40, 32, 8, 128, 1, 32768) == 2304
+    assert f(64, 320, 32, 8, 128, 1, 2048) == 0       # batch 64 fills the GPU already
+    assert f(256, 1279, 32, 8, 128, 1, 4096) == 0
+    assert f(8, 40, 32, 8, 128, 1, 2000) == 256       # at least 256 tokens per partition
+    assert f(8, 40, 32, 8, 128, 1, 200) == 0          # one partition would hold the longest context
+    assert f(0, 40, 32, 8, 128, 1, 32768) == 0 and f(8, 40, 32, 8, 96, 1, 32768) == 0
