@@ -887,6 +887,18 @@ __global__ __launch_bounds__(256) void merge_mq_parts_kernel(T* __restrict__ out
 // ------------------------------------------------------------------ host side
 namespace {
 
+// Rows (one wave each) per workgroup of the merge kernels: one for merges of
+// up to eight rows per compute unit, so that a small merge (a few hundred to
+// a few thousand rows of long partial lists) spreads its loads over every
+// compute unit instead of a quarter of them. PA_MERGE_ROWS=1|2|4 overrides.
+int merge_rows_per_block(int64_t rows) {
+  if (const char* e = getenv("PA_MERGE_ROWS")) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4) return v;
+  }
+  return rows <= 8 * static_cast<int64_t>(device_cus()) ? 1 : 4;
+}
+
 // Blocks per chunk (CB) and one-chunk register lookahead (PF), chosen per
 // shape so a wave fits in 256 VGPRs without spilling (2 waves per SIMD).
 template <typename T, int D, int G, bool F8 = false>
@@ -1078,7 +1090,7 @@ int launch_split(const SplitArgs& args, int dtype, int head_size, hipStream_t st
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(threads), lds, stream, args);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   const int64_t rows = static_cast<int64_t>(args.num_seqs) * args.num_heads;
-  constexpr int kRowsPerBlock = 4;
+  const int kRowsPerBlock = merge_rows_per_block(rows);
   const int64_t mgrid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (mgrid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   dim3 g(static_cast<unsigned>(mgrid)), b(kRowsPerBlock * kWave);
@@ -1098,7 +1110,7 @@ int launch_split(const SplitArgs& args, int dtype, int head_size, hipStream_t st
 int launch_merge(void* out, float* lse_out, const float* o_parts, const float* lse_parts, int64_t rows,
                  int num_parts, int head_size, int dtype, hipStream_t stream) {
   if (rows <= 0) return PA_OK;
-  constexpr int kRowsPerBlock = 4;
+  const int kRowsPerBlock = merge_rows_per_block(rows);
   const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
@@ -1125,7 +1137,7 @@ int launch_merge_parts(void* out, float* lse_out, const float* o_parts, const fl
                        int num_parts, int slots, int head_size, int dtype, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
   if (rows <= 0) return PA_OK;
-  constexpr int kRowsPerBlock = 4;
+  const int kRowsPerBlock = merge_rows_per_block(rows);
   const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   dim3 g(static_cast<unsigned>(grid)), b(kRowsPerBlock * kWave);
@@ -1189,7 +1201,7 @@ int launch_merge_mq_parts(void* out, float* lse_out, const float* o_parts, const
                               int num_parts, int head_size, int dtype, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(num_tokens) * num_heads;
   if (rows <= 0) return PA_OK;
-  constexpr int kRowsPerBlock = 4;
+  const int kRowsPerBlock = merge_rows_per_block(rows);
   const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (grid > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const int max_tokens = max_blocks * kBlockTokens;

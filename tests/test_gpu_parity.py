@@ -403,10 +403,12 @@ def test_empty_contexts(pa):
         assert max_err(o, ref) <= 1e-5 and max_err(l, ref_lse) <= 1e-5
 
 
+@pytest.mark.parametrize("rows", ["1", "2", "4"])
 @pytest.mark.parametrize("P", [9, 40, 70, 130])
-def test_merge_partitions_alone(pa, P):
+def test_merge_partitions_alone(pa, monkeypatch, P, rows):
     """One batch of partials (9), two (40), the lane-strided log-sum-exps past
-    64 (70, 130)."""
+    64 (70, 130); 30 rows (a ragged last workgroup at 4 rows each)."""
+    monkeypatch.setenv("PA_MERGE_ROWS", rows)
     rng = np.random.default_rng(17)
     S, H, dh = 5, 6, 128
     o = rng.standard_normal((S, H, P, dh)).astype(np.float32)
