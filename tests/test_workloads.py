@@ -94,3 +94,24 @@ def test_algorithmic_bytes():
     cfg = W.CONFIG_BY_NAME["llama3_8b_b256"]
     n = np.array([1000, 10], np.int32)
     assert W.algorithmic_kv_bytes(cfg, n) == 1010 * 4096
+
+
+@pytest.mark.parametrize("name", [c.name for c in W.MQ_CONFIGS])
+def test_multi_query_lengths(name):
+    """Each multi-query workload's lengths: every sequence has at least one new
+    token and at least as many stored keys, the contexts fit the block tables
+    and the pool, and the step has the new-token count its description gives."""
+    cfg = W.MQ_CONFIG_BY_NAME[name]
+    base = cfg.base
+    n, q = W.multi_lengths(cfg)
+    assert n.shape == q.shape == (base.num_seqs,)
+    assert (q >= 1).all() and (n >= q).all()
+    bs = base.block_size
+    assert int(np.ceil(n / bs).sum()) <= base.num_blocks
+    kind = cfg.new_tokens[0]
+    if kind == "fixed":
+        assert (q == cfg.new_tokens[1]).all()
+    else:
+        _, m, c, ctx = cfg.new_tokens
+        assert (q[:m] == c).all() and (n[:m] == ctx).all() and (q[m:] == 1).all()
+    np.testing.assert_array_equal(W.multi_lengths(cfg)[0], n)   # deterministic

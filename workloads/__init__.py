@@ -453,13 +453,10 @@ class MultiQueryInputs:
         return int(self.query_start_loc[-1])
 
 
-def make_multi_inputs(cfg: MultiQueryConfig, mode: str = "parity", seed: int | None = None,
-                      context_lens: np.ndarray | None = None, query_lens: np.ndarray | None = None
-                      ) -> MultiQueryInputs:
-    """Draw one multi-query step: the base workload's inputs (make_inputs, same
-    draws) with the lengths adjusted as ``new_tokens`` says, then the new
-    tokens' queries from a second stream. ``context_lens``/``query_lens``
-    override the lengths."""
+def multi_lengths(cfg: MultiQueryConfig, seed: int | None = None, context_lens: np.ndarray | None = None,
+                  query_lens: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Context lengths n (new tokens included) and new-token counts q of one
+    multi-query step, as ``new_tokens`` says (or as given)."""
     base = cfg.base
     s = base.seed if seed is None else seed
     n = draw_context_lens(base, s) if context_lens is None else np.asarray(context_lens, np.int32).copy()
@@ -478,6 +475,20 @@ def make_multi_inputs(cfg: MultiQueryConfig, mode: str = "parity", seed: int | N
             n[:m] = ctx
     else:
         raise ValueError(kind)
+    return n, q
+
+
+def make_multi_inputs(cfg: MultiQueryConfig, mode: str = "parity", seed: int | None = None,
+                      context_lens: np.ndarray | None = None, query_lens: np.ndarray | None = None
+                      ) -> MultiQueryInputs:
+    """Draw one multi-query step: the base workload's inputs (make_inputs, same
+    draws) with the lengths adjusted as ``new_tokens`` says, then the new
+    tokens' queries from a second stream. ``context_lens``/``query_lens``
+    override the lengths."""
+    base = cfg.base
+    s = base.seed if seed is None else seed
+    n, q = multi_lengths(cfg, s, context_lens, query_lens)
+    S = n.shape[0]
     inp = make_inputs(base, mode, seed=s, context_lens=n)
     loc = np.concatenate([[0], np.cumsum(q, dtype=np.int64)]).astype(np.int32)
     T = int(loc[-1])
