@@ -352,7 +352,10 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   const int g = a.group;
 
   int slot, kvh;
-  slot_and_head(blockIdx.x, a.num_kv_heads, slot, kvh);
+  if (a.query_start_loc != nullptr && a.part_blocks == 0 && a.prefix_keys == 0)
+    slot_and_head_phased(blockIdx.x, gridDim.x, a.num_kv_heads, slot, kvh);
+  else
+    slot_and_head(blockIdx.x, a.num_kv_heads, slot, kvh);
   if (slot >= a.num_slots) return;
   const int max_tokens = a.max_blocks * kBlockTokens;
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > max_tokens ? max_tokens : v); };

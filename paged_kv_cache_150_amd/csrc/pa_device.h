@@ -182,4 +182,28 @@ __device__ __forceinline__ void slot_and_head(int id, int num_kv_heads, int& slo
   slot = group * 8 + xcd;
 }
 
+// Workgroup id -> (slot, kv head) for launches whose consecutive slots share
+// keys (several tiles of new tokens of one sequence). Each XCD walks its slots
+// in phases of kPhase slot groups: within a phase it serves one kv head for
+// all the phase's slots before the next head, so the tiles that re-read a
+// sequence's keys of one head run on one XCD close together and find them in
+// its L2, instead of every XCD holding every head. Heads are rotated by XCD
+// and by phase so that no XCD keeps the slower heads. `grid` must be
+// ceil(slots / 8) * 8 * num_kv_heads; the map is a bijection onto
+// [0, grid / num_kv_heads) x [0, num_kv_heads).
+__device__ __forceinline__ void slot_and_head_phased(int id, int grid, int num_kv_heads, int& slot, int& kvh) {
+  constexpr int kPhase = 32;
+  const int xcd = id & 7;
+  const int k = id >> 3;
+  const int groups = (grid >> 3) / num_kv_heads;  // slot groups of 8 (one slot per XCD)
+  const int span = kPhase * num_kv_heads;
+  const int phase = k / span;
+  const int full = groups / kPhase;
+  const int f = phase < full ? kPhase : groups - full * kPhase;  // groups in this phase
+  const int r = k - phase * span;
+  const int h = r / f;
+  kvh = (h + xcd + phase) % num_kv_heads;
+  slot = (phase * kPhase + (r - h * f)) * 8 + xcd;
+}
+
 }  // namespace pa
