@@ -500,9 +500,7 @@ def main():
     launch_ms = ms_per_step if one_launch else dec_avg
     dec_gbs = roof_bytes / (launch_ms * 1e-3) / 1e9
     traffic = stored_traffic(cfg.name, args.decode + ("_separate" if args.separate_write else ""))
-    tiles = one_launch or pa.pa_decode_uses_tiles(S, Hq, cfg.num_kv_heads, d, pa.PA_DTYPE_BF16
-                                                  if cfg.dtype == "bf16" else pa.PA_DTYPE_F32, fp8)
-    one = "paged_multi_query_kernel (one token per sequence)" if tiles else "paged_decode_kernel (persistent)"
+    one = "paged_multi_query_kernel (one token per sequence)"
     if one_launch:
         one += " with the new-token write"
     split_label = "paged_decode_split_kernel + merge_pieces_kernel"

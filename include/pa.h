@@ -98,7 +98,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
  * FP8 KV caches.
  *
  * The pages name an FP8 KV cache as a way to enlarge the pool (llm-stack-book
- * 7.3, "Running vLLM well in practice", item 5) without fixing a format. This
+ * 7.3, "The knobs that actually matter", item 5) without fixing a format. This
  * library's reading: caches hold OCP FP8 E4M3 codes (1 sign, 4 exponent bits
  * with bias 7, 3 mantissa bits; largest finite 448; S.1111.111 is NaN; no
  * infinity), one code per element, in the same [num_blocks, block_size,
@@ -171,15 +171,11 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapp
  * softmax is evaluated online over the streamed blocks (stanleyjacob.dev
  * "vLLM", Part IV "Stage 6: The forward pass").
  *
- * Work is cut into jobs of one (sequence, kv head) each. Two kernels serve
- * them: the tile kernel (the multi-query kernel with one new token per
- * sequence: one workgroup per job, handed out by the hardware in seq_order,
- * P*V on the matrix cores; 8-wave workgroups when every resident 4-wave
- * workgroup would get at most one job, 4-wave ones otherwise), used by
- * default, and a persistent kernel (workgroups that walk jobs in a fixed
- * order), kept as the alternative (PA_DECODE_KERNEL=persistent;
- * pa_decode_uses_tiles tells which runs). Results differ between the two only
- * by rounding order.
+ * Work is cut into jobs of one (sequence, kv head): one workgroup of the tile
+ * kernel (the multi-query kernel with one new token per sequence, P*V on the
+ * matrix cores) per job, handed out by the hardware in seq_order; 8-wave
+ * workgroups when every resident 4-wave workgroup would get at most one job,
+ * 4-wave ones otherwise (PA_OPT_TILE_WAVES).
  *
  *   out               [num_seqs, num_heads, head_size], written (dtype).
  *   lse_out           optional float32 [num_seqs, num_heads]: ln sum_t exp(s_t).
@@ -313,14 +309,26 @@ int pa_decode_prefix(void* out, const void* query, const void* key_cache, const 
  * Token i is sequence i's new token: its K/V (key, value [num_seqs, H_kv,
  * head_size]) are written to slot_mapping[i] and the step's attention is
  * computed as pa_decode computes it (the forward step of llm-stack-book 7.3,
- * "The forward step in detail": scatter the new K/V, then attend). Each
- * workgroup writes its sequence's slice for its kv head with the very lanes
- * that later read that slot back, so the write needs no extra pass or fence.
+ * "The forward step in detail": scatter the new K/V, then attend).
  *
- *   slot_mapping      int64 [num_seqs]: the slot of position context_lens[i]-1
- *                     of sequence i (the usual decode step), or negative for
- *                     no write. A slot elsewhere is still written, but its
- *                     order against other sequences' reads is unspecified.
+ *   slot_mapping      int64 [num_seqs], device. Three cases per sequence i,
+ *                     with n = context_lens[i]:
+ *                     - the slot the block table gives position n - 1
+ *                       (block_tables[i][(n-1)/block_size] * block_size +
+ *                       (n-1) % block_size), the usual decode step: the row is
+ *                       written and the attention uses the new K/V at
+ *                       position n - 1. The workgroup that reads that slot
+ *                       writes it with the very lanes that hold it, so the
+ *                       write needs no extra pass or fence.
+ *                     - negative or >= num_blocks * block_size: nothing is
+ *                       written (as pa_reshape_and_cache).
+ *                     - any other slot (n = 0 included): the row is written,
+ *                       and the attention reads what the cache holds at every
+ *                       position, position n - 1 included. The result equals
+ *                       pa_reshape_and_cache followed by pa_decode only if no
+ *                       context of this step reads that slot (e.g. a free
+ *                       block); otherwise whether a reader sees the old or the
+ *                       new row is unspecified.
  * Runs on the tile kernel for every batch size. Other arguments as pa_decode
  * and pa_reshape_and_cache (same dtype for key, value, query, out and caches).
  * Returns PA_OK or an error status.
@@ -370,17 +378,6 @@ int pa_multi_query(void* out, const void* query, const void* key_cache, const vo
                    int32_t dtype, float* lse_out, void* stream);
 
 /*
- * pa_decode_uses_tiles - which kernel pa_decode / pa_decode_fp8 /
- * pa_decode_prefix would run for this shape on the current device: 1 for the
- * tile kernel (the multi-query kernel with one new token per sequence), 0 for
- * the persistent decode kernel, -1 for invalid arguments. The tile kernel
- * runs unless the environment variable PA_DECODE_KERNEL=persistent selects
- * the other. Launches nothing.
- */
-int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                         int32_t dtype, int32_t fp8_cache);
-
-/*
  * pa_decode_split_workspace_bytes - workspace pa_decode_split needs.
  *
  * slots = ceil(max_context_len / partition_size) + 1. The workspace holds, each
@@ -414,7 +411,7 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  *
  * Pieces (groups above 16; groups of at most 4 when num_seqs * H_kv is below
  * the number of resident tile workgroups, i.e. a few long contexts; or
- * PA_SPLIT_KERNEL=pieces): the kv heads are taken
+ * PA_OPT_SPLIT_CUT = 2): the kv heads are taken
  * in groups of up to 8 (one persistent workgroup has one wave per kv head of
  * its group, all walking the same blocks). Per head group, the blocks of all
  * sequences are laid end to end (sequence i has nb_i = ceil(n_i / block_size)
@@ -455,10 +452,8 @@ int pa_decode_split(void* out, const void* query, const void* key_cache, const v
  * pa_decode_split_part_tokens - the cut pa_decode_split makes for these
  * arguments on the current device: the partition length P' (a multiple of
  * partition_size) of the partition cut, 0 for the pieces cut, -1 for invalid
- * arguments. PA_SPLIT_KERNEL=pieces|tiles overrides the choice of cut (tiles
- * need H_q / H_kv <= 16) and PA_SPLIT_PART_FACTOR=k the factor P' / P (capped
- * at ceil(max_context_len / P)). Queries the device's CU count, launches
- * nothing.
+ * arguments, with the options PA_OPT_SPLIT_CUT and PA_OPT_SPLIT_PART_FACTOR
+ * as they stand. Queries the device's CU count, launches nothing.
  */
 int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                     int32_t max_context_len, int32_t partition_size);
@@ -466,7 +461,11 @@ int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t
 /*
  * pa_merge_partitions - exact log-sum-exp merge of partial attention results.
  *
- * For each (sequence, head): M = max_p lse_p, w_p = exp(lse_p - M),
+ * A softmax over a whole context can be carried piecewise as a running maximum
+ * and normaliser, so attention computed separately over pieces of a context
+ * recombines exactly (stanleyjacob.dev "vLLM", Part V "The attention backend
+ * dispatch layer": tiling plus online softmax; Part IV "Stage 6: The forward
+ * pass"). For each (sequence, head): M = max_p lse_p, w_p = exp(lse_p - M),
  *     out = sum_p w_p o_p / sum_p w_p,   lse = M + ln sum_p w_p.
  * Partitions with lse_p = -inf carry no weight and their o_p is never used
  * (it may hold anything). If all are -inf: out = 0, lse = -inf.
@@ -480,6 +479,48 @@ int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t
 int pa_merge_partitions(void* out, float* lse_out, const float* o_parts, const float* lse_parts,
                         int32_t num_seqs, int32_t num_heads, int32_t num_parts,
                         int32_t head_size, int32_t dtype, void* stream);
+
+/*
+ * Kernel-choice overrides.
+ *
+ * Every entry point picks its launch shape from the call's arguments and the
+ * device (the defaults are the measured choices). These process-wide options
+ * force one of the alternatives instead, so that tests can cover every path
+ * and measurements can compare them; each choice computes the same result up
+ * to rounding order. An option applies to calls made after it is set; which
+ * value a call made concurrently from another thread sees is unspecified.
+ *
+ *   PA_OPT_TILE_WAVES        waves per workgroup of the tile kernel (16-column
+ *                            tiles of 16-bit and FP8 caches): 0 = 8 when the
+ *                            launch has at most one job per resident 4-wave
+ *                            workgroup, else 4 (default); or 4, or 8.
+ *   PA_OPT_TILE_COLUMNS      columns per multi-query tile: 0 = 32 when the step
+ *                            averages more new tokens per sequence than a
+ *                            16-column tile holds, else 16 (default); or 16,
+ *                            or 32.
+ *   PA_OPT_SPLIT_CUT         pa_decode_split's cut: 0 = by shape (default),
+ *                            1 = partitions (groups <= 16), 2 = pieces.
+ *   PA_OPT_SPLIT_PART_FACTOR the partition cut's factor k (partitions of
+ *                            k * partition_size tokens): 0 = by grid size
+ *                            (default), or k >= 1 (capped at
+ *                            ceil(max_context_len / partition_size)).
+ *   PA_OPT_MERGE_ROWS        (sequence, head) rows per workgroup of the merge
+ *                            kernels: 0 = by row count (default), or 1, 2, 4.
+ *
+ * pa_set_option returns PA_OK, or PA_ERR_INVALID_ARG for an unknown option or
+ * a value outside its range (the option keeps its value). pa_get_option
+ * returns the value, or -1 for an unknown option.
+ */
+typedef enum pa_option {
+  PA_OPT_TILE_WAVES = 0,
+  PA_OPT_TILE_COLUMNS = 1,
+  PA_OPT_SPLIT_CUT = 2,
+  PA_OPT_SPLIT_PART_FACTOR = 3,
+  PA_OPT_MERGE_ROWS = 4
+} pa_option;
+
+int pa_set_option(int option, int value);
+int pa_get_option(int option);
 
 /* pa_status_string - static, NUL-terminated description of a status code. */
 const char* pa_status_string(int status);

@@ -2,7 +2,7 @@
 
 The pages name an FP8 KV cache only as a way to enlarge the pool
 (llm-stack-book 7.3 "vLLM: Architecture, PagedAttention & Internals",
-"Running vLLM well in practice", item 5; modernaiengineering.com lesson 13.15,
+"The knobs that actually matter", item 5; modernaiengineering.com lesson 13.15,
 "Memory efficiency") and fix no format, so this module takes its own reading,
 the plainest one:
 

@@ -25,13 +25,21 @@ __all__ = [
     "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes", "pa_multi_query_split",
     "pa_multi_query_split_partition_size",
     "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
-    "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_uses_tiles", "pa_decode_split_part_tokens",
-    "pa_merge_partitions", "pa_status_string",
+    "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_split_part_tokens",
+    "pa_merge_partitions", "pa_status_string", "pa_set_option", "pa_get_option", "options",
+    "PA_OPT_TILE_WAVES", "PA_OPT_TILE_COLUMNS", "PA_OPT_SPLIT_CUT", "PA_OPT_SPLIT_PART_FACTOR", "PA_OPT_MERGE_ROWS",
 ]
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 BLOCK_SIZE = 16
+
+# Kernel-choice options (pa_option in include/pa.h); 0 is the default choice.
+PA_OPT_TILE_WAVES = 0         # 0, 4 or 8
+PA_OPT_TILE_COLUMNS = 1       # 0, 16 or 32
+PA_OPT_SPLIT_CUT = 2          # 0, 1 (partitions) or 2 (pieces)
+PA_OPT_SPLIT_PART_FACTOR = 3  # 0 or k >= 1
+PA_OPT_MERGE_ROWS = 4         # 0, 1, 2 or 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -77,8 +85,10 @@ def load_library() -> ctypes.CDLL:
     lib.pa_reshape_and_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32,
                                           c_i32, c_i64, c_i32, c_f, c_i32, c_p, c_p, c_p]
     lib.pa_reshape_and_decode.restype = c_int
-    lib.pa_decode_uses_tiles.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]
-    lib.pa_decode_uses_tiles.restype = c_int
+    lib.pa_set_option.argtypes = [c_int, c_int]
+    lib.pa_set_option.restype = c_int
+    lib.pa_get_option.argtypes = [c_int]
+    lib.pa_get_option.restype = c_int
     lib.pa_decode_split_part_tokens.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_split_part_tokens.restype = c_i32
     lib.pa_multi_query_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -111,6 +121,38 @@ def load_library() -> ctypes.CDLL:
 
 def pa_status_string(status: int) -> str:
     return load_library().pa_status_string(int(status)).decode()
+
+
+def pa_set_option(option: int, value: int) -> None:
+    """Force a kernel choice process-wide (see pa_option in include/pa.h); 0 restores the default."""
+    _check(load_library().pa_set_option(int(option), int(value)), "pa_set_option")
+
+
+def pa_get_option(option: int) -> int:
+    v = int(load_library().pa_get_option(int(option)))
+    if v < 0:
+        raise ValueError(f"unknown option {option}")
+    return v
+
+
+class options:
+    """Context manager: ``with options({PA_OPT_SPLIT_CUT: 2}): ...`` sets the
+    given options and restores their previous values on exit."""
+
+    def __init__(self, values: dict):
+        self._values = dict(values)
+        self._saved = {}
+
+    def __enter__(self):
+        for k, v in self._values.items():
+            self._saved[k] = pa_get_option(k)
+            pa_set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self._saved.items():
+            pa_set_option(k, v)
+        return False
 
 
 # ------------------------------------------------------------------ marshalling helpers
@@ -352,15 +394,6 @@ def pa_multi_query_split(out: torch.Tensor, query: torch.Tensor, key_cache: torc
     lib = load_library()
     _invoke(lib.pa_multi_query_split, "pa_multi_query_split", *ptrs, float(scale), _dtype_code(query),
             int(max_context_len), int(partition_size), ws, nbytes, lse_ptr, _stream(stream))
-
-
-def pa_decode_uses_tiles(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int, dtype: int = PA_DTYPE_BF16,
-                         fp8_cache: bool = False) -> bool:
-    """Whether pa_decode (and the FP8 / shared-prefix variants) runs the tile kernel for this shape."""
-    r = load_library().pa_decode_uses_tiles(num_seqs, num_heads, num_kv_heads, head_size, dtype, int(fp8_cache))
-    if r < 0:
-        raise ValueError("invalid decode shape")
-    return bool(r)
 
 
 def pa_decode_split_part_tokens(num_seqs: int, num_heads: int, num_kv_heads: int, max_context_len: int,

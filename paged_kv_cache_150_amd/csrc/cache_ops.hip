@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const u32x4_t* _
 // included) clamped to 448, NaN written as S.1111.111 with x's sign, and the
 // rest converted by the hardware to the nearest code, ties to even. The format
 // and the scale are this library's reading: the pages name an FP8 KV cache
-// without fixing one (llm-stack-book 7.3, "Running vLLM well in practice").
+// without fixing one (llm-stack-book 7.3, "The knobs that actually matter", item 5).
 __device__ __forceinline__ uint32_t quantize4_e4m3(float a, float b, float c, float d, float scale) {
   float v[4] = {__fdiv_rn(a, scale), __fdiv_rn(b, scale), __fdiv_rn(c, scale), __fdiv_rn(d, scale)};
   uint32_t nan_bits = 0;

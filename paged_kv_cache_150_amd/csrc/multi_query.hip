@@ -468,24 +468,27 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
   auto is_mask = [&](int i) { return wave + i * kMqWaves >= mask_from; };
 
-  // Decode with the new token's write folded in: every lane loads its pieces
-  // of the new K/V row up front (no dependence on anything else); the wave
-  // whose last chunk holds position n - 1 swaps them into that chunk's
-  // registers before using it, and stores them to the slot once its chunks
-  // are done. Nothing in this launch reads the slot from memory after the
-  // store, so no ordering is needed.
+  // Decode with the new token's write folded in. Every lane loads its pieces
+  // of the new K/V row up front (no dependence on anything else). When the
+  // slot is the one the block table gives position n - 1 (the decode step's
+  // own token), the wave whose last chunk holds that position swaps the new
+  // rows into that chunk's registers before using it, and stores them to the
+  // slot once its chunks are done; nothing in this launch reads the slot from
+  // memory after the store, so no ordering is needed. Any other slot (an
+  // empty context included) is only written, by wave 0: attention then uses
+  // what the cache holds at position n - 1.
   // (Decode mode always runs 16-column tiles; the 32-column instantiations
   // leave this out.)
   constexpr bool kFusedWrite = !F8 && NT == 1;
   u32x4_t kn[S::kKSeg];
   uint32_t vn[S::kVDw];
-  bool own_new = false;
+  bool own_new = false;    // this wave stores the new rows
+  bool patch_own = false;  // ... and uses them in place of position n - 1
   int new_ib = 0, new_r0 = 0;
   int64_t new_slot = -1;
   if constexpr (kFusedWrite) {
-    if (a.slot_mapping != nullptr && key_end > 0) {
+    if (a.slot_mapping != nullptr) {
       new_slot = a.slot_mapping[seq];
-      const int pos = key_end - 1;
       if (new_slot >= 0 && new_slot < a.num_blocks * kBlockTokens) {
         const int64_t src_off = (static_cast<int64_t>(seq) * a.num_kv_heads + kvh) * D * S::kElemBytes;
         const gchar_t* ksrc = uniform_ptr(static_cast<const char*>(a.new_key) + src_off);
@@ -493,10 +496,18 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
 #pragma unroll
         for (int sg = 0; sg < S::kKSeg; ++sg) kn[sg] = gload16(ksrc + sg * 64 + (lane >> 4) * 16);
         load_dwords<S::kVDw>(vn, vsrc + (lane & 15) * (S::kVDw * 4));
-        const int c_last = (pos / kBlockTokens) / CB;
-        own_new = c_last % kMqWaves == wave;
-        new_ib = pos / kBlockTokens - c_last * CB;
-        new_r0 = pos % kBlockTokens;
+        const int pos = key_end - 1;
+        const bool on_pos = pos >= 0 && static_cast<int64_t>(bt_row[pos / kBlockTokens]) * kBlockTokens +
+                                            pos % kBlockTokens == new_slot;
+        if (on_pos) {
+          const int c_last = (pos / kBlockTokens) / CB;
+          own_new = c_last % kMqWaves == wave;
+          patch_own = own_new;
+          new_ib = pos / kBlockTokens - c_last * CB;
+          new_r0 = pos % kBlockTokens;
+        } else {
+          own_new = wave == 0;
+        }
       }
     }
   }
@@ -558,12 +569,12 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       if constexpr (kFusedWrite) {
-        if (own_new) patch_new(fb);
+        if (patch_own) patch_new(fb);
       }
       mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
     } else {
       if constexpr (kFusedWrite) {
-        if (own_new) patch_new(fa);
+        if (patch_own) patch_new(fa);
       }
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
     }
@@ -716,14 +727,12 @@ MultiKernel pick_multi(int dtype, int D, int NT, bool fp8_cache, int& W) {
 }
 
 // Waves per workgroup for a launch of `jobs` workgroups: 8 when every
-// resident 4-wave workgroup (two per CU) would get at most one job, else 4.
-// PA_MQ_WAVES=4|8 overrides. (pick_multi keeps 4 where no 8-wave kernel is
+// resident 4-wave workgroup (two per CU) would get at most one job, else 4;
+// PA_OPT_TILE_WAVES forces one. (pick_multi keeps 4 where no 8-wave kernel is
 // built.)
 int pick_waves(int64_t jobs) {
-  if (const char* e = getenv("PA_MQ_WAVES")) {
-    const int v = atoi(e);
-    if (v == 4 || v == 8) return v;
-  }
+  const int v = option_value(PA_OPT_TILE_WAVES);
+  if (v == 4 || v == 8) return v;
   return jobs <= 2 * static_cast<int64_t>(device_cus()) ? 8 : 4;
 }
 
@@ -733,12 +742,11 @@ inline bool aligned16_mq(const void* p) { return (reinterpret_cast<uintptr_t>(p)
 
 // Tiles of 32 columns when the step averages more new tokens per sequence
 // than one 16-column tile holds: prompt chunks and longer speculative runs
-// then read each key once per 32 columns instead of per 16.
+// then read each key once per 32 columns instead of per 16
+// (PA_OPT_TILE_COLUMNS forces a width).
 int pick_tiles(int num_tokens, int num_seqs, int group) {
-  if (const char* e = getenv("PA_MQ_TILE_COLUMNS")) {
-    const int v = atoi(e);
-    if (v == 16 || v == 32) return v / 16;
-  }
+  const int v = option_value(PA_OPT_TILE_COLUMNS);
+  if (v == 16 || v == 32) return v / 16;
   return static_cast<int64_t>(num_tokens) * group > static_cast<int64_t>(num_seqs) * 16 ? 2 : 1;
 }
 

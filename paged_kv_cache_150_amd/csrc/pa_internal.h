@@ -58,4 +58,8 @@ int launch_merge_mq_parts(void* out, float* lse_out, const float* o_parts, const
 // Compute units of the current device (256 when it cannot be queried).
 int device_cus();
 
+// Current value of a kernel-choice option (pa_option in pa.h); 0 = the
+// default choice.
+int option_value(int option);
+
 }  // namespace pa

@@ -1,4 +1,6 @@
-// Paged decode attention for gfx950: pa_decode, pa_decode_split, pa_merge_partitions.
+// Paged decode attention for gfx950: the decode entry points (pa_decode,
+// pa_decode_fp8, pa_decode_prefix, pa_decode_split, pa_merge_partitions), the
+// pieces cut of the split path, and the log-sum-exp merges.
 //
 // What is computed (llm-stack-book 7.3 "vLLM: Architecture, PagedAttention &
 // Internals", sections "PagedAttention in one paragraph" and "The forward step
@@ -6,14 +8,15 @@
 // new query over the sequence's whole context, with K/V rows found through the
 // block table instead of in one contiguous tensor. The softmax runs online over
 // streamed blocks (stanleyjacob.dev "vLLM", Part IV "Stage 6: The forward
-// pass"); a context split into partitions is recombined exactly with
-// log-sum-exp weights.
+// pass"); a context split into pieces is recombined exactly with log-sum-exp
+// weights (Part V, "The attention backend dispatch layer": tiling plus online
+// softmax).
 //
-// Work decomposition (one workgroup per (sequence, kv head, context
-// partition), W waves per workgroup):
-//  * A wave handles "chunks" of CB consecutive 16-token blocks; chunk c goes to
-//    wave c % W. All g = H_q/H_kv query heads of the kv head share every K/V
-//    tile the wave loads.
+// The one-pass decode runs on the tile kernel of multi_query.hip (one new
+// token per sequence). This file holds the pieces kernel of pa_decode_split
+// (persistent workgroups over an even cut of all blocks, one wave per kv head):
+//  * A wave streams chunks of CB consecutive 16-token blocks. All g = H_q/H_kv
+//    query heads of the kv head share every K/V tile the wave loads.
 //  * Scores: one 16x16 MFMA tile per block, A = K rows (M = the block's 16
 //    tokens), B = the group's query rows (N = up to 16 heads), contracted over
 //    head_size. Each lane loads its K operand straight from HBM: token
@@ -25,16 +28,16 @@
 //    reads head_size/16 contiguous elements (d = (l%16)*head_size/16 ...) of
 //    the 4 rows, so each load instruction covers 4 whole rows, and the
 //    probabilities a lane needs come from its own 16-lane row by DPP broadcast.
-//  * P*V runs on the VALU in fp32 (the V tile would need a transpose for MFMA).
+//  * P*V runs on the VALU in fp32.
 //  * Online softmax per chunk with base-2 exponentials (scale*log2(e) folded
 //    into the scores); the chunk maximum is reduced across the 4 row groups.
-//  * At the end each wave reduces its partial sums across row groups and the W
-//    waves merge through LDS with log-sum-exp weights.
-// Reduction order depends only on logical token positions, W and CB, never on
+// Reduction order depends only on logical token positions and CB, never on
 // physical block ids, so results do not change when blocks move or are shared.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+
+#include <atomic>
 
 #include "pa.h"
 #include "pa_device.h"
@@ -42,33 +45,6 @@
 #include "pa_tiles.h"
 
 namespace pa {
-
-struct DecodeArgs {
-  const void* query;
-  const void* key_cache;
-  const void* value_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  void* out;
-  float* lse_out;            // optional
-  const int32_t* seq_order;  // optional processing order of sequences
-  int64_t num_blocks;
-  int32_t max_blocks;
-  int32_t num_seqs;
-  int32_t num_heads;
-  int32_t num_kv_heads;
-  int32_t group;        // H_q / H_kv
-  int32_t num_jobs;     // job ids: ceil(num_seqs / 8) * 8 * num_kv_heads
-  float scale_log2;     // scale * log2(e) (times k_scale for FP8 caches)
-  float v_scale;        // multiplies the normalised output: v_scale for FP8 caches, else 1
-  // Suffix pass of the shared-prefix decode: keys of blocks < skip_blocks were
-  // attended by the prefix pass, whose normalised float32 output and
-  // log-sum-exp per (sequence, query head) join the final merge. Zero / null
-  // for a plain decode.
-  int32_t skip_blocks;
-  const float* prefix_o;    // [num_seqs, num_heads, D]
-  const float* prefix_lse;  // [num_seqs, num_heads]
-};
 
 template <typename T, int D, int G, int CB>
 struct WaveState {
@@ -162,15 +138,6 @@ __device__ __forceinline__ void softmax_pv_chunk(WaveState<T, D, G, CB>& st, con
 }
 
 template <typename T, int D, int G, int CB, bool F8 = false>
-__device__ __forceinline__ void compute_chunk(WaveState<T, D, G, CB>& st, const Chunk<T, D, G, CB, F8>& f,
-                                              const u32x4_t (&q)[DecodeShape<T, D, G, CB, F8>::kQSeg],
-                                              float scale_log2, int tok0, int t_end, bool mask, int lane) {
-  float s[CB][4];
-  qk_chunk<T, D, G, CB, F8>(s, f, q, scale_log2);
-  softmax_pv_chunk<T, D, G, CB, F8>(st, f, s, tok0, t_end, mask, lane);
-}
-
-template <typename T, int D, int G, int CB, bool F8 = false>
 __device__ __forceinline__ void load_query(const void* query, int seq, int num_heads, int head0, int g, int lane,
                                            u32x4_t (&q)[DecodeShape<T, D, G, CB, F8>::kQSeg]) {
   using S = DecodeShape<T, D, G, CB, F8>;
@@ -189,248 +156,6 @@ __device__ __forceinline__ void load_query(const void* query, int seq, int num_h
     u32x4_t v = gload16(qb + off + qoff);
     q[sg] = hq < g ? v : u32x4_t{0u, 0u, 0u, 0u};
   }
-}
-
-// One decode job is one (sequence, kv head); job ids follow the XCD-aware
-// order of slot_and_head (id % 8 names the XCD meant to run it, and all kv
-// heads of a sequence share it), and ids past the last sequence are padding.
-struct DecodeJob {
-  int seq;  // -1 for a padding id
-  int kvh;
-  int n;    // context tokens, clamped to the block table
-};
-
-__device__ __forceinline__ DecodeJob decode_job(const DecodeArgs& a, int id) {
-  DecodeJob j;
-  int seq, kvh;
-  slot_and_head(id, a.num_kv_heads, seq, kvh);
-  j.kvh = kvh;
-  j.seq = -1;
-  j.n = 0;
-  if (seq >= a.num_seqs) return j;
-  if (a.seq_order != nullptr) {
-    // Schedule hint: the j-th dispatched sequence is seq_order[j]. Out-of-range
-    // entries are clamped (wrong output for that caller, never a bad access).
-    const uint32_t o = static_cast<uint32_t>(a.seq_order[seq]);
-    seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
-  }
-  const int max_tokens = a.max_blocks * kBlockTokens;
-  const int n = a.context_lens[seq];
-  j.n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-  j.seq = seq;
-  return j;
-}
-
-// Job k of persistent workgroup w out of `grid`: rounds of `grid` consecutive
-// ids, walked forwards in even rounds and backwards in odd ones, so that with
-// jobs in longest-first order every workgroup gets a similar total. grid is a
-// multiple of 8, so the kv heads of one sequence (ids equal mod 8) still run on
-// one XCD.
-__device__ __forceinline__ int job_of(int k, int w, int grid) {
-  const int base = k * grid;
-  return (k & 1) ? base + grid - 1 - w : base + w;
-}
-
-// This wave's share of one job: chunks wave, wave + W, ... of the context.
-struct JobPlan {
-  const int32_t* bt_row;
-  int64_t head_off;
-  int blk_last;    // last block of the context
-  int mine;        // chunks of this wave
-  int mask_chunk;  // the chunk that reaches past the context end, or -1
-};
-
-// Chunk c of a job starts at block skip_blocks + c * CB.
-
-template <int EB, int D, int CB>  // EB: bytes per cache element
-__device__ __forceinline__ JobPlan plan_job(const DecodeArgs& a, const DecodeJob& j, int wave, int nwaves) {
-  JobPlan p;
-  p.bt_row = a.block_tables + static_cast<int64_t>(j.seq < 0 ? 0 : j.seq) * a.max_blocks;
-  p.head_off = static_cast<int64_t>(j.kvh) * D * EB;
-  const int blk_end = (j.n + kBlockTokens - 1) / kBlockTokens;
-  const int nchunk = blk_end > a.skip_blocks ? (blk_end - a.skip_blocks + CB - 1) / CB : 0;
-  p.blk_last = blk_end - 1;
-  p.mine = (j.seq >= 0 && wave < nchunk) ? (nchunk - wave + nwaves - 1) / nwaves : 0;
-  p.mask_chunk = ((a.skip_blocks + nchunk * CB) * kBlockTokens > j.n) ? nchunk - 1 : -1;
-  return p;
-}
-
-// Persistent workgroups, each taking the jobs job_of(0, w), job_of(1, w), ...
-// While a job's waves merge their partial results, the next job's query and
-// first chunk are already being loaded, so no workgroup waits on a cold start
-// between jobs.
-// Two workgroups per CU (at most 256 registers per lane); the 16-head group
-// needs more registers and runs one workgroup per CU.
-template <typename T, int D, int G, int CB, bool PF, bool F8 = false>
-__global__ __launch_bounds__(G >= 16 ? 256 : 512, 1) void paged_decode_kernel(DecodeArgs a) {
-  using S = DecodeShape<T, D, G, CB, F8>;
-  extern __shared__ float s_acc[];  // [W][G][D]
-  __shared__ float s_m[8][16];
-  __shared__ float s_l[8][16];
-
-  const int lane = threadIdx.x & 63;
-  // Wave-uniform by construction; readfirstlane lets the compiler keep all
-  // per-wave indexing (units, block ids, base addresses) in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int grid = gridDim.x;
-  const int w = blockIdx.x;
-  const int g = a.group;
-
-  const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
-  const int64_t blk_stride = static_cast<int64_t>(tok_stride) * kBlockTokens;
-  const char* kc = static_cast<const char*>(a.key_cache);
-  const char* vc = static_cast<const char*>(a.value_cache);
-
-  int k = 0;
-  const int id0 = job_of(0, w, grid);
-  DecodeJob cur;
-  cur.seq = -1;
-  cur.kvh = 0;
-  cur.n = 0;
-  if (id0 < a.num_jobs) cur = decode_job(a, id0);
-  JobPlan pc = plan_job<S::kElemBytes, D, CB>(a, cur, wave, nwaves);
-  // Block of this wave's i-th chunk of a job.
-  auto blk_of = [&](int i) { return a.skip_blocks + (wave + i * nwaves) * CB; };
-
-  u32x4_t q[S::kQSeg];
-  Chunk<T, D, G, CB, F8> fa;
-  if (cur.n > 0 && cur.seq >= 0) {
-    load_query<T, D, G, CB, F8>(a.query, cur.seq, a.num_heads, cur.kvh * g, g, lane, q);
-    if (PF && pc.mine > 0)
-      load_chunk<T, D, G, CB, F8>(fa, kc, vc, pc.bt_row, blk_of(0), pc.blk_last, a.num_blocks, tok_stride,
-                              blk_stride, pc.head_off, lane);
-  }
-  int id = id0;
-  while (id < a.num_jobs) {
-    // The next job is known now: its metadata is fetched a whole job ahead.
-    const int id_next = job_of(k + 1, w, grid);
-    DecodeJob nxt;
-    nxt.seq = -1;
-    nxt.kvh = 0;
-    nxt.n = 0;
-    if (id_next < a.num_jobs) nxt = decode_job(a, id_next);
-
-    WaveState<T, D, G, CB> st;
-    st.m = -__builtin_inff();
-    st.l = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = 0.f;
-
-    const int mine = pc.mine;
-    auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
-    auto is_mask = [&](int i) { return wave + i * nwaves == pc.mask_chunk; };
-    if constexpr (PF) {
-      // One chunk of lookahead, fa already in flight. The steady-state loop
-      // issues its lookahead loads unconditionally and the last one or two
-      // chunks are peeled off: with a conditional load inside the loop the
-      // hardware wait counts on the two paths differ and the wait before the
-      // current chunk's use would also cover the lookahead. The scheduling
-      // barriers keep the loads ahead of the current chunk's arithmetic (left
-      // alone, the scheduler sinks them to shorten register live ranges).
-      // Only the final chunk of the context, a wave's last, can need a mask.
-      Chunk<T, D, G, CB, F8> fb;
-      if (mine > 0) {
-        int i = 0;
-        for (; i + 2 < mine; i += 2) {
-          load_chunk<T, D, G, CB, F8>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
-                                  blk_stride, pc.head_off, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          load_chunk<T, D, G, CB, F8>(fa, kc, vc, pc.bt_row, blk_of(i + 2), pc.blk_last, a.num_blocks, tok_stride,
-                                  blk_stride, pc.head_off, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<T, D, G, CB, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, false, lane);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (i + 1 < mine) {
-          load_chunk<T, D, G, CB, F8>(fb, kc, vc, pc.bt_row, blk_of(i + 1), pc.blk_last, a.num_blocks, tok_stride,
-                                  blk_stride, pc.head_off, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, false, lane);
-          compute_chunk<T, D, G, CB, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), cur.n, is_mask(i + 1), lane);
-        } else {
-          compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
-        }
-      }
-    } else {
-      for (int i = 0; i < mine; ++i) {
-        load_chunk<T, D, G, CB, F8>(fa, kc, vc, pc.bt_row, blk_of(i), pc.blk_last, a.num_blocks, tok_stride,
-                                blk_stride, pc.head_off, lane);
-        compute_chunk<T, D, G, CB, F8>(st, fa, q, a.scale_log2, tok_of(i), cur.n, is_mask(i), lane);
-      }
-    }
-
-    // The next job's query and first chunk go out before this job's merge.
-    const JobPlan pn = plan_job<S::kElemBytes, D, CB>(a, nxt, wave, nwaves);
-    if (nxt.n > 0 && nxt.seq >= 0) {
-      load_query<T, D, G, CB, F8>(a.query, nxt.seq, a.num_heads, nxt.kvh * g, g, lane, q);
-      if (PF && pn.mine > 0)
-        load_chunk<T, D, G, CB, F8>(fa, kc, vc, pn.bt_row, blk_of(0), pn.blk_last, a.num_blocks, tok_stride,
-                                blk_stride, pn.head_off, lane);
-    }
-
-    // Sum this wave's partials over the 4 row groups (lanes l, l^16, l^32, l^48).
-    st.l = rows_sum(st.l);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < S::kVec; ++e) st.acc[h][e] = rows_sum(st.acc[h][e]);
-    if (lane < 16) {
-      s_m[wave][lane] = st.m;
-      s_l[wave][lane] = st.l;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < S::kVec; ++e) s_acc[(wave * G + h) * D + lane * S::kVec + e] = st.acc[h][e];
-    }
-    __syncthreads();
-
-    if (cur.seq >= 0) {
-      // Merge the waves: weights 2^(m_w - M). A prefix-pass result joins as
-      // one more part with l = 1, acc = its output and m = its lse in base 2.
-      const int head0 = cur.kvh * g;
-      for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        const int64_t row = static_cast<int64_t>(cur.seq) * a.num_heads + head0 + h;
-        float M = -__builtin_inff();
-        for (int v = 0; v < nwaves; ++v) M = fmaxf(M, s_m[v][h]);
-        float pm = -__builtin_inff();
-        if (a.prefix_o != nullptr) {
-          pm = a.prefix_lse[row] * kLog2e;
-          M = fmaxf(M, pm);
-        }
-        float o = 0.f, L = 0.f;
-        if (M != -__builtin_inff()) {
-          for (int v = 0; v < nwaves; ++v) {
-            const float wt = fast_exp2(s_m[v][h] - M);
-            L = fmaf(wt, s_l[v][h], L);
-            o = fmaf(wt, s_acc[(v * G + h) * D + d], o);
-          }
-          if (pm != -__builtin_inff()) {
-            const float wt = fast_exp2(pm - M);
-            L += wt;
-            o = fmaf(wt, a.prefix_o[row * D + d], o);
-          }
-          o = o / L * a.v_scale;
-        }
-        const float lse = (M == -__builtin_inff()) ? -__builtin_inff() : (M + fast_log2(L)) * kLn2;
-        store_elem<T>(static_cast<T*>(a.out) + row * D + d, o);
-        if (a.lse_out != nullptr && d == 0) a.lse_out[row] = lse;
-      }
-    }
-    __syncthreads();  // the next job rewrites the LDS partials
-
-    id = id_next;
-    cur = nxt;
-    pc = pn;
-    ++k;
-  }
-
 }
 
 // ------------------------------------------------------------------ partitioned path
@@ -890,27 +615,12 @@ namespace {
 // Rows (one wave each) per workgroup of the merge kernels: one for merges of
 // up to eight rows per compute unit, so that a small merge (a few hundred to
 // a few thousand rows of long partial lists) spreads its loads over every
-// compute unit instead of a quarter of them. PA_MERGE_ROWS=1|2|4 overrides.
+// compute unit instead of a quarter of them; PA_OPT_MERGE_ROWS forces a count.
 int merge_rows_per_block(int64_t rows) {
-  if (const char* e = getenv("PA_MERGE_ROWS")) {
-    const int v = atoi(e);
-    if (v == 1 || v == 2 || v == 4) return v;
-  }
+  const int v = option_value(PA_OPT_MERGE_ROWS);
+  if (v == 1 || v == 2 || v == 4) return v;
   return rows <= 8 * static_cast<int64_t>(device_cus()) ? 1 : 4;
 }
-
-// Blocks per chunk (CB) and one-chunk register lookahead (PF), chosen per
-// shape so a wave fits in 256 VGPRs without spilling (2 waves per SIMD).
-template <typename T, int D, int G, bool F8 = false>
-struct Policy {
-  static constexpr int kElemBytes = F8 ? 1 : static_cast<int>(sizeof(T));
-  static constexpr int kRegsPerBlock = D * kElemBytes / 8;  // K + V dwords per lane
-  static constexpr int kAcc = G * D / 16;
-  // FP8 blocks take half the registers; small groups use twice the blocks per
-  // chunk (larger ones would spill the conversion temporaries).
-  static constexpr int CB = (kRegsPerBlock <= 16 && G <= 2) ? 4 : (kRegsPerBlock <= 32 && G <= 4) ? 2 : 1;
-  static constexpr bool PF = 2 * CB * kRegsPerBlock + kAcc <= 160;
-};
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -918,54 +628,6 @@ int next_pow2_group(int g) {
   int G = 1;
   while (G < g) G <<= 1;
   return G;
-}
-
-// Waves per workgroup forced through PA_DECODE_WAVES (1, 2, 4 or 8), else 0.
-int waves_override() {
-  static int w = [] {
-    const char* e = getenv("PA_DECODE_WAVES");
-    int v = e ? atoi(e) : 0;
-    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
-  }();
-  return w;
-}
-
-
-typedef void (*DecodeKernel)(DecodeArgs);
-
-template <typename T, int D, int G, bool F8 = false>
-DecodeKernel kernel_for() {
-  using P = Policy<T, D, G, F8>;
-  return paged_decode_kernel<T, D, G, P::CB, P::PF, F8>;
-}
-
-template <int D>
-DecodeKernel pick_group_fp8(int G) {
-  switch (G) {
-    case 1: return kernel_for<bf16_t, D, 1, true>();
-    case 2: return kernel_for<bf16_t, D, 2, true>();
-    case 4: return kernel_for<bf16_t, D, 4, true>();
-    case 8: return kernel_for<bf16_t, D, 8, true>();
-    case 16: return kernel_for<bf16_t, D, 16, true>();
-    default: return nullptr;
-  }
-}
-
-template <typename T, int D>
-DecodeKernel pick_group(int G) {
-  switch (G) {
-    case 1: return kernel_for<T, D, 1>();
-    case 2: return kernel_for<T, D, 2>();
-    case 4: return kernel_for<T, D, 4>();
-    case 8: return kernel_for<T, D, 8>();
-    case 16: return kernel_for<T, D, 16>();
-    default: return nullptr;
-  }
-}
-
-DecodeKernel pick_decode(int dtype, int D, int G) {
-  if (dtype == PA_DTYPE_BF16) return D == 128 ? pick_group<bf16_t, 128>(G) : pick_group<bf16_t, 64>(G);
-  return D == 128 ? pick_group<float, 128>(G) : pick_group<float, 64>(G);
 }
 
 int check_common(const void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -994,55 +656,6 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess) return 0;
   return cus * (per_cu > 0 ? per_cu : 1);
-}
-
-// Which kernel serves a decode step: the tile kernel (the multi-query kernel
-// with one token per sequence: P*V on the matrix cores, one workgroup per
-// (sequence, kv head) handed out by the hardware in seq_order, with 8-wave
-// workgroups when the grid is a single round) measured faster on every
-// workload; the persistent kernel is kept as the alternative.
-// PA_DECODE_KERNEL=persistent|tiles forces one (the tests run both).
-bool decode_by_tiles(int group) {
-  if (const char* e = getenv("PA_DECODE_KERNEL")) {
-    if (e[0] == 'p') return false;
-  }
-  return group <= 16;
-}
-
-int launch_decode(DecodeArgs args, int num_seqs, int dtype, int head_size, hipStream_t stream,
-                  bool fp8_cache = false) {
-  const int G = next_pow2_group(args.group);
-  DecodeKernel k = fp8_cache ? (head_size == 128 ? pick_group_fp8<128>(G) : pick_group_fp8<64>(G))
-                             : pick_decode(dtype, head_size, G);
-  if (!k) return PA_ERR_UNSUPPORTED;
-  // Job ids padded to whole XCD rounds (a multiple of 8).
-  const int64_t jobs = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * args.num_kv_heads;
-  if (jobs <= 0) return PA_OK;
-  if (jobs > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
-  // Four waves per workgroup (two workgroups per CU), unless every workgroup
-  // would get at most one job: then eight waves (one workgroup per CU) split
-  // each job twice as finely, which narrows the spread of finishing times
-  // (batch 64: 76 -> 71 us). The 16-head group fits 4 waves only.
-  int W = waves_override();
-  if (W == 0 || (W == 8 && G >= 16)) {
-    W = 4;
-    if (G < 16) {
-      const int64_t resident4 = resident_groups(reinterpret_cast<const void*>(k), 4 * kWave,
-                                                static_cast<size_t>(4) * G * head_size * sizeof(float));
-      if (resident4 > 0 && jobs <= resident4) W = 8;
-    }
-  }
-  const size_t lds = static_cast<size_t>(W) * G * head_size * sizeof(float);
-  // Persistent grid: the workgroups that fit at once, a multiple of 8 (one
-  // round over the XCDs), and no more than there are jobs.
-  int64_t grid = resident_groups(reinterpret_cast<const void*>(k), W * kWave, lds);
-  if (grid <= 0) return PA_ERR_HIP;
-  if (grid >= 8) grid -= grid % 8;
-  if (grid > jobs) grid = jobs;
-
-  args.num_jobs = static_cast<int32_t>(jobs);
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), lds, stream, args);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 typedef void (*SplitKernel)(SplitArgs);
@@ -1161,14 +774,12 @@ int launch_merge_parts(void* out, float* lse_out, const float* o_parts, const fl
 // batch has fewer (sequence, kv head) pairs than resident tile workgroups (2
 // per CU): long contexts of a few sequences, where the pieces measured faster.
 // (Larger groups keep the tiles: the piece kernel's per-lane accumulators
-// spill registers from a group of 8 up.) PA_SPLIT_KERNEL=pieces|tiles
-// overrides.
+// spill registers from a group of 8 up.) PA_OPT_SPLIT_CUT forces a cut.
 bool split_by_tiles(int group, int num_seqs, int num_kv_heads) {
   if (group > 16) return false;
-  if (const char* e = getenv("PA_SPLIT_KERNEL")) {
-    if (e[0] == 'p') return false;
-    if (e[0] == 't') return true;
-  }
+  const int v = option_value(PA_OPT_SPLIT_CUT);
+  if (v == 1) return true;
+  if (v == 2) return false;
   if (group > 4) return true;
   return static_cast<int64_t>(num_seqs) * num_kv_heads >= 2 * static_cast<int64_t>(device_cus());
 }
@@ -1177,12 +788,11 @@ bool split_by_tiles(int group, int num_seqs, int num_kv_heads) {
 // that still leaves about three rounds of resident tile workgroups for the
 // longest possible batch (num_seqs contexts of max_context_len tokens), so
 // each workgroup streams long enough to amortise its start; at most the
-// longest context. PA_SPLIT_PART_FACTOR=k overrides k.
+// longest context. PA_OPT_SPLIT_PART_FACTOR forces k.
 int split_part_tokens(int num_seqs, int num_kv_heads, int max_context_len, int P) {
   const int64_t n_p = (static_cast<int64_t>(max_context_len) + P - 1) / P;
   if (n_p <= 1) return P;
-  int64_t k = 0;
-  if (const char* e = getenv("PA_SPLIT_PART_FACTOR")) k = atoi(e);
+  int64_t k = option_value(PA_OPT_SPLIT_PART_FACTOR);
   if (k <= 0) {
     const int64_t target = 3 * 2 * static_cast<int64_t>(device_cus());  // 2 tile workgroups per CU
     k = static_cast<int64_t>(num_seqs) * n_p * num_kv_heads / target;
@@ -1231,37 +841,9 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
   int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
                         num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
   if (st != PA_OK || num_seqs == 0) return st;
-  if (decode_by_tiles(num_heads / num_kv_heads))
-    return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
-                               num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
-                               dtype, false, lse_out, seq_order, 0, nullptr, nullptr,
-                               static_cast<hipStream_t>(stream));
-  DecodeArgs args{};
-  args.query = query;
-  args.key_cache = key_cache;
-  args.value_cache = value_cache;
-  args.block_tables = block_tables;
-  args.context_lens = context_lens;
-  args.out = out;
-  args.lse_out = lse_out;
-  args.seq_order = seq_order;
-  args.num_blocks = num_blocks;
-  args.max_blocks = max_blocks_per_seq;
-  args.num_seqs = num_seqs;
-  args.num_heads = num_heads;
-  args.num_kv_heads = num_kv_heads;
-  args.group = num_heads / num_kv_heads;
-  args.scale_log2 = scale * kLog2e;
-  args.v_scale = 1.0f;
-  return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream));
-}
-
-extern "C" int pa_decode_uses_tiles(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                                    int32_t dtype, int32_t fp8_cache) {
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
-  if (num_heads / num_kv_heads > 16 || (head_size != 64 && head_size != 128)) return -1;
-  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return -1;
-  return decode_by_tiles(num_heads / num_kv_heads) ? 1 : 0;
+  return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f, dtype,
+                             false, lse_out, seq_order, 0, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -1305,31 +887,9 @@ extern "C" int pa_decode_prefix(void* out, const void* query, const void* key_ca
                           num_heads, num_kv_heads, head_size, num_blocks, prefix_blocks, scale, dtype, part_o,
                           part_lse, s);
   if (st != PA_OK) return st;
-  if (decode_by_tiles(num_heads / num_kv_heads))
-    return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
-                               num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
-                               dtype, false, lse_out, seq_order, prefix_blocks, part_o, part_lse, s);
-  DecodeArgs args{};
-  args.query = query;
-  args.key_cache = key_cache;
-  args.value_cache = value_cache;
-  args.block_tables = block_tables;
-  args.context_lens = context_lens;
-  args.out = out;
-  args.lse_out = lse_out;
-  args.seq_order = seq_order;
-  args.num_blocks = num_blocks;
-  args.max_blocks = max_blocks_per_seq;
-  args.num_seqs = num_seqs;
-  args.num_heads = num_heads;
-  args.num_kv_heads = num_kv_heads;
-  args.group = num_heads / num_kv_heads;
-  args.scale_log2 = scale * kLog2e;
-  args.v_scale = 1.0f;
-  args.skip_blocks = prefix_blocks;
-  args.prefix_o = part_o;
-  args.prefix_lse = part_lse;
-  return launch_decode(args, num_seqs, dtype, head_size, s);
+  return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f, dtype,
+                             false, lse_out, seq_order, prefix_blocks, part_o, part_lse, s);
 }
 
 extern "C" int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const uint8_t* value_cache,
@@ -1344,30 +904,11 @@ extern "C" int pa_decode_fp8(void* out, const void* query, const uint8_t* key_ca
   if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
     return PA_ERR_INVALID_ARG;
-  if (decode_by_tiles(num_heads / num_kv_heads))
-    return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
-                               num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * k_scale * kLog2e,
-                               v_scale, dtype, true, lse_out, seq_order, 0, nullptr, nullptr,
-                               static_cast<hipStream_t>(stream));
-  DecodeArgs args{};
-  args.query = query;
-  args.key_cache = key_cache;
-  args.value_cache = value_cache;
-  args.block_tables = block_tables;
-  args.context_lens = context_lens;
-  args.out = out;
-  args.lse_out = lse_out;
-  args.seq_order = seq_order;
-  args.num_blocks = num_blocks;
-  args.max_blocks = max_blocks_per_seq;
-  args.num_seqs = num_seqs;
-  args.num_heads = num_heads;
-  args.num_kv_heads = num_kv_heads;
-  args.group = num_heads / num_kv_heads;
   // Keys are code values times k_scale: the scale folds into the scores'.
-  args.scale_log2 = scale * k_scale * kLog2e;
-  args.v_scale = v_scale;
-  return launch_decode(args, num_seqs, dtype, head_size, static_cast<hipStream_t>(stream), true);
+  return launch_decode_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * k_scale * kLog2e,
+                             v_scale, dtype, true, lse_out, seq_order, 0, nullptr, nullptr,
+                             static_cast<hipStream_t>(stream));
 }
 
 // Workspace layout: o_p [S, H_q, slots, D] float32 | lse_p [S, H_q, slots]
@@ -1467,4 +1008,38 @@ extern "C" int pa_merge_partitions(void* out, float* lse_out, const float* o_par
   if (!aligned16(out) || !aligned16(o_parts)) return PA_ERR_INVALID_ARG;
   return launch_merge(out, lse_out, o_parts, lse_parts, static_cast<int64_t>(num_seqs) * num_heads, num_parts,
                       head_size, dtype, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ kernel-choice options
+namespace {
+
+constexpr int kNumOptions = 5;
+std::atomic<int> g_options[kNumOptions];
+
+bool option_ok(int option, int value) {
+  switch (option) {
+    case PA_OPT_TILE_WAVES: return value == 0 || value == 4 || value == 8;
+    case PA_OPT_TILE_COLUMNS: return value == 0 || value == 16 || value == 32;
+    case PA_OPT_SPLIT_CUT: return value >= 0 && value <= 2;
+    case PA_OPT_SPLIT_PART_FACTOR: return value >= 0;
+    case PA_OPT_MERGE_ROWS: return value == 0 || value == 1 || value == 2 || value == 4;
+    default: return false;
+  }
+}
+
+}  // namespace
+
+int pa::option_value(int option) {
+  return option >= 0 && option < kNumOptions ? g_options[option].load(std::memory_order_relaxed) : 0;
+}
+
+extern "C" int pa_set_option(int option, int value) {
+  if (option < 0 || option >= kNumOptions || !option_ok(option, value)) return PA_ERR_INVALID_ARG;
+  g_options[option].store(value, std::memory_order_relaxed);
+  return PA_OK;
+}
+
+extern "C" int pa_get_option(int option) {
+  if (option < 0 || option >= kNumOptions) return -1;
+  return g_options[option].load(std::memory_order_relaxed);
 }

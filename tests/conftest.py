@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _default_kernel_options():
+    """Every test starts and ends with the library's default kernel choices
+    (a test may force some through pa_set_option)."""
+    yield
+    mod = sys.modules.get("paged_kv_cache_150_amd")
+    if mod is not None and getattr(mod, "_lib", None) is not None:
+        for opt in range(5):
+            mod.pa_set_option(opt, 0)

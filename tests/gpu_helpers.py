@@ -13,6 +13,12 @@ LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}    # max |lse - oracle|
 PART_TOL = {"bf16": 1e-3, "f32": 1e-5}   # float32 partials from bf16 inputs
 
 
+def forced(pa, **opts):
+    """Context manager forcing kernel-choice options by short name
+    (tile_waves=4, split_cut=2, ...) for the calls inside it."""
+    return pa.options({getattr(pa, "PA_OPT_" + k.upper()): int(v) for k, v in opts.items()})
+
+
 def ensure_built():
     import paged_kv_cache_150_amd as pa
     if not os.path.exists(pa.library_path()):

@@ -36,7 +36,7 @@ def test_headers_declare_the_boundary():
         "pa_multi_query_split", "pa_multi_query_split_partition_size", "pa_decode_prefix_workspace_bytes",
         "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",
-        "pa_decode_uses_tiles", "pa_decode_split_part_tokens"])
+        "pa_decode_split_part_tokens", "pa_set_option", "pa_get_option"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
         "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
         "pa_pool_allocate", "pa_pool_append_slot", "pa_pool_share", "pa_pool_release",
@@ -51,6 +51,20 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+
+
+def test_kernel_options(lib):
+    """Options keep valid values, reject the rest unchanged, and read back."""
+    valid = {0: [0, 4, 8], 1: [0, 16, 32], 2: [0, 1, 2], 3: [0, 1, 7], 4: [0, 1, 2, 4]}
+    invalid = {0: [2, 16, -1], 1: [8, 64], 2: [3, -1], 3: [-1], 4: [3, 8]}
+    for opt, vals in valid.items():
+        for v in vals:
+            assert lib.pa_set_option(opt, v) == 0 and lib.pa_get_option(opt) == v
+        for v in invalid[opt]:
+            assert lib.pa_set_option(opt, v) == 1 and lib.pa_get_option(opt) == vals[-1]
+        assert lib.pa_set_option(opt, 0) == 0
+    assert lib.pa_set_option(5, 0) == 1 and lib.pa_set_option(-1, 0) == 1
+    assert lib.pa_get_option(5) == -1 and lib.pa_get_option(-1) == -1
 
 
 def test_status_strings(lib):
@@ -170,33 +184,34 @@ def test_multi_query_host_validation(lib):
     assert f(*ok, 3, 5, *shape, c(0.1), 2, None, None) == 1              # dtype
 
 
-def test_split_cut_choice(lib, monkeypatch):
+def test_split_cut_choice(lib):
     """pa_decode_split cuts into partitions of k * P tokens (tile kernel) when
     its 16-column tiles hold the group and the batch has at least as many
     (sequence, kv head) pairs as resident tile workgroups, else into pieces;
     the overrides win where they apply. Host-only: with no device the CU count
     defaults to 256 (512 resident tile workgroups)."""
     f = lib.pa_decode_split_part_tokens
-    monkeypatch.delenv("PA_SPLIT_KERNEL", raising=False)
-    monkeypatch.setenv("PA_SPLIT_PART_FACTOR", "1")
+    PART_FACTOR, CUT = 3, 2
+    lib.pa_set_option(PART_FACTOR, 1)
     assert f(64, 32, 8, 2048, 512) == 512                 # 512 pairs: partitions
     assert f(8, 32, 8, 32768, 512) == 0                   # 64 pairs, group 4: pieces
     assert f(8, 64, 8, 32768, 512) == 512                 # 64 pairs, group 8: partitions
     assert f(256, 64, 2, 4096, 512) == 0                  # group of 32: pieces
-    monkeypatch.setenv("PA_SPLIT_PART_FACTOR", "3")
+    lib.pa_set_option(PART_FACTOR, 3)
     assert f(64, 32, 8, 32768, 512) == 1536
     assert f(64, 32, 8, 1000, 512) == 1024                # k capped at ceil(1000 / 512)
     assert f(64, 32, 8, 300, 512) == 512
     for bad in [(8, 30, 8, 4096, 512), (8, 32, 0, 4096, 512), (8, 32, 8, -1, 512), (8, 32, 8, 4096, 24),
                 (-1, 32, 8, 4096, 512)]:
         assert f(*bad) == -1
-    monkeypatch.delenv("PA_SPLIT_PART_FACTOR")
+    lib.pa_set_option(PART_FACTOR, 0)
     assert f(64, 32, 8, 2048, 512) == 512                 # 64 * 4 * 8 / 1536 rounds down to k = 1
     assert f(256, 32, 8, 4096, 512) == 4096               # k = 10, capped at 8 partitions
-    monkeypatch.setenv("PA_SPLIT_KERNEL", "pieces")
+    lib.pa_set_option(CUT, 2)
     assert f(64, 32, 8, 2048, 512) == 0
-    monkeypatch.setenv("PA_SPLIT_KERNEL", "tiles")
+    lib.pa_set_option(CUT, 1)
     assert f(8, 32, 8, 32768, 512) == 1024 and f(256, 64, 2, 4096, 512) == 0   # k = 8 * 64 * 8 // 1536
+    lib.pa_set_option(CUT, 0)
 
 
 def test_multi_query_split_host_validation(lib):

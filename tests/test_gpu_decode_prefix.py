@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import LSE_TOL, TOL, Dev, bits, ensure_built, f64, to_dev
+from gpu_helpers import LSE_TOL, TOL, Dev, bits, ensure_built, f64, forced, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -17,16 +17,15 @@ def pa():
     return ensure_built()
 
 
-@pytest.fixture(autouse=True, params=["persistent", "tiles", "tiles4"])
-def decode_kernel(request, monkeypatch):
-    """Run every test here with each decode kernel (both must give the
-    oracle's answers): the tile kernel with its own choice of waves per
+@pytest.fixture(autouse=True, params=["tiles", "tiles4"])
+def decode_kernel(request, pa):
+    """Run every test here with the tile kernel's own choice of waves per
     workgroup (8 on these small grids) and with 4 forced."""
-    kernel = "tiles" if request.param.startswith("tiles") else request.param
-    monkeypatch.setenv("PA_DECODE_KERNEL", kernel)
     if request.param == "tiles4":
-        monkeypatch.setenv("PA_MQ_WAVES", "4")
-    return kernel
+        with forced(pa, tile_waves=4):
+            yield request.param
+    else:
+        yield request.param
 
 
 def _prefix_decode(pa, dev, prefix_blocks, lse=True, order=None):
@@ -127,8 +126,8 @@ def test_workspace_and_argument_errors(pa):
 
 
 def test_prefix_70b_full_size(pa):
-    """The 70B-shaped shared-prefix workload at full size: the shared-prefix
-    decode against pa_decode everywhere and against the oracle on a sample."""
+    """The 70B-shaped shared-prefix workload at full size: every row of the
+    shared-prefix decode against the oracle, and against pa_decode."""
     cfg = W.CONFIG_BY_NAME["prefix_70b"]
     inp = W.make_inputs(cfg)
     dev = Dev(inp)
@@ -137,8 +136,7 @@ def test_prefix_70b_full_size(pa):
     torch.cuda.synchronize()
     assert np.abs(f64(out) - f64(ref_out)).max() <= TOL["bf16"]
     assert np.abs(f64(lse) - f64(ref_lse)).max() <= LSE_TOL["bf16"]
-    rows = np.random.default_rng(2).choice(cfg.num_seqs, 10, replace=False)
-    ref, rl = oracle.paged_decode(inp.query[rows], inp.key_cache, inp.value_cache, inp.block_tables[rows],
-                                  inp.context_lens[rows], cfg.scale, "bf16")
-    assert np.abs(f64(out)[rows] - ref).max() <= TOL["bf16"]
-    assert np.abs(f64(lse)[rows] - rl).max() <= LSE_TOL["bf16"]
+    ref, rl = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
+                                  cfg.scale, "bf16")
+    assert np.abs(f64(out) - ref).max() <= TOL["bf16"]
+    assert np.abs(f64(lse) - rl).max() <= LSE_TOL["bf16"]

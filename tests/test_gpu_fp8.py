@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import LSE_TOL, TOL, bits, ensure_built, f64, max_err, to_dev
+from gpu_helpers import LSE_TOL, TOL, bits, ensure_built, f64, forced, max_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -17,16 +17,15 @@ def pa():
     return ensure_built()
 
 
-@pytest.fixture(autouse=True, params=["persistent", "tiles", "tiles4"])
-def decode_kernel(request, monkeypatch):
-    """Run every test here with each decode kernel (both must give the
-    oracle's answers): the tile kernel with its own choice of waves per
+@pytest.fixture(autouse=True, params=["tiles", "tiles4"])
+def decode_kernel(request, pa):
+    """Run every test here with the tile kernel's own choice of waves per
     workgroup (8 on these small grids) and with 4 forced."""
-    kernel = "tiles" if request.param.startswith("tiles") else request.param
-    monkeypatch.setenv("PA_DECODE_KERNEL", kernel)
     if request.param == "tiles4":
-        monkeypatch.setenv("PA_MQ_WAVES", "4")
-    return kernel
+        with forced(pa, tile_waves=4):
+            yield request.param
+    else:
+        yield request.param
 
 
 def _dev_u8(a):
@@ -92,10 +91,10 @@ def test_decode_fp8_matches_the_oracle(pa, d, Hq, Hkv):
     np.testing.assert_array_equal(bits(out), bits(out2))
 
 
-def test_fp8_step_full_size_sampled(pa):
+def test_fp8_step_full_size(pa):
     """The FP8 batch-256 workload: quantizing write of the 256 new tokens into
-    the pool, then decode; every code written is checked, and the outputs of a
-    sample of sequences against the oracle."""
+    the pool, then decode; every code written is checked, and every output
+    row and log-sum-exp against the oracle."""
     cfg = W.CONFIG_BY_NAME["llama3_8b_b256_fp8"]
     inp = W.make_inputs(cfg, mode="perf")
     kc_h, vc_h = W.caches_before_write(inp)
@@ -103,8 +102,9 @@ def test_fp8_step_full_size_sampled(pa):
     pa.pa_reshape_and_cache_fp8(to_dev(inp.new_key), to_dev(inp.new_value), gk, gv, to_dev(inp.slot_mapping),
                                 cfg.k_scale, cfg.v_scale)
     out = torch.empty((cfg.num_seqs, cfg.num_heads, cfg.head_size), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.num_seqs, cfg.num_heads), dtype=torch.float32, device="cuda")
     pa.pa_decode_fp8(out, to_dev(inp.query), gk, gv, to_dev(inp.block_tables), to_dev(inp.context_lens),
-                     cfg.scale, cfg.k_scale, cfg.v_scale)
+                     cfg.scale, cfg.k_scale, cfg.v_scale, lse_out=lse)
     torch.cuda.synchronize()
     rows = cfg.num_blocks * 16
     slots = inp.slot_mapping
@@ -113,14 +113,7 @@ def test_fp8_step_full_size_sampled(pa):
     np.testing.assert_array_equal(flat_k, oracle.quantize(inp.new_key, cfg.k_scale))
     np.testing.assert_array_equal(flat_v, oracle.quantize(inp.new_value, cfg.v_scale))
     kc_after, vc_after = gk.cpu().numpy(), gv.cpu().numpy()
-    got = f64(out)
-    q = oracle.decode_values(inp.query, "bf16")
-    rng = np.random.default_rng(0)
-    g = cfg.num_heads // cfg.num_kv_heads
-    for i in rng.choice(cfg.num_seqs, 12, replace=False):
-        n = int(inp.context_lens[i])
-        Kc, Vc = oracle.gather_context(kc_after, vc_after, inp.block_tables[i], n, 16)
-        Kf, Vf = oracle.dequantize(Kc, cfg.k_scale), oracle.dequantize(Vc, cfg.v_scale)
-        for h in range(cfg.num_kv_heads):
-            ro, _ = oracle.attention_contiguous(q[i, h * g:(h + 1) * g], Kf[:, h:h + 1], Vf[:, h:h + 1], cfg.scale)
-            assert np.abs(got[i, h * g:(h + 1) * g] - ro).max() <= TOL["bf16"]
+    ref, ref_lse = oracle.paged_decode_fp8(inp.query, kc_after, vc_after, inp.block_tables, inp.context_lens,
+                                           cfg.scale, cfg.k_scale, cfg.v_scale)
+    assert max_err(out, ref) <= TOL["bf16"]
+    assert max_err(lse, ref_lse) <= LSE_TOL["bf16"]

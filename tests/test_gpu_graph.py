@@ -78,9 +78,9 @@ def test_reshape_and_decode_graph(pa):
     _replay_against_eager(q, _queries(q.shape, q.dtype, REPLAYS, 1), graph, [out, lse, kc, vc], eager)
 
 
-@pytest.mark.parametrize("kernel", ["tiles", "persistent"])
-def test_decode_split_graph(pa, monkeypatch, kernel):
-    monkeypatch.setenv("PA_SPLIT_KERNEL", kernel)
+@pytest.mark.parametrize("cut", [1, 2], ids=["partitions", "pieces"])
+def test_decode_split_graph(pa, cut):
+    pa.pa_set_option(pa.PA_OPT_SPLIT_CUT, cut)
     cfg, inp = _decode_case(seed=62)
     kc, vc = to_dev(inp.key_cache), to_dev(inp.value_cache)
     bt, cl = to_dev(inp.block_tables), to_dev(inp.context_lens)

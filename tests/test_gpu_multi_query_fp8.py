@@ -44,8 +44,8 @@ NLENS = [1, 100, 16, 33, 200, 300, 50, 3, 17, 160, 17, 0]
 
 @pytest.mark.parametrize("columns", ["16", "32"])
 @pytest.mark.parametrize("d,Hq,Hkv", [(128, 32, 8), (128, 8, 8), (64, 16, 2), (64, 16, 16), (128, 12, 4)])
-def test_multi_query_fp8_matches_the_oracle(pa, monkeypatch, d, Hq, Hkv, columns):
-    monkeypatch.setenv("PA_MQ_TILE_COLUMNS", columns)
+def test_multi_query_fp8_matches_the_oracle(pa, d, Hq, Hkv, columns):
+    pa.pa_set_option(pa.PA_OPT_TILE_COLUMNS, int(columns))
     mq = _fp8_case(Hq, Hkv, d, QLENS, NLENS, seed=51)
     p, cfg = mq.paged, mq.paged.cfg
     q = to_dev(mq.query)
@@ -63,10 +63,9 @@ def test_multi_query_fp8_matches_the_oracle(pa, monkeypatch, d, Hq, Hkv, columns
     assert np.abs(got_lse[~dead] - ref_lse[~dead]).max() <= LSE_TOL["bf16"]
 
 
-def test_fp8_decode_through_the_multi_query_kernel(pa, monkeypatch):
+def test_fp8_decode_through_the_multi_query_kernel(pa):
     """pa_decode_fp8 with one token per sequence through the multi-query kernel
     equals the oracle's FP8 decode, empty contexts included."""
-    monkeypatch.setenv("PA_DECODE_KERNEL", "tiles")
     lens = np.array([1, 15, 16, 17, 33, 100, 257, 31, 48, 129, 0], np.int32)
     for d, Hq, Hkv in [(128, 32, 8), (64, 8, 2), (128, 16, 1)]:
         cfg = W.small_case("fp8mq", len(lens), Hq, Hkv, d, "bf16", ("uniform", 1, 2), seed=52, num_blocks=220,

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_helpers import (LSE_TOL, PART_TOL, TOL, Dev, bits, ensure_built, f64, max_err, to_dev)
+from gpu_helpers import (LSE_TOL, PART_TOL, TOL, Dev, bits, ensure_built, f64, forced, max_err, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,19 +22,15 @@ def pa():
     return ensure_built()
 
 
-@pytest.fixture(autouse=True, params=["persistent", "tiles", "tiles4"])
-def decode_kernel(request, monkeypatch):
-    """Run every test here with each decode kernel (the library picks one by
-    batch size; both must give the oracle's answers) — the tile kernel with
-    its own choice of waves per workgroup (8 on these small grids) and with 4
-    forced — and pa_decode_split with the matching cut: pieces on the
-    persistent split kernel, or partitions on the tile kernel."""
-    kernel = "tiles" if request.param.startswith("tiles") else request.param
-    monkeypatch.setenv("PA_DECODE_KERNEL", kernel)
-    monkeypatch.setenv("PA_SPLIT_KERNEL", "pieces" if kernel == "persistent" else "tiles")
-    if request.param == "tiles4":
-        monkeypatch.setenv("PA_MQ_WAVES", "4")
-    return kernel
+@pytest.fixture(autouse=True, params=["tiles_partitions", "tiles4_pieces"])
+def decode_kernel(request, pa):
+    """Run every test here twice: with the tile kernel's own choice of waves
+    per workgroup (8 on these small grids) and pa_decode_split cut into
+    partitions on the tile kernel, then with 4-wave tile workgroups and the
+    split cut into pieces on the persistent split kernel."""
+    opts = dict(split_cut=1) if request.param == "tiles_partitions" else dict(tile_waves=4, split_cut=2)
+    with forced(pa, **opts):
+        yield request.param
 
 
 def _say(msg):
@@ -197,13 +193,13 @@ def test_shape_sweep(pa, dtype, d_h, Hq, Hkv):
 
 @pytest.mark.parametrize("factor", ["auto", "1", "3"])
 @pytest.mark.parametrize("Hq,Hkv", [(16, 4), (24, 12)])
-def test_split_pieces_long_contexts(pa, monkeypatch, decode_kernel, Hq, Hkv, factor):
+def test_split_pieces_long_contexts(pa, decode_kernel, Hq, Hkv, factor):
     """Long contexts cut in many pieces or partitions; for the partition cut,
     partitions of P tokens and of k * P (the library's choice, or forced)."""
     if factor != "auto":
-        if decode_kernel == "persistent":
+        if decode_kernel != "tiles_partitions":
             pytest.skip("the factor applies to the partition cut only")
-        monkeypatch.setenv("PA_SPLIT_PART_FACTOR", factor)
+        pa.pa_set_option(pa.PA_OPT_SPLIT_PART_FACTOR, int(factor))
     cfg = W.small_case("pieces", 5, Hq, Hkv, 128, "bf16", ("uniform", 900, 3000), seed=31, num_blocks=1200,
                        partition_size=64)
     inp = W.make_inputs(cfg)
@@ -349,9 +345,9 @@ def test_seq_order_is_only_a_schedule(pa):
 
 
 def test_many_jobs_per_workgroup(pa):
-    """Far more (sequence, kv head) jobs than resident workgroups: each
-    persistent workgroup walks many jobs, short and empty ones included, and the
-    schedule (natural order, longest first, random) never changes a bit."""
+    """Far more (sequence, kv head) jobs than resident workgroups: many rounds
+    of tile workgroups, short and empty jobs included, and the schedule
+    (natural order, longest first, random) never changes a bit."""
     S = 1100
     cfg = W.small_case("many_jobs", S, 16, 8, 64, "bf16", ("uniform", 1, 40), seed=41, num_blocks=4000)
     inp = W.make_inputs(cfg)
@@ -405,10 +401,10 @@ def test_empty_contexts(pa):
 
 @pytest.mark.parametrize("rows", ["1", "2", "4"])
 @pytest.mark.parametrize("P", [9, 40, 70, 130])
-def test_merge_partitions_alone(pa, monkeypatch, P, rows):
+def test_merge_partitions_alone(pa, P, rows):
     """One batch of partials (9), two (40), the lane-strided log-sum-exps past
     64 (70, 130); 30 rows (a ragged last workgroup at 4 rows each)."""
-    monkeypatch.setenv("PA_MERGE_ROWS", rows)
+    pa.pa_set_option(pa.PA_OPT_MERGE_ROWS, int(rows))
     rng = np.random.default_rng(17)
     S, H, dh = 5, 6, 128
     o = rng.standard_normal((S, H, P, dh)).astype(np.float32)
