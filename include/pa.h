@@ -449,6 +449,37 @@ int pa_decode_split(void* out, const void* query, const void* key_cache, const v
                     float* lse_out, void* stream);
 
 /*
+ * pa_decode_split_noalloc - pa_decode_split without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same arguments,
+ * result and kernels as pa_decode_split, minus workspace / workspace_bytes:
+ * the partials, log-sum-exps and pieces header live in a device array inside
+ * the library, PA_DECODE_SPLIT_NOALLOC_MAX_BYTES large, one per GPU the
+ * library runs on, held until the process ends. No device memory is
+ * allocated or freed by the call (the array's device address is looked up
+ * once per device, on the first call there).
+ *
+ *   Limit: pa_decode_split_workspace_bytes(num_seqs, num_heads, head_size,
+ *          max_context_len, partition_size) must not exceed
+ *          PA_DECODE_SPLIT_NOALLOC_MAX_BYTES; otherwise PA_ERR_WORKSPACE and
+ *          nothing is launched.
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *          last call's contents (nothing in it needs to start at zero). Calls
+ *          whose work overlaps on one GPU (different streams, or other host
+ *          threads) race on it; serialise them (one stream, or events).
+ * Returns PA_OK or an error status (PA_ERR_HIP if the array's address cannot
+ * be found on the current device).
+ */
+#define PA_DECODE_SPLIT_NOALLOC_MAX_BYTES (64u << 20)
+
+int pa_decode_split_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                            int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
+                            int32_t partition_size, float* lse_out, void* stream);
+
+/*
  * pa_decode_split_part_tokens - the cut pa_decode_split makes for these
  * arguments on the current device: the partition length P' (a multiple of
  * partition_size) of the partition cut, 0 for the pieces cut, -1 for invalid

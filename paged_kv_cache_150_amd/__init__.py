@@ -26,6 +26,7 @@ __all__ = [
     "pa_multi_query_split_partition_size",
     "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
     "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_split_part_tokens",
+    "pa_decode_split_noalloc", "PA_DECODE_SPLIT_NOALLOC_MAX_BYTES",
     "pa_merge_partitions", "pa_status_string", "pa_set_option", "pa_get_option", "options",
     "PA_OPT_TILE_WAVES", "PA_OPT_TILE_COLUMNS", "PA_OPT_SPLIT_CUT", "PA_OPT_SPLIT_PART_FACTOR", "PA_OPT_MERGE_ROWS",
 ]
@@ -111,6 +112,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_split.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
                                     c_i32, c_f, c_i32, c_i32, c_i32, c_p, c_sz, c_p, c_p]
     lib.pa_decode_split.restype = c_int
+    lib.pa_decode_split_noalloc.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                            c_i32, c_f, c_i32, c_i32, c_i32, c_p, c_p]
+    lib.pa_decode_split_noalloc.restype = c_int
     lib.pa_merge_partitions.argtypes = [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p]
     lib.pa_merge_partitions.restype = c_int
     lib.pa_status_string.argtypes = [c_int]
@@ -512,6 +516,23 @@ def pa_decode_split(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Ten
     _invoke(lib.pa_decode_split, "pa_decode_split", p["out"], p["query"], p["kc"], p["vc"], p["bt"], MB, p["cl"], S,
             Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), int(max_context_len), int(partition_size), ws,
             nbytes, p["lse"], _stream(stream))
+
+
+PA_DECODE_SPLIT_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def pa_decode_split_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                            value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            scale: float, max_context_len: int, partition_size: int,
+                            lse_out: torch.Tensor | None = None, stream=None) -> None:
+    """pa_decode_split with the library's own per-GPU device array as workspace
+    (no allocation; at most PA_DECODE_SPLIT_NOALLOC_MAX_BYTES of workspace)."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out)
+    lib = load_library()
+    _invoke(lib.pa_decode_split_noalloc, "pa_decode_split_noalloc", p["out"], p["query"], p["kc"], p["vc"], p["bt"],
+            MB, p["cl"], S, Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), int(max_context_len),
+            int(partition_size), p["lse"], _stream(stream))
 
 
 def workspace_views(workspace: torch.Tensor, num_seqs: int, num_heads: int, head_size: int,

@@ -38,6 +38,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_device.h"
@@ -936,23 +937,17 @@ extern "C" size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_
   return split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size, L) ? L.total : 0;
 }
 
-extern "C" int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
-                               const int32_t* block_tables, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                               int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
-                               int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
-                               int32_t partition_size, void* workspace, size_t workspace_bytes,
-                               float* lse_out, void* stream) {
-  int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
-                        num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
-  if (st != PA_OK) return st;
-  if (partition_size <= 0 || partition_size % kBlockTokens != 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PA_OK;
-  SplitLayout L;
-  if (!split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size, L)) return PA_ERR_UNSUPPORTED;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
-  if (workspace_bytes < L.total) return PA_ERR_WORKSPACE;
-  if ((static_cast<size_t>(num_seqs) + 1) * sizeof(int) > 64 * 1024) return PA_ERR_UNSUPPORTED;  // LDS prefix
+namespace {
+
+// The work of pa_decode_split once the arguments and the layout are checked:
+// partials, log-sum-exps and the pieces header go to `workspace`.
+int decode_split_launch(void* out, const void* query, const void* key_cache, const void* value_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                        int64_t num_blocks, float scale, int32_t dtype, int32_t max_context_len,
+                        int32_t partition_size, const SplitLayout& L, void* workspace, float* lse_out,
+                        void* stream) {
+  int st = PA_OK;
 
   SplitArgs args{};
   args.query = query;
@@ -995,6 +990,96 @@ extern "C" int pa_decode_split(void* out, const void* query, const void* key_cac
                               static_cast<int>(cap), pt, num_parts, args.slots, head_size, dtype, s);
   }
   return launch_split(args, dtype, head_size, static_cast<hipStream_t>(stream));
+}
+
+// Host checks shared by pa_decode_split and pa_decode_split_noalloc; on PA_OK
+// with num_seqs > 0, L holds the workspace layout.
+int check_split(const void* out, const void* query, const void* key_cache, const void* value_cache,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                int32_t block_size, int32_t dtype, int32_t max_context_len, int32_t partition_size,
+                SplitLayout& L) {
+  int st = check_common(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % kBlockTokens != 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!split_layout(num_seqs, num_heads, head_size, max_context_len, partition_size, L)) return PA_ERR_UNSUPPORTED;
+  if ((static_cast<size_t>(num_seqs) + 1) * sizeof(int) > 64 * 1024) return PA_ERR_UNSUPPORTED;  // LDS prefix
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                               int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes,
+                               float* lse_out, void* stream) {
+  SplitLayout L;
+  const int st = check_split(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype,
+                             max_context_len, partition_size, L);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return PA_ERR_WORKSPACE;
+  return decode_split_launch(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale, dtype,
+                             max_context_len, partition_size, L, workspace, lse_out, stream);
+}
+
+// ------------------------------------------------------------------ pa_decode_split_noalloc
+// The workspace of pa_decode_split_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in); it passes the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[PA_DECODE_SPLIT_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    p = ptr;
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_split_noalloc(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                                       int32_t block_size, float scale, int32_t dtype, int32_t max_context_len,
+                                       int32_t partition_size, float* lse_out, void* stream) {
+  SplitLayout L;
+  const int st = check_split(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, dtype,
+                             max_context_len, partition_size, L);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (L.total > static_cast<size_t>(PA_DECODE_SPLIT_NOALLOC_MAX_BYTES)) return PA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return PA_ERR_HIP;
+  return decode_split_launch(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                             num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale, dtype,
+                             max_context_len, partition_size, L, ws, lse_out, stream);
 }
 
 extern "C" int pa_merge_partitions(void* out, float* lse_out, const float* o_parts, const float* lse_parts,

@@ -36,7 +36,7 @@ def test_headers_declare_the_boundary():
         "pa_multi_query_split", "pa_multi_query_split_partition_size", "pa_decode_prefix_workspace_bytes",
         "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",
-        "pa_decode_split_part_tokens", "pa_set_option", "pa_get_option"])
+        "pa_decode_split_part_tokens", "pa_set_option", "pa_get_option", "pa_decode_split_noalloc"])
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
         "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
         "pa_pool_allocate", "pa_pool_append_slot", "pa_pool_share", "pa_pool_release",
@@ -114,6 +114,10 @@ def test_split_and_merge_host_validation(lib):
     assert lib.pa_decode_split(*args, 64, 16, None, need, None, None) == 1     # no workspace
     assert lib.pa_decode_split(*args, 64, 16, 272, need, None, None) == 1      # misaligned workspace
     assert lib.pa_decode_split(*args, 64, 16, 256, need - 1, None, None) == 3  # too small
+    n = lib.pa_decode_split_noalloc
+    assert n(*args, 64, 24, None, None) == 1                                  # P % 16 != 0
+    assert n(*args, 1 << 24, 16, None, None) == 3                             # past the array's size
+    assert n(*args[:7], 0, *args[8:], 64, 16, None, None) == 0                # no sequences
     assert lib.pa_merge_partitions(16, None, 16, 16, 2, 8, 0, 128, 1, None) == 1
     assert lib.pa_merge_partitions(16, None, 16, 16, 2, 8, 3, 80, 1, None) == 2
 
