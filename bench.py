@@ -401,7 +401,8 @@ def main():
     out = torch.empty_like(q)
     # The schedule a serving loop would pass: it knows every context length on
     # the host when it builds the block tables.
-    order = up(np.argsort(-inp.context_lens, kind="stable").astype(np.int32)) if args.order == "longest" else None
+    longest = up(np.argsort(-inp.context_lens, kind="stable").astype(np.int32))
+    order = longest if args.order == "longest" else None
     S, Hq, d = cfg.num_seqs, cfg.num_heads, cfg.head_size
     mcl = inp.max_context_len
     ws = torch.empty(max(256, pa.pa_decode_split_workspace_bytes(S, Hq, d, mcl, P),
@@ -410,79 +411,55 @@ def main():
         print(f"bench.py: {cfg.name} has no shared prefix (--decode prefix needs one)", file=sys.stderr)
         sys.exit(2)
     stream = torch.cuda.current_stream()
-
-    def decode(kc, vc):
-        if fp8:
-            pa.pa_decode_fp8(out, q, kc, vc, bt, cl, cfg.scale, cfg.k_scale, cfg.v_scale, seq_order=order,
-                             stream=stream)
-        elif args.decode == "fused":
-            pa.pa_decode(out, q, kc, vc, bt, cl, cfg.scale, seq_order=order, stream=stream)
-        elif args.decode == "prefix":
-            pa.pa_decode_prefix(out, q, kc, vc, bt, cl, cfg.scale, inp.shared_prefix_blocks, ws, seq_order=order,
-                                stream=stream)
-        else:
-            pa.pa_decode_split(out, q, kc, vc, bt, cl, cfg.scale, mcl, P, ws, stream=stream)
-
-    def reshape(kc, vc):
-        if fp8:
-            pa.pa_reshape_and_cache_fp8(new_k, new_v, kc, vc, slots, cfg.k_scale, cfg.v_scale, stream=stream)
-        else:
-            pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slots, stream=stream)
-
-    # The binding's checks run once here; the loops below repeat the bare
-    # library calls (one ctypes call per launch).
     # The plain decode step runs as one launch (pa_reshape_and_decode: the
     # new tokens' write folded into the decode) unless asked otherwise.
     one_launch = args.decode == "fused" and not fp8 and not args.separate_write
-    if one_launch:
-        def fused_step(kc, vc):
-            pa.pa_reshape_and_decode(out, q, new_k, new_v, slots, kc, vc, bt, cl, cfg.scale, seq_order=order,
-                                     stream=stream)
-        reshape_p = [lambda: None, lambda: None]
-        decode_p = [pa.prepared(fused_step, *pools[k]) for k in range(2)]
-    else:
-        reshape_p = [pa.prepared(reshape, *pools[k]) for k in range(2)]
-        decode_p = [pa.prepared(decode, *pools[k]) for k in range(2)]
 
-    def step(i):
-        reshape_p[i & 1]()
-        decode_p[i & 1]()
+    def make_step(kc, vc, tables, slot_map, seq_order):
+        """(write, attend) callables of one step on these buffers; the binding's
+        checks run once here and the calls repeat the bare library calls."""
+        if one_launch:
+            def fused(): pa.pa_reshape_and_decode(out, q, new_k, new_v, slot_map, kc, vc, tables, cl, cfg.scale,
+                                                  seq_order=seq_order, stream=stream)
+            return (lambda: None), pa.prepared(fused)
 
+        def reshape():
+            if fp8:
+                pa.pa_reshape_and_cache_fp8(new_k, new_v, kc, vc, slot_map, cfg.k_scale, cfg.v_scale, stream=stream)
+            else:
+                pa.pa_reshape_and_cache(new_k, new_v, kc, vc, slot_map, stream=stream)
+
+        def decode():
+            if fp8:
+                pa.pa_decode_fp8(out, q, kc, vc, tables, cl, cfg.scale, cfg.k_scale, cfg.v_scale,
+                                 seq_order=seq_order, stream=stream)
+            elif args.decode == "fused":
+                pa.pa_decode(out, q, kc, vc, tables, cl, cfg.scale, seq_order=seq_order, stream=stream)
+            elif args.decode == "prefix":
+                pa.pa_decode_prefix(out, q, kc, vc, tables, cl, cfg.scale, inp.shared_prefix_blocks, ws,
+                                    seq_order=seq_order, stream=stream)
+            else:
+                pa.pa_decode_split(out, q, kc, vc, tables, cl, cfg.scale, mcl, P, ws, stream=stream)
+        return pa.prepared(reshape), pa.prepared(decode)
+
+    steps = [make_step(*pools[k], bt, slots, order) for k in range(2)]
     print(f"[bench] warmup {args.warmup}, timed {args.steps} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i)
+        steps[i & 1][0]()
+        steps[i & 1][1]()
     torch.cuda.synchronize()
 
-    # Two timed passes of `steps` steps each. The step rate comes from a pass
-    # with events only at its two ends (an event between kernels costs GPU
-    # time of its own); the per-launch duration of the decode call (with the
-    # write folded in, for the one-launch step) comes from a second pass with
-    # events around each launch, on the stream the kernels run on.
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # The step rate comes from a pass with events only at its two ends (an
+    # event between kernels costs GPU time of its own); the per-launch
+    # durations of the attention call (with the write folded in, for the
+    # one-launch step) from a second pass with events around each launch, on
+    # the stream the kernels run on.
     wall0 = time.perf_counter()
-    hold_gpu(stream)
-    t_begin.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed_pass(steps, args.steps, stream)
     wall = time.perf_counter() - wall0
-    total_ms = t_begin.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    hold_gpu(stream)
-    for i in range(args.steps):
-        reshape_p[i & 1]()
-        ev[i][0].record(stream)
-        decode_p[i & 1]()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    out_timed = out.clone()
+    dec_ms = per_launch_pass(steps, args.steps, stream)
     dec_avg = statistics.fmean(dec_ms)
-    dec_med = statistics.median(dec_ms)
 
     kv_bytes = W.algorithmic_kv_bytes(cfg, inp.context_lens)
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -499,6 +476,70 @@ def main():
     # are kept as a cross-check.
     launch_ms = ms_per_step if one_launch else dec_avg
     dec_gbs = roof_bytes / (launch_ms * 1e-3) / 1e9
+
+    # What the memory system delivers, measured beside the decode: a plain
+    # streaming read of 1 GiB (two buffers, alternating), and the decode's own
+    # loads without its arithmetic over the same pools and tables.
+    print("[bench] ceilings", file=sys.stderr, flush=True)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    bufs = [torch.ones(1 << 28, dtype=torch.int32, device=dev) for _ in range(2)]
+    reads = [(lambda: None, pa.prepared(pa.pa_stream_read, bufs[k], sink, stream=stream)) for k in range(2)]
+    for i in range(10):
+        reads[i & 1][1]()
+    stream_ms = timed_pass(reads, max(50, args.steps // 2), stream)
+    ceiling_gbs = (1 << 30) / (stream_ms * 1e-3) / 1e9
+    del bufs
+    gathers = [(lambda: None, pa.prepared(pa.pa_stream_kv, *pools[k], bt, cl, sink, seq_order=order,
+                                          stream=stream)) for k in range(2)]
+    for i in range(10):
+        gathers[i & 1][1]()
+    gather_ms = timed_pass(gathers, args.steps, stream)
+    gather_gbs = kv_bytes / (gather_ms * 1e-3) / 1e9
+
+    # The same step in natural sequence order (no seq_order hint), and with
+    # every sequence's blocks laid end to end in the pool (contiguous
+    # placement, the same contents): the cost of the schedule hint's absence
+    # and of scattered placement.
+    extra = {}
+    if args.decode in ("fused", "prefix") and order is not None:
+        nat = [make_step(*pools[k], bt, slots, None) for k in range(2)]
+        for i in range(args.warmup):
+            nat[i & 1][0]()
+            nat[i & 1][1]()
+        nat_ms = timed_pass(nat, args.steps, stream)
+        extra["natural_order"] = {"ms_per_step": round(nat_ms, 5),
+                                  "value": round(kv_bytes / (nat_ms * 1e-3) / 1e9, 1),
+                                  "pct_hbm_peak": round(100 * kv_bytes / (nat_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    ref_ids, tables_c, slots_c = W.contiguous_placement(inp)
+    ids_t = up(ref_ids)
+    cpools = [(pools[k][0].index_select(0, ids_t), pools[k][1].index_select(0, ids_t)) for k in range(2)]
+    bt_c, slots_c_t = up(tables_c), up(slots_c)
+    cont = [make_step(*cpools[k], bt_c, slots_c_t, order) for k in range(2)]
+    for i in range(args.warmup):
+        cont[i & 1][0]()
+        cont[i & 1][1]()
+    cont_ms = timed_pass(cont, args.steps, stream)
+    del cpools
+    extra["placement"] = {"shuffled_ms_per_step": round(ms_per_step, 5), "contiguous_ms_per_step": round(cont_ms, 5),
+                          "shuffled_over_contiguous": round(ms_per_step / cont_ms, 4),
+                          "contiguous_blocks": int(ref_ids.size)}
+
+    # Parity of the timed step's output (the first pass's last step) against
+    # the oracle on the same inputs, computed after all timing.
+    print("[bench] parity of the timed output against the oracle", file=sys.stderr, flush=True)
+    import oracle
+    if fp8:
+        kc_ref, vc_ref = oracle.reshape_and_cache_fp8(inp.new_key, inp.new_value, inp.key_cache, inp.value_cache,
+                                                      inp.slot_mapping, cfg.k_scale, cfg.v_scale)
+        ref, _ = oracle.paged_decode_fp8(inp.query, kc_ref, vc_ref, inp.block_tables, inp.context_lens, cfg.scale,
+                                         cfg.k_scale, cfg.v_scale)
+        del kc_ref, vc_ref
+    else:
+        ref, _ = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
+                                     cfg.scale, cfg.dtype)
+    parity_err = float(np.abs(out_timed.float().cpu().numpy().astype(np.float64) - ref).max())
+    tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
+
     traffic = stored_traffic(cfg.name, args.decode + ("_separate" if args.separate_write else ""))
     one = "paged_multi_query_kernel (one token per sequence)"
     if one_launch:
@@ -508,6 +549,7 @@ def main():
         split_label = "paged_multi_query_kernel (context partitions) + merge_parts_kernel"
     kernel_label = {"fused": one, "split": split_label,
                     "prefix": "paged_multi_query_kernel (shared prefix) + " + one}[args.decode]
+    pct = lambda v: round(float(np.percentile(dec_ms, v)), 5)  # noqa: E731
     rec = {
         "metric": "paged decode attention effective KV GB/s (% of HBM peak) + seqs/sec, 1 GPU",
         "value": round(step_gbs, 1),
@@ -536,7 +578,9 @@ def main():
         "seqs_per_s": round(S / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "decode_ms_avg": round(dec_avg, 5),
-        "decode_ms_median": round(dec_med, 5),
+        "decode_ms_median": round(statistics.median(dec_ms), 5),
+        "decode_ms_p10": pct(10),
+        "decode_ms_p90": pct(90),
         "launch_ms": round(launch_ms, 5),
         "launch_timing": ("timed region / steps (one launch per step)" if one_launch
                           else "HIP events around each launch"),
@@ -545,14 +589,56 @@ def main():
                      "traffic": traffic,
                      "kernel": kernel_label,
                      "algorithmic_bytes_per_launch": roof_bytes,
+                     "measured_ceiling_gbs": round(ceiling_gbs, 1),
+                     "measured_ceiling": "pa_stream_read: 1 GiB read once, contiguous range per workgroup, "
+                                         "non-temporal 16-byte loads",
+                     "frac_of_measured_ceiling": round(dec_gbs / ceiling_gbs, 4),
+                     "access_pattern_ceiling_gbs": round(gather_gbs, 1),
+                     "access_pattern_ceiling": "pa_stream_kv: the one-pass decode's K/V loads over the same "
+                                               "pools and tables, no arithmetic (GB/s of algorithmic KV bytes)",
+                     "decode_time_over_access_pattern_time": round(launch_ms / gather_ms, 4),
                      "kernel_source_hash": kernel_source_hash()},
+        "parity_max_abs_err": parity_err,
+        "parity_tolerance": tol,
+        "parity_ok": bool(parity_err <= tol),
         "wall_s_timed": round(wall, 4),  # includes the spin kernel queued ahead of the timed steps
     }
+    rec.update(extra)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
+
+def timed_pass(steps, n, stream) -> float:
+    """Average ms per step of n steps (write then attend, alternating between
+    the two entries of `steps`) queued back to back behind a spin kernel, with
+    events only at the two ends."""
+    import torch
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    hold_gpu(stream)
+    t0.record(stream)
+    for i in range(n):
+        steps[i & 1][0]()
+        steps[i & 1][1]()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
+def per_launch_pass(steps, n, stream) -> list:
+    """ms of each attention launch of n steps, from events around it."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    hold_gpu(stream)
+    for i in range(n):
+        steps[i & 1][0]()
+        ev[i][0].record(stream)
+        steps[i & 1][1]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
 
 if __name__ == "__main__":
     main()

@@ -26,7 +26,7 @@ __all__ = [
     "pa_multi_query_split_partition_size",
     "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
     "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_decode_split_part_tokens",
-    "pa_decode_split_noalloc", "PA_DECODE_SPLIT_NOALLOC_MAX_BYTES",
+    "pa_decode_split_noalloc", "PA_DECODE_SPLIT_NOALLOC_MAX_BYTES", "pa_stream_read", "pa_stream_kv",
     "pa_merge_partitions", "pa_status_string", "pa_set_option", "pa_get_option", "options",
     "PA_OPT_TILE_WAVES", "PA_OPT_TILE_COLUMNS", "PA_OPT_SPLIT_CUT", "PA_OPT_SPLIT_PART_FACTOR", "PA_OPT_MERGE_ROWS",
 ]
@@ -115,6 +115,10 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_split_noalloc.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i64,
                                             c_i32, c_f, c_i32, c_i32, c_i32, c_p, c_p]
     lib.pa_decode_split_noalloc.restype = c_int
+    lib.pa_stream_read.argtypes = [c_p, c_sz, c_p, c_p]
+    lib.pa_stream_read.restype = c_int
+    lib.pa_stream_kv.argtypes = [c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i64, c_i32, c_i32, c_p, c_p, c_p]
+    lib.pa_stream_kv.restype = c_int
     lib.pa_merge_partitions.argtypes = [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p]
     lib.pa_merge_partitions.restype = c_int
     lib.pa_status_string.argtypes = [c_int]
@@ -573,3 +577,36 @@ def pa_merge_partitions(out: torch.Tensor, o_parts: torch.Tensor, lse_parts: tor
     _invoke(lib.pa_merge_partitions, "pa_merge_partitions", _dev(out, "out"), lse_ptr,
             _dev(o_parts, "o_parts", torch.float32), _dev(lse_parts, "lse_parts", torch.float32), S, H, P, d,
             _dtype_code(out), _stream(stream))
+
+
+# ------------------------------------------------------------------ measurement kernels (include/pa_measure.h)
+def pa_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of ``src`` once (the plain streaming-read ceiling); ``sink`` is int32 [>= 1]."""
+    nbytes = src.numel() * src.element_size()
+    lib = load_library()
+    _invoke(lib.pa_stream_read, "pa_stream_read", _dev(src, "src"), nbytes, _dev(sink, "sink", torch.int32),
+            _stream(stream))
+
+
+def pa_stream_kv(key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, sink: torch.Tensor, seq_order: torch.Tensor | None = None,
+                 stream=None) -> None:
+    """The K/V loads of pa_decode on these tables without its arithmetic (the
+    decode's access-pattern ceiling); uint8 caches are FP8."""
+    NB, bs, Hkv, d = _cache_dims(key_cache, value_cache)
+    kind = {torch.float32: 0, torch.bfloat16: 1, torch.uint8: 2}.get(key_cache.dtype)
+    if kind is None:
+        raise TypeError(f"unsupported cache dtype {key_cache.dtype}")
+    if block_tables.dim() != 2 or context_lens.shape != (int(block_tables.shape[0]),):
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq] and context_lens [num_seqs]")
+    S = int(block_tables.shape[0])
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.shape != (S,):
+            raise ValueError("seq_order must be [num_seqs]")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
+    lib = load_library()
+    _invoke(lib.pa_stream_kv, "pa_stream_kv", _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(block_tables, "block_tables", torch.int32, 2), int(block_tables.shape[1]),
+            _dev(context_lens, "context_lens", torch.int32, 1), S, Hkv, d, NB, bs, kind, order_ptr,
+            _dev(sink, "sink", torch.int32), _stream(stream))

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["paged_decode.hip", "multi_query.hip", "cache_ops.hip", "block_pool.cpp"]
+SOURCES = ["paged_decode.hip", "multi_query.hip", "cache_ops.hip", "measure.hip", "block_pool.cpp"]
 
 
 def hipcc() -> str:

@@ -37,6 +37,7 @@ def test_headers_declare_the_boundary():
         "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",
         "pa_decode_split_part_tokens", "pa_set_option", "pa_get_option", "pa_decode_split_noalloc"])
+    assert declared_functions(os.path.join(inc, "pa_measure.h")) == ["pa_stream_kv", "pa_stream_read"]
     assert declared_functions(os.path.join(inc, "pa_pool.h")) == sorted([
         "pa_pool_create", "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count", "pa_pool_blocks_for",
         "pa_pool_allocate", "pa_pool_append_slot", "pa_pool_share", "pa_pool_release",
@@ -120,6 +121,18 @@ def test_split_and_merge_host_validation(lib):
     assert n(*args[:7], 0, *args[8:], 64, 16, None, None) == 0                # no sequences
     assert lib.pa_merge_partitions(16, None, 16, 16, 2, 8, 0, 128, 1, None) == 1
     assert lib.pa_merge_partitions(16, None, 16, 16, 2, 8, 3, 80, 1, None) == 2
+
+
+def test_measure_host_validation(lib):
+    assert lib.pa_stream_read(16, 0, 16, None) == 0                      # nothing to read
+    assert lib.pa_stream_read(16, 24, 16, None) == 1                     # not a multiple of 16
+    assert lib.pa_stream_read(8, 32, 16, None) == 1                      # misaligned
+    assert lib.pa_stream_read(16, 32, None, None) == 1                   # no sink
+    f = lib.pa_stream_kv
+    assert f(16, 16, 16, 4, 16, 0, 8, 128, 10, 16, 1, None, 16, None) == 0   # no sequences
+    assert f(16, 16, 16, 4, 16, 2, 8, 128, 10, 16, 3, None, 16, None) == 1   # cache kind
+    assert f(16, 16, 16, 4, 16, 2, 8, 96, 10, 16, 1, None, 16, None) == 2    # head size
+    assert f(16, 16, 16, 4, 16, 2, 8, 128, 10, 16, 1, None, None, None) == 1  # no sink
 
 
 def test_reshape_host_validation(lib):

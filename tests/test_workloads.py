@@ -115,3 +115,22 @@ def test_multi_query_lengths(name):
         _, m, c, ctx = cfg.new_tokens
         assert (q[:m] == c).all() and (n[:m] == ctx).all() and (q[m:] == 1).all()
     np.testing.assert_array_equal(W.multi_lengths(cfg)[0], n)   # deterministic
+
+
+def test_contiguous_placement_keeps_every_context():
+    """Laying the blocks end to end renumbers them only: the oracle's decode is
+    bit-identical, the new ids are 0..k-1, and every slot lands in its block."""
+    import oracle
+    for name in ("tiny_f32", "prefix_70b"):
+        cfg = W.CONFIG_BY_NAME[name]
+        inp = W.make_inputs(cfg)
+        ids, tables, slots = W.contiguous_placement(inp)
+        assert sorted(set(tables[tables >= 0].ravel().tolist())) == list(range(ids.size))
+        ok = inp.slot_mapping >= 0
+        np.testing.assert_array_equal(ids[slots[ok] // 16], inp.slot_mapping[ok] // 16)
+        np.testing.assert_array_equal(slots[ok] % 16, inp.slot_mapping[ok] % 16)
+        a = oracle.paged_decode(inp.query, inp.key_cache, inp.value_cache, inp.block_tables, inp.context_lens,
+                                cfg.scale, cfg.dtype)[0]
+        b = oracle.paged_decode(inp.query, inp.key_cache[ids], inp.value_cache[ids], tables, inp.context_lens,
+                                cfg.scale, cfg.dtype)[0]
+        np.testing.assert_array_equal(a, b)

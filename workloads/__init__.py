@@ -369,6 +369,25 @@ def caches_before_write(inp: PagedInputs):
     return kc, vc
 
 
+def contiguous_placement(inp: PagedInputs):
+    """The same contexts with their blocks laid end to end from block 0, in
+    allocation order (a shared prefix first, then each sequence's own blocks
+    in logical order): returns (ids, tables, slots) where block k of the new
+    pool is block ids[k] of the old one, and tables / slots are the workload's
+    block tables and slot mapping in the new numbering (-1 kept)."""
+    bs = inp.cfg.block_size
+    ids = np.asarray(inp.referenced_blocks, dtype=np.int64)
+    remap = np.full(inp.cfg.num_blocks, -1, dtype=np.int64)
+    remap[ids] = np.arange(ids.size)
+    bt = inp.block_tables
+    tables = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    s = inp.slot_mapping
+    ok = s >= 0
+    slots = np.full_like(s, -1)
+    slots[ok] = remap[s[ok] // bs] * bs + s[ok] % bs
+    return ids, tables, slots
+
+
 def algorithmic_kv_bytes(cfg: PagedConfig, context_lens: np.ndarray) -> int:
     """K and V bytes one decode call must read: sum_i n_i * 2 * H_kv * d_h * b."""
     return int(np.asarray(context_lens, dtype=np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_size * cfg.kv_elem_bytes
