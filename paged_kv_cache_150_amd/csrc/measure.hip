@@ -72,7 +72,8 @@ __device__ __forceinline__ uint32_t fold_chunk(const Chunk<T, D, 16, CB, F8>& f)
 // The tile kernel's decode mode (paged_multi_query_kernel with one new token
 // per sequence) with the arithmetic taken out: the same workgroup per
 // (sequence, kv head) in the same dispatch order, chunk c of CB blocks to wave
-// c % W, one chunk of look-ahead in registers, the same loads (load_chunk).
+// c % W, one chunk of look-ahead in registers, the same non-temporal loads
+// (load_chunk).
 template <typename T, int D, int CB, bool F8, int W>
 __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void stream_kv_kernel(StreamKvArgs a) {
   using S = DecodeShape<T, D, 16, CB, F8>;
@@ -104,23 +105,23 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void stream_kv_kernel(St
   uint32_t acc = 0;
   Chunk<T, D, 16, CB, F8> fa, fb;
   if (mine > 0) {
-    load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
+    load_chunk<T, D, 16, CB, F8, true>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
                                  head_off, lane, last_rows);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
-      load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, 16, CB, F8, true>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
                                    blk_stride, head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
       acc ^= fold_chunk<T, D, CB, F8>(fa);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, 16, CB, F8, true>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride,
                                    blk_stride, head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
       acc ^= fold_chunk<T, D, CB, F8>(fb);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
-      load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, 16, CB, F8, true>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
                                    blk_stride, head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
       acc ^= fold_chunk<T, D, CB, F8>(fa);

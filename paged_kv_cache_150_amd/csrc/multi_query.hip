@@ -362,6 +362,7 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // The tile reads keys [16 * blk_begin, key_end); column p of this lane sees
   // keys below lim[p]; min_lim is the smallest limit of the tile's columns.
   int seq, q0, tok0, ntok, key_end, min_lim, blk_begin = 0, part = -1;
+  int ntiles_seq = 0;  // tiles of this tile's sequence (0 in the shared-prefix pass)
   int lim[NT];
   if (a.prefix_keys > 0) {
     // Shared-prefix pass: tile `slot` of the queries, all over row 0's prefix.
@@ -425,6 +426,7 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     if (ql <= 0) return;
     const int ntiles = (ql + a.tile_tokens - 1) / a.tile_tokens;
     if (r < 0 || r >= ntiles) return;
+    ntiles_seq = ntiles;
     // Later tiles see longer contexts: they take the lower slots of the sequence.
     const int tile = ntiles - 1 - r;
     tok0 = tile * a.tile_tokens;                               // first new token of the tile
@@ -545,27 +547,33 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // Register double buffer with unconditional steady-state loads and a peeled
   // tail, as in the decode kernel. For new tokens of one sequence only a
   // wave's last chunk can need a mask; in the shared-prefix pass columns may
-  // stop anywhere, so every chunk checks.
-  Chunk<T, D, 16, CB, F8> fa, fb;
-  if (mine > 0) {
-    load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
-                             head_off, lane, last_rows);
+  // stop anywhere, so every chunk checks. Keys that no other workgroup reads
+  // (a sequence's only tile, and never the shared prefix) are streamed with
+  // non-temporal loads; the keys of a sequence cut into several tiles stay
+  // cached for its other tiles.
+  const bool stream_keys = a.prefix_keys == 0 && ntiles_seq == 1;
+  auto run_chunks = [&](auto stream_tag) {
+    constexpr bool kStream = decltype(stream_tag)::value;
+    Chunk<T, D, 16, CB, F8> fa, fb;
+    auto load = [&](Chunk<T, D, 16, CB, F8>& f, int i) {
+      load_chunk<T, D, 16, CB, F8, kStream>(f, kc, vc, bt_row, blk_of(i), blk_last, a.num_blocks, tok_stride,
+                                            blk_stride, head_off, lane, last_rows);
+    };
+    if (mine <= 0) return;
+    load(fa, 0);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
-      load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
-                               head_off, lane, last_rows);
+      load(fb, i + 1);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk<T, D, 16, CB, F8>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride, blk_stride,
-                               head_off, lane, last_rows);
+      load(fa, i + 2);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
-      load_chunk<T, D, 16, CB, F8>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride, blk_stride,
-                               head_off, lane, last_rows);
+      load(fb, i + 1);
       __builtin_amdgcn_sched_barrier(0);
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
       if constexpr (kFusedWrite) {
@@ -578,7 +586,11 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
       }
       mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
     }
-  }
+  };
+  if (stream_keys)
+    run_chunks(std::true_type{});
+  else
+    run_chunks(std::false_type{});
   if (kFusedWrite && own_new) {
     // The new token's slice to its slot (the lanes that hold it).
     typedef __attribute__((address_space(1))) char gwchar_t;

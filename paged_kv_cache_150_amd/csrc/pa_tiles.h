@@ -35,8 +35,8 @@ struct Chunk {
 // 32-bit per-lane offset. Block blk_last holds only last_rows valid rows: its
 // lanes for later rows read the last valid row again (same lines, no extra
 // memory traffic); those rows are masked out by the caller (16-bit and FP8
-// caches).
-template <typename T, int D, int G, int CB, bool F8 = false>
+// caches). STREAM: non-temporal loads (data no other workgroup reads again).
+template <typename T, int D, int G, int CB, bool F8 = false, bool STREAM = false>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
                                            const int32_t* bt_row, int blk0, int blk_last,
                                            int64_t num_blocks, uint32_t tok_stride_bytes,
@@ -64,21 +64,21 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
     if constexpr (S::kElemBytes <= 2) {
       const uint32_t ko = last ? koff_last : koff;
 #pragma unroll
-      for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + ko);
+      for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16s<STREAM>(kb + s * 64 + ko);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // V: rows 4j + r, piece tok.
         const int row = last ? min(4 * j + r, lr) : 4 * j + r;
-        load_dwords<S::kVDw>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
+        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
       }
     } else {
       // fp32 caches (the small workloads) read whole blocks: the per-row
       // offsets would spill registers there.
 #pragma unroll
-      for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16(kb + s * 64 + koff);
+      for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16s<STREAM>(kb + s * 64 + koff);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        load_dwords<S::kVDw>(f.v[i][r], vb + r * tok_stride_bytes + voff);
+        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + r * tok_stride_bytes + voff);
     }
   }
 }

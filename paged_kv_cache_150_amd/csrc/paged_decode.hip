@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * kMaxHeadsPerGroup, 1) void paged_decode_split_
   u32x4_t q[S::kKSeg];
   load_query<T, D, G, CB>(a.query, cur.seq, a.num_heads, (live(cur) ? cur.kvh : 0) * g, g, lane, q);
   Chunk<T, D, G, CB> fa, fb;
-  load_chunk<T, D, G, CB>(fa, kc, vc, bt_row(cur.seq), cur.b_lo, cur.b_hi - 1, a.num_blocks, tok_stride,
+  load_chunk<T, D, G, CB, false, true>(fa, kc, vc, bt_row(cur.seq), cur.b_lo, cur.b_hi - 1, a.num_blocks, tok_stride,
                           blk_stride, head_off(cur), lane);
   PieceCursor nx = cur;
   cursor_next<CB>(nx, a, s_pre, nblk, R, wave);
@@ -429,13 +429,14 @@ __global__ __launch_bounds__(64 * kMaxHeadsPerGroup, 1) void paged_decode_split_
   // The lookahead load is issued unconditionally inside the loop (the exit
   // test comes first), so the hardware wait before the current chunk's use
   // leaves the lookahead in flight; the scheduling barriers keep the loads
-  // ahead of the arithmetic.
+  // ahead of the arithmetic. Every block is read by one wave only, so the
+  // loads are non-temporal.
   auto advance = [&](Chunk<T, D, G, CB>& fcur, Chunk<T, D, G, CB>& fnext) -> bool {
     if (nx.x < 0) {
       compute(fcur);
       return false;
     }
-    load_chunk<T, D, G, CB>(fnext, kc, vc, bt_row(nx.seq), nx.b_lo + nx.c * CB, nx.b_hi - 1, a.num_blocks,
+    load_chunk<T, D, G, CB, false, true>(fnext, kc, vc, bt_row(nx.seq), nx.b_lo + nx.c * CB, nx.b_hi - 1, a.num_blocks,
                             tok_stride, blk_stride, head_off(nx), lane);
     __builtin_amdgcn_sched_barrier(0);
     compute(fcur);
