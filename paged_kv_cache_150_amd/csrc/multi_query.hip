@@ -153,11 +153,13 @@ __device__ __forceinline__ uint32_t pick_bf16(const uint32_t* ra, const uint32_t
   return __builtin_amdgcn_perm(rb[T_ / 2], ra[T_ / 2], (T_ & 1) ? 0x07060302u : 0x05040100u);
 }
 
-template <typename T, int D, int CB, int NT, bool F8>
+// One chunk of the online softmax and P*V. MASK: the chunk reaches past some
+// column's last visible key (a compile-time choice, so the chunks that need no
+// mask carry none of its selects).
+template <typename T, int D, int CB, int NT, bool F8, bool MASK>
 __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<T, D, 16, CB, F8>& f,
                                          const u32x4_t (&q)[NT][DecodeShape<T, D, 16, CB, F8>::kQSeg],
-                                         float scale_log2, int tok0, const int (&lim)[NT], int key_end,
-                                         bool mask, int lane) {
+                                         float scale_log2, int tok0, const int (&lim)[NT], int key_end, int lane) {
   using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kTiles = D / 16;
   const int rg = lane >> 4;
@@ -172,7 +174,7 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
   float s[NT][CB][4];
 #pragma unroll
   for (int p = 0; p < NT; ++p) qk_chunk<T, D, 16, CB, F8>(s[p], f, q[p], 1.0f);
-  if (mask) {
+  if constexpr (MASK) {
     // Keys at or past the tile's last position: weight 0 for every column,
     // and their V rows (possibly stale or poisoned) are replaced by 0.
 #pragma unroll
@@ -362,7 +364,6 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // The tile reads keys [16 * blk_begin, key_end); column p of this lane sees
   // keys below lim[p]; min_lim is the smallest limit of the tile's columns.
   int seq, q0, tok0, ntok, key_end, min_lim, blk_begin = 0, part = -1;
-  int ntiles_seq = 0;  // tiles of this tile's sequence (0 in the shared-prefix pass)
   int lim[NT];
   if (a.prefix_keys > 0) {
     // Shared-prefix pass: tile `slot` of the queries, all over row 0's prefix.
@@ -426,7 +427,6 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     if (ql <= 0) return;
     const int ntiles = (ql + a.tile_tokens - 1) / a.tile_tokens;
     if (r < 0 || r >= ntiles) return;
-    ntiles_seq = ntiles;
     // Later tiles see longer contexts: they take the lower slots of the sequence.
     const int tile = ntiles - 1 - r;
     tok0 = tile * a.tile_tokens;                               // first new token of the tile
@@ -462,13 +462,9 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   const int nchunk = blk_end > blk_begin ? (blk_end - blk_begin + CB - 1) / CB : 0;
   const int blk_last = blk_end - 1;
   const int last_rows = key_end - blk_last * kBlockTokens;  // valid rows of the last block
-  // Chunks from mask_from on reach past some column's last visible key.
-  constexpr int kChunkTokens = CB * kBlockTokens;
-  const int mask_from = max(min_lim - blk_begin * kBlockTokens, 0) / kChunkTokens;
   const int mine = wave < nchunk ? (nchunk - wave + kMqWaves - 1) / kMqWaves : 0;
   auto blk_of = [&](int i) { return blk_begin + (wave + i * kMqWaves) * CB; };
   auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
-  auto is_mask = [&](int i) { return wave + i * kMqWaves >= mask_from; };
 
   // Decode with the new token's write folded in. Every lane loads its pieces
   // of the new K/V row up front (no dependence on anything else). When the
@@ -547,17 +543,32 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // Register double buffer with unconditional steady-state loads and a peeled
   // tail, as in the decode kernel. For new tokens of one sequence only a
   // wave's last chunk can need a mask; in the shared-prefix pass columns may
-  // stop anywhere, so every chunk checks. Keys that no other workgroup reads
-  // (a sequence's only tile, and never the shared prefix) are streamed with
-  // non-temporal loads; the keys of a sequence cut into several tiles stay
-  // cached for its other tiles.
-  const bool stream_keys = a.prefix_keys == 0 && ntiles_seq == 1;
-  auto run_chunks = [&](auto stream_tag) {
+  // stop anywhere, so every chunk checks. A decode launch (one new token per
+  // sequence, whole contexts or partitions) reads every key once and streams
+  // it with non-temporal loads; multi-query launches keep plain loads (the
+  // keys of a sequence cut into several tiles are re-read from L2 by its other
+  // tiles: the batch-256 step with a 1,024-token chunk ran 255 vs 238 us with
+  // its one-tile sequences streamed), and so do both passes of the
+  // shared-prefix decode (the suffix pass measured 55.5 vs 57.8 us per step on
+  // the 70B-shaped workload).
+  const bool stream_keys = a.query_start_loc == nullptr && a.prefix_keys == 0 && a.prefix_o == nullptr;
+  // Chunk i of this wave with the mask applied or not (compile time). In a
+  // decode or multi-query launch only a wave's last chunk can reach past some
+  // column's limit, so the loop below runs the unmasked chunk everywhere else
+  // (no selects) and the masked one last. In the shared-prefix pass a column
+  // may stop anywhere when a context is shorter than the prefix; such tiles
+  // (min_lim < key_end) mask every chunk.
+  auto run_chunks = [&](auto stream_tag, auto all_masked_tag) {
     constexpr bool kStream = decltype(stream_tag)::value;
+    constexpr bool kAllMasked = decltype(all_masked_tag)::value;
     Chunk<T, D, 16, CB, F8> fa, fb;
     auto load = [&](Chunk<T, D, 16, CB, F8>& f, int i) {
       load_chunk<T, D, 16, CB, F8, kStream>(f, kc, vc, bt_row, blk_of(i), blk_last, a.num_blocks, tok_stride,
                                             blk_stride, head_off, lane, last_rows);
+    };
+    auto compute = [&](const Chunk<T, D, 16, CB, F8>& f, int i, auto mask_tag) {
+      mq_chunk<T, D, CB, NT, F8, decltype(mask_tag)::value || kAllMasked>(st, f, q, a.scale_log2, tok_of(i), lim,
+                                                                          key_end, lane);
     };
     if (mine <= 0) return;
     load(fa, 0);
@@ -565,32 +576,34 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     for (; i + 2 < mine; i += 2) {
       load(fb, i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      compute(fa, i, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       load(fa, i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
+      compute(fb, i + 1, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
       load(fb, i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      compute(fa, i, std::false_type{});
       if constexpr (kFusedWrite) {
         if (patch_own) patch_new(fb);
       }
-      mq_chunk<T, D, CB, NT, F8>(st, fb, q, a.scale_log2, tok_of(i + 1), lim, key_end, is_mask(i + 1), lane);
+      compute(fb, i + 1, std::true_type{});
     } else {
       if constexpr (kFusedWrite) {
         if (patch_own) patch_new(fa);
       }
-      mq_chunk<T, D, CB, NT, F8>(st, fa, q, a.scale_log2, tok_of(i), lim, key_end, is_mask(i), lane);
+      compute(fa, i, std::true_type{});
     }
   };
   if (stream_keys)
-    run_chunks(std::true_type{});
+    run_chunks(std::true_type{}, std::false_type{});
+  else if (a.prefix_keys > 0 && min_lim < key_end)
+    run_chunks(std::false_type{}, std::true_type{});
   else
-    run_chunks(std::false_type{});
+    run_chunks(std::false_type{}, std::false_type{});
   if (kFusedWrite && own_new) {
     // The new token's slice to its slot (the lanes that hold it).
     typedef __attribute__((address_space(1))) char gwchar_t;
