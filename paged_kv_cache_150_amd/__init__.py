@@ -53,7 +53,9 @@ class PaError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libpa.so")
+    """The in-tree libpa.so, or the file PA_LIBRARY names (the host-sanitizer
+    build of the tests uses this)."""
+    return os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 
 def load_library() -> ctypes.CDLL:

@@ -61,5 +61,54 @@ def build_library(extra_flags: list[str] | None = None, verbose: bool = False) -
     return LIB
 
 
+# Host-code sanitizers: the host side of every source (argument checks, the
+# block pool, launch set-up) built with AddressSanitizer and
+# UndefinedBehaviorSanitizer; device code is built as usual. The library
+# needs the shared ASan runtime preloaded into the process that loads it
+# (asan_runtime()).
+SAN_BUILD = os.path.join(PKG, "_build_san")
+SAN_LIB = os.path.join(SAN_BUILD, "libpa_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-shared-libasan", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of hipcc's clang."""
+    import glob
+    root = os.path.dirname(os.path.dirname(hipcc()))
+    for cand in sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                              "libclang_rt.asan-x86_64.so"))):
+        return cand
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found next to hipcc")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Compile every source with host sanitizers into _build_san/libpa_san.so."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(SAN_BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
+        cmd = [hipcc(), *COMPILE_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        return obj
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan",
+           "-o", SAN_LIB + ".tmp", *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}", file=sys.stderr)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build_library(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitized":
+        build_sanitized(verbose=True)
+    else:
+        build_library(verbose=True)
