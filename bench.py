@@ -430,14 +430,19 @@ def main():
     stream = torch.cuda.current_stream()
     # The plain decode step runs as one launch (pa_reshape_and_decode: the
     # new tokens' write folded into the decode) unless asked otherwise.
-    one_launch = args.decode == "fused" and not fp8 and not args.separate_write
+    one_launch = args.decode == "fused" and not args.separate_write
 
     def make_step(kc, vc, tables, slot_map, seq_order):
         """(write, attend) callables of one step on these buffers; the binding's
         checks run once here and the calls repeat the bare library calls."""
         if one_launch:
-            def fused(): pa.pa_reshape_and_decode(out, q, new_k, new_v, slot_map, kc, vc, tables, cl, cfg.scale,
-                                                  seq_order=seq_order, stream=stream)
+            def fused():
+                if fp8:
+                    pa.pa_reshape_and_decode_fp8(out, q, new_k, new_v, slot_map, kc, vc, tables, cl, cfg.scale,
+                                                 cfg.k_scale, cfg.v_scale, seq_order=seq_order, stream=stream)
+                else:
+                    pa.pa_reshape_and_decode(out, q, new_k, new_v, slot_map, kc, vc, tables, cl, cfg.scale,
+                                             seq_order=seq_order, stream=stream)
             return (lambda: None), pa.prepared(fused)
 
         def reshape():
@@ -484,8 +489,11 @@ def main():
     # roofline is priced on the unique bytes.
     roof_bytes = W.unique_kv_bytes(inp) if args.decode == "prefix" else kv_bytes
     if one_launch:
-        # The launch also reads the new tokens' K/V and writes them to their slots.
-        roof_bytes += 4 * int(np.count_nonzero(inp.slot_mapping >= 0)) * cfg.num_kv_heads * d * cfg.kv_elem_bytes
+        # The launch also reads the new tokens' K/V (query dtype) and writes
+        # them to their slots (cache dtype).
+        in_bytes = 2 if cfg.dtype == "bf16" else 4
+        roof_bytes += (2 * in_bytes + 2 * cfg.kv_elem_bytes) * int(np.count_nonzero(inp.slot_mapping >= 0)) \
+            * cfg.num_kv_heads * d
     # With one launch per step the first pass, timed at its two ends over
     # launches queued back to back on the kernel's stream, gives the kernel's
     # average launch duration directly (any gap between launches counts
@@ -587,7 +595,8 @@ def main():
                    "seq_order": args.order if args.decode in ("fused", "prefix") else None,
                    "prefix_blocks": inp.shared_prefix_blocks if args.decode == "prefix" else None,
                    "kv_cache": cfg.cache_dtype, "options": forced or None,
-                   "step": ("pa_reshape_and_cache_fp8 + pa_decode_fp8" if fp8 else
+                   "step": ("pa_reshape_and_decode_fp8 (one launch)" if fp8 and one_launch else
+                            "pa_reshape_and_cache_fp8 + pa_decode_fp8" if fp8 else
                             "pa_reshape_and_decode (one launch)" if one_launch else
                             "pa_reshape_and_cache + " + {"fused": "pa_decode", "split": "pa_decode_split",
                                                          "prefix": "pa_decode_prefix"}[args.decode])},

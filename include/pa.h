@@ -136,6 +136,22 @@ int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache, const 
                   const int32_t* seq_order, void* stream);
 
 /*
+ * pa_reshape_and_decode_fp8 - pa_reshape_and_cache_fp8 of one decode step's
+ * new tokens followed by pa_decode_fp8, in one launch: the FP8 counterpart of
+ * pa_reshape_and_decode (same three slot cases). key, value [num_seqs, H_kv,
+ * head_size] are bf16 (dtype PA_DTYPE_BF16, like query and out); each row is
+ * quantized with k_scale / v_scale exactly as pa_reshape_and_cache_fp8 does,
+ * written to slot_mapping[i], and used as position n - 1's codes when the
+ * slot is that position's. Other arguments as pa_decode_fp8.
+ */
+int pa_reshape_and_decode_fp8(void* out, const void* query, const void* key, const void* value,
+                              const int64_t* slot_mapping, uint8_t* key_cache, uint8_t* value_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                              int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                              int32_t dtype, float* lse_out, const int32_t* seq_order, void* stream);
+
+/*
  * pa_copy_blocks - whole-block copies: the GPU half of copy-on-write.
  *
  * When a sequence must write into a block that others still read, it gets a

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "PA_DTYPE_F32", "PA_DTYPE_BF16", "PaError", "library_path", "load_library", "prepared",
     "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
-    "pa_reshape_and_decode",
+    "pa_reshape_and_decode", "pa_reshape_and_decode_fp8",
     "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes", "pa_multi_query_split",
     "pa_multi_query_split_partition_size",
     "pa_decode_prefix_workspace_bytes", "pa_decode_prefix",
@@ -88,6 +88,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_reshape_and_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32,
                                           c_i32, c_i64, c_i32, c_f, c_i32, c_p, c_p, c_p]
     lib.pa_reshape_and_decode.restype = c_int
+    lib.pa_reshape_and_decode_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32,
+                                              c_i32, c_i32, c_i64, c_i32, c_f, c_f, c_f, c_i32, c_p, c_p, c_p]
+    lib.pa_reshape_and_decode_fp8.restype = c_int
     lib.pa_set_option.argtypes = [c_int, c_int]
     lib.pa_set_option.restype = c_int
     lib.pa_get_option.argtypes = [c_int]
@@ -464,6 +467,33 @@ def pa_reshape_and_decode(out: torch.Tensor, query: torch.Tensor, key: torch.Ten
             _dev(value, "value"), _dev(slot_mapping, "slot_mapping", torch.int64, 1), p["kc"], p["vc"], p["bt"],
             MB, p["cl"], S, Hq, Hkv, d, NB, bs, float(scale), _dtype_code(query), p["lse"], order_ptr,
             _stream(stream))
+
+
+def pa_reshape_and_decode_fp8(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                              slot_mapping: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, k_scale: float,
+                              v_scale: float, lse_out: torch.Tensor | None = None,
+                              seq_order: torch.Tensor | None = None, stream=None) -> None:
+    """One FP8 decode step in one launch: quantize sequence i's new bf16
+    key[i]/value[i] into slot_mapping[i] of the uint8 (E4M3) caches, then
+    pa_decode_fp8."""
+    p, (S, Hq, Hkv, d, NB, bs, MB) = _decode_common(out, query, key_cache, value_cache, block_tables,
+                                                   context_lens, lse_out, fp8=True)
+    if key.shape != (S, Hkv, d) or value.shape != (S, Hkv, d) or key.dtype != query.dtype \
+            or value.dtype != query.dtype:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_size] in the query dtype")
+    if slot_mapping.shape != (S,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.shape != (S,):
+            raise ValueError("seq_order must be [num_seqs]")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32, 1)
+    lib = load_library()
+    _invoke(lib.pa_reshape_and_decode_fp8, "pa_reshape_and_decode_fp8", p["out"], p["query"], _dev(key, "key"),
+            _dev(value, "value"), _dev(slot_mapping, "slot_mapping", torch.int64, 1), p["kc"], p["vc"], p["bt"],
+            MB, p["cl"], S, Hq, Hkv, d, NB, bs, float(scale), float(k_scale), float(v_scale), _dtype_code(query),
+            p["lse"], order_ptr, _stream(stream))
 
 
 def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

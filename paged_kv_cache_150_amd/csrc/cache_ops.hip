@@ -12,6 +12,7 @@
 
 #include "pa.h"
 #include "pa_device.h"
+#include "pa_internal.h"
 
 namespace pa {
 
@@ -35,38 +36,17 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const u32x4_t* _
 }
 
 // pa_reshape_and_cache_fp8: the quantizing scatter. A thread turns 8 values
-// of a token row (bf16 or float32) into 8 E4M3 codes: x / scale in float32
-// (IEEE division, round to nearest), magnitudes above 448 (infinities
-// included) clamped to 448, NaN written as S.1111.111 with x's sign, and the
-// rest converted by the hardware to the nearest code, ties to even. The format
-// and the scale are this library's reading: the pages name an FP8 KV cache
-// without fixing one (llm-stack-book 7.3, "The knobs that actually matter", item 5).
-__device__ __forceinline__ uint32_t quantize4_e4m3(float a, float b, float c, float d, float scale) {
-  float v[4] = {__fdiv_rn(a, scale), __fdiv_rn(b, scale), __fdiv_rn(c, scale), __fdiv_rn(d, scale)};
-  uint32_t nan_bits = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (v[i] != v[i]) {
-      nan_bits |= ((__builtin_bit_cast(uint32_t, v[i]) >> 31) << 7 | 0x7Fu) << (8 * i);
-      v[i] = 0.f;
-    } else {
-      v[i] = fminf(fmaxf(v[i], -448.f), 448.f);
-    }
-  }
-  uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
-  w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], static_cast<int>(w), true));
-  // NaN lanes were converted as zero (code 0): OR in their NaN code.
-  return w | nan_bits;
-}
-
-template <typename T>
+// of a token row (bf16 or float32) into 8 E4M3 codes with quantize4_e4m3
+// (pa_device.h), the encoding the one-launch FP8 decode step uses too.
+template <typename T, bool POW2>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(const T* __restrict__ key,
                                                                     const T* __restrict__ value,
                                                                     u32x2_t* __restrict__ key_cache,
                                                                     u32x2_t* __restrict__ value_cache,
                                                                     const int64_t* __restrict__ slot_mapping,
                                                                     int64_t num_tokens, int64_t num_slots,
-                                                                    int row_groups, float k_scale, float v_scale) {
+                                                                    int row_groups, float k_scale, float v_scale,
+                                                                    float k_inv, float v_inv) {
   // One group = 8 consecutive elements of a token row = one 8-byte piece of
   // its cache row.
   const int64_t total = num_tokens * row_groups;
@@ -100,10 +80,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(const T* __r
       }
     }
     const int64_t dst = slot * row_groups + grp;
-    key_cache[dst] = u32x2_t{quantize4_e4m3(k[0], k[1], k[2], k[3], k_scale),
-                             quantize4_e4m3(k[4], k[5], k[6], k[7], k_scale)};
-    value_cache[dst] = u32x2_t{quantize4_e4m3(v[0], v[1], v[2], v[3], v_scale),
-                               quantize4_e4m3(v[4], v[5], v[6], v[7], v_scale)};
+    key_cache[dst] = u32x2_t{quantize4_e4m3<POW2>(k[0], k[1], k[2], k[3], k_scale, k_inv),
+                             quantize4_e4m3<POW2>(k[4], k[5], k[6], k[7], k_scale, k_inv)};
+    value_cache[dst] = u32x2_t{quantize4_e4m3<POW2>(v[0], v[1], v[2], v[3], v_scale, v_inv),
+                               quantize4_e4m3<POW2>(v[4], v[5], v[6], v[7], v_scale, v_inv)};
   }
 }
 
@@ -230,17 +210,31 @@ extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, uint
   int64_t blocks = (total + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == PA_DTYPE_BF16)
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       s, static_cast<const bf16_t*>(key), static_cast<const bf16_t*>(value),
-                       reinterpret_cast<u32x2_t*>(key_cache), reinterpret_cast<u32x2_t*>(value_cache),
-                       slot_mapping, num_tokens, num_blocks * kBlockTokens, static_cast<int>(row_groups), k_scale,
-                       v_scale);
-  else
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       s, static_cast<const float*>(key), static_cast<const float*>(value),
-                       reinterpret_cast<u32x2_t*>(key_cache), reinterpret_cast<u32x2_t*>(value_cache),
-                       slot_mapping, num_tokens, num_blocks * kBlockTokens, static_cast<int>(row_groups), k_scale,
-                       v_scale);
+  float k_inv = 0.f, v_inv = 0.f;
+  const bool pow2 = exact_reciprocal(k_scale, &k_inv) && exact_reciprocal(v_scale, &v_inv);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  auto* kd = reinterpret_cast<u32x2_t*>(key_cache);
+  auto* vd = reinterpret_cast<u32x2_t*>(value_cache);
+  const int64_t ns = num_blocks * kBlockTokens;
+  const int rg = static_cast<int>(row_groups);
+  if (dtype == PA_DTYPE_BF16) {
+    const auto* k = static_cast<const bf16_t*>(key);
+    const auto* v = static_cast<const bf16_t*>(value);
+    if (pow2)
+      hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<bf16_t, true>), grid, block, 0, s, k, v, kd, vd, slot_mapping,
+                         num_tokens, ns, rg, k_scale, v_scale, k_inv, v_inv);
+    else
+      hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<bf16_t, false>), grid, block, 0, s, k, v, kd, vd, slot_mapping,
+                         num_tokens, ns, rg, k_scale, v_scale, k_inv, v_inv);
+  } else {
+    const auto* k = static_cast<const float*>(key);
+    const auto* v = static_cast<const float*>(value);
+    if (pow2)
+      hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<float, true>), grid, block, 0, s, k, v, kd, vd, slot_mapping,
+                         num_tokens, ns, rg, k_scale, v_scale, k_inv, v_inv);
+    else
+      hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<float, false>), grid, block, 0, s, k, v, kd, vd, slot_mapping,
+                         num_tokens, ns, rg, k_scale, v_scale, k_inv, v_inv);
+  }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -93,9 +93,13 @@ struct MultiArgs {
   // Decode mode with the new tokens' write folded in: sequence i's new K/V
   // (new_key/new_value row i, [num_seqs, H_kv, D]) go to slot_mapping[i]
   // first. Null: the caches already hold them.
-  const void* new_key;
+  const void* new_key;             // query dtype (bf16 for FP8 caches)
   const void* new_value;
   const int64_t* slot_mapping;
+  float k_scale;                   // FP8 caches: the write's scales (codes = value / scale)
+  float v_scale_write;
+  float k_inv, v_inv;              // their exact reciprocals when scales_pow2
+  int32_t scales_pow2;             // both scales are powers of two
   // Decode mode cut into context partitions (part_blocks > 0): slot
   // p * num_seqs + j attends the keys [p * P, min((p + 1) * P, n)) of sequence
   // i = (j - p) mod num_seqs (P = 16 * part_blocks) and writes the normalised
@@ -305,6 +309,25 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
 }
 
 
+// The new token's bf16 K and V pieces of one lane (kraw: two 16-byte loads per
+// 16-code K piece; vraw: the V piece) to E4M3 codes in the layout the FP8
+// chunk loads use (kn: 16 codes per K piece, vn: 4 codes per dword).
+template <bool POW2, int KS, int VD>
+__device__ __forceinline__ void quantize_rows(u32x4_t (&kn)[KS], uint32_t (&vn)[VD], const u32x4_t (&kraw)[2 * KS],
+                                              const uint32_t (&vraw)[2 * VD], float k_scale, float k_inv,
+                                              float v_scale, float v_inv) {
+#pragma unroll
+  for (int sg = 0; sg < KS; ++sg) {
+    const u32x4_t lo = kraw[2 * sg], hi = kraw[2 * sg + 1];
+    kn[sg] = u32x4_t{quantize_bf16x4_e4m3<POW2>(lo[0], lo[1], k_scale, k_inv),
+                     quantize_bf16x4_e4m3<POW2>(lo[2], lo[3], k_scale, k_inv),
+                     quantize_bf16x4_e4m3<POW2>(hi[0], hi[1], k_scale, k_inv),
+                     quantize_bf16x4_e4m3<POW2>(hi[2], hi[3], k_scale, k_inv)};
+  }
+#pragma unroll
+  for (int w = 0; w < VD; ++w) vn[w] = quantize_bf16x4_e4m3<POW2>(vraw[2 * w], vraw[2 * w + 1], v_scale, v_inv);
+}
+
 // Query fragments of a tile's columns: column c = 16 p + (lane % 16) is new
 // token c / g (row `row0` + c / g) and head head0 + c % g; columns past the
 // tile's `ncols` get zeros. Same d order as the K operand of qk_chunk.
@@ -466,20 +489,22 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   auto blk_of = [&](int i) { return blk_begin + (wave + i * kMqWaves) * CB; };
   auto tok_of = [&](int i) { return blk_of(i) * kBlockTokens; };
 
-  // Decode with the new token's write folded in. Every lane loads its pieces
-  // of the new K/V row up front (no dependence on anything else). When the
-  // slot is the one the block table gives position n - 1 (the decode step's
-  // own token), the wave whose last chunk holds that position swaps the new
-  // rows into that chunk's registers before using it, and stores them to the
-  // slot once its chunks are done; nothing in this launch reads the slot from
-  // memory after the store, so no ordering is needed. Any other slot (an
-  // empty context included) is only written, by wave 0: attention then uses
-  // what the cache holds at position n - 1.
-  // (Decode mode always runs 16-column tiles; the 32-column instantiations
-  // leave this out.)
-  constexpr bool kFusedWrite = !F8 && NT == 1;
+  // Decode with the new token's write folded in. When the slot is the one the
+  // block table gives position n - 1 (the decode step's own token), the wave
+  // whose last chunk holds that position loads the new rows, swaps them into
+  // that chunk's registers before using it, and stores them to the slot once
+  // its chunks are done; nothing in this launch reads the slot from memory
+  // after the store, so no ordering is needed. Any other slot (an empty
+  // context included) is only written, by wave 0: attention then uses what
+  // the cache holds at position n - 1. FP8 caches get the new rows quantized
+  // (quantize4_e4m3, the encoding of pa_reshape_and_cache_fp8) in the same
+  // register layout as the codes the chunks load. (Decode mode always runs
+  // 16-column tiles; the 32-column instantiations leave this out.)
+  constexpr bool kFusedWrite = NT == 1;
   u32x4_t kn[S::kKSeg];
   uint32_t vn[S::kVDw];
+  u32x4_t kraw[2 * S::kKSeg];  // FP8 caches: the new bf16 rows before quantizing
+  uint32_t vraw[2 * S::kVDw];
   bool own_new = false;    // this wave stores the new rows
   bool patch_own = false;  // ... and uses them in place of position n - 1
   int new_ib = 0, new_r0 = 0;
@@ -488,12 +513,6 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     if (a.slot_mapping != nullptr) {
       new_slot = a.slot_mapping[seq];
       if (new_slot >= 0 && new_slot < a.num_blocks * kBlockTokens) {
-        const int64_t src_off = (static_cast<int64_t>(seq) * a.num_kv_heads + kvh) * D * S::kElemBytes;
-        const gchar_t* ksrc = uniform_ptr(static_cast<const char*>(a.new_key) + src_off);
-        const gchar_t* vsrc = uniform_ptr(static_cast<const char*>(a.new_value) + src_off);
-#pragma unroll
-        for (int sg = 0; sg < S::kKSeg; ++sg) kn[sg] = gload16(ksrc + sg * 64 + (lane >> 4) * 16);
-        load_dwords<S::kVDw>(vn, vsrc + (lane & 15) * (S::kVDw * 4));
         const int pos = key_end - 1;
         const bool on_pos = pos >= 0 && static_cast<int64_t>(bt_row[pos / kBlockTokens]) * kBlockTokens +
                                             pos % kBlockTokens == new_slot;
@@ -508,7 +527,41 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
         }
       }
     }
+    if (own_new) {
+      // Only the storing wave reads the new rows (query dtype).
+      const int64_t src_off = (static_cast<int64_t>(seq) * a.num_kv_heads + kvh) * D * sizeof(T);
+      const gchar_t* ksrc = uniform_ptr(static_cast<const char*>(a.new_key) + src_off);
+      const gchar_t* vsrc = uniform_ptr(static_cast<const char*>(a.new_value) + src_off);
+      if constexpr (F8) {
+        // Elements 64 sg + 16 (lane / 16) .. +15 (K) and (lane % 16) * D/16
+        // .. +D/16 - 1 (V): the elements of the codes this lane holds.
+#pragma unroll
+        for (int sg = 0; sg < S::kKSeg; ++sg) {
+          const gchar_t* kp = ksrc + 2 * (sg * 64 + (lane >> 4) * 16);
+          kraw[2 * sg] = gload16(kp);
+          kraw[2 * sg + 1] = gload16(kp + 16);
+        }
+        load_dwords<2 * S::kVDw>(vraw, vsrc + 2 * (lane & 15) * S::kVec);
+      } else {
+#pragma unroll
+        for (int sg = 0; sg < S::kKSeg; ++sg) kn[sg] = gload16(ksrc + sg * 64 + (lane >> 4) * 16);
+        load_dwords<S::kVDw>(vn, vsrc + (lane & 15) * (S::kVDw * 4));
+      }
+    }
   }
+  // FP8 caches: the storing wave turns the new rows into codes (the encoding
+  // of pa_reshape_and_cache_fp8). Called once the wave's first chunk loads are
+  // in flight, so the IEEE divisions overlap their latency.
+  auto quantize_new = [&]() __attribute__((always_inline)) {
+    if constexpr (kFusedWrite && F8) {
+      if (own_new) {
+        if (a.scales_pow2)
+          quantize_rows<true>(kn, vn, kraw, vraw, a.k_scale, a.k_inv, a.v_scale_write, a.v_inv);
+        else
+          quantize_rows<false>(kn, vn, kraw, vraw, a.k_scale, a.k_inv, a.v_scale_write, a.v_inv);
+      }
+    }
+  };
   // K row new_r0 of block new_ib lives in lanes with lane % 16 == new_r0; V row
   // new_r0 in lanes with lane / 16 == new_r0 / 4, register row new_r0 % 4.
   auto patch_new = [&](Chunk<T, D, 16, CB, F8>& f) {
@@ -570,8 +623,11 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
       mq_chunk<T, D, CB, NT, F8, decltype(mask_tag)::value || kAllMasked>(st, f, q, a.scale_log2, tok_of(i), lim,
                                                                           key_end, lane);
     };
+    if (mine > 0) load(fa, 0);
+    // The write is folded only into decode launches, and those always stream
+    // (stream_keys), so only the streaming loop quantizes.
+    if constexpr (kStream) quantize_new();
     if (mine <= 0) return;
-    load(fa, 0);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
       load(fb, i + 1);
@@ -806,7 +862,8 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
                  int32_t dtype, bool fp8_cache, float* lse_out, const int32_t* seq_order, hipStream_t stream,
                  int32_t skip_blocks = 0, const float* prefix_o = nullptr, const float* prefix_lse = nullptr,
                  const void* new_key = nullptr, const void* new_value = nullptr,
-                 const int64_t* slot_mapping = nullptr) {
+                 const int64_t* slot_mapping = nullptr, float write_k_scale = 1.0f,
+                 float write_v_scale = 1.0f) {
   const int g = num_heads / num_kv_heads;
   int NT = query_start_loc == nullptr ? 1 : pick_tiles(num_tokens, num_seqs, g);
   NT = NT < max_tiles(dtype, head_size) ? NT : max_tiles(dtype, head_size);
@@ -848,6 +905,9 @@ int launch_multi(void* out, const void* query, const void* key_cache, const void
   a.new_key = new_key;
   a.new_value = new_value;
   a.slot_mapping = slot_mapping;
+  a.k_scale = write_k_scale;
+  a.v_scale_write = write_v_scale;
+  a.scales_pow2 = exact_reciprocal(write_k_scale, &a.k_inv) && exact_reciprocal(write_v_scale, &a.v_inv);
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(W * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -1131,4 +1191,25 @@ extern "C" int pa_reshape_and_decode(void* out, const void* query, const void* k
                       num_seqs, num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * kLog2e, 1.0f,
                       dtype, false, lse_out, seq_order, static_cast<hipStream_t>(stream), 0, nullptr, nullptr, key,
                       value, slot_mapping);
+}
+
+extern "C" int pa_reshape_and_decode_fp8(void* out, const void* query, const void* key, const void* value,
+                                         const int64_t* slot_mapping, uint8_t* key_cache, uint8_t* value_cache,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_size, int64_t num_blocks,
+                                         int32_t block_size, float scale, float k_scale, float v_scale, int32_t dtype,
+                                         float* lse_out, const int32_t* seq_order, void* stream) {
+  int st = check_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_seqs, num_heads, num_kv_heads, head_size, num_blocks, block_size, scale, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == __builtin_inff() || v_scale == __builtin_inff())
+    return PA_ERR_INVALID_ARG;
+  if (!key || !value || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned16_mq(key) || !aligned16_mq(value)) return PA_ERR_INVALID_ARG;
+  return launch_multi(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, nullptr,
+                      num_seqs, num_seqs, num_heads, num_kv_heads, head_size, num_blocks, scale * k_scale * kLog2e,
+                      v_scale, dtype, true, lse_out, seq_order, static_cast<hipStream_t>(stream), 0, nullptr, nullptr,
+                      key, value, slot_mapping, k_scale, v_scale);
 }

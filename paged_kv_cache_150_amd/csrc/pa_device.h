@@ -126,6 +126,53 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
+// Four values to four FP8 E4M3 codes (byte i = value i): x / scale in float32
+// (IEEE division, round to nearest), magnitudes above 448 (infinities
+// included) clamped to 448, NaN written as S.1111.111 with x's sign, and the
+// rest converted by the hardware to the nearest code, ties to even. The format
+// and the scale are this library's reading: the pages name an FP8 KV cache
+// without fixing one (llm-stack-book 7.3, "The knobs that actually matter",
+// item 5). POW2: scale is a power of two and inv its exact reciprocal, so
+// x * inv is the correctly rounded quotient x / scale (both round the same
+// exact value once) at the cost of one multiplication instead of a division.
+template <bool POW2>
+__device__ __forceinline__ uint32_t quantize4_e4m3(float a, float b, float c, float d, float scale, float inv) {
+  float v[4];
+  if constexpr (POW2) {
+    v[0] = a * inv;
+    v[1] = b * inv;
+    v[2] = c * inv;
+    v[3] = d * inv;
+  } else {
+    v[0] = __fdiv_rn(a, scale);
+    v[1] = __fdiv_rn(b, scale);
+    v[2] = __fdiv_rn(c, scale);
+    v[3] = __fdiv_rn(d, scale);
+  }
+  uint32_t nan_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] != v[i]) {
+      nan_bits |= ((__builtin_bit_cast(uint32_t, v[i]) >> 31) << 7 | 0x7Fu) << (8 * i);
+      v[i] = 0.f;
+    } else {
+      v[i] = fminf(fmaxf(v[i], -448.f), 448.f);
+    }
+  }
+  uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false));
+  w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], static_cast<int>(w), true));
+  // NaN lanes were converted as zero (code 0): OR in their NaN code.
+  return w | nan_bits;
+}
+
+// Two dwords of bf16 (four values, low halves first) to four E4M3 codes.
+template <bool POW2>
+__device__ __forceinline__ uint32_t quantize_bf16x4_e4m3(uint32_t w0, uint32_t w1, float scale, float inv) {
+  return quantize4_e4m3<POW2>(__builtin_bit_cast(float, w0 << 16), __builtin_bit_cast(float, w0 & 0xFFFF0000u),
+                              __builtin_bit_cast(float, w1 << 16), __builtin_bit_cast(float, w1 & 0xFFFF0000u),
+                              scale, inv);
+}
+
 // float32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);

@@ -58,6 +58,16 @@ int launch_merge_mq_parts(void* out, float* lse_out, const float* o_parts, const
 // Compute units of the current device (256 when it cannot be queried).
 int device_cus();
 
+// True when scale is a power of two in [2^-120, 2^120]; then *inv is its
+// exact reciprocal and x * inv equals the correctly rounded x / scale.
+inline bool exact_reciprocal(float scale, float* inv) {
+  int e = 0;
+  const float m = __builtin_frexpf(scale, &e);
+  if (m != 0.5f || e < -119 || e > 121) return false;
+  *inv = __builtin_ldexpf(1.0f, 1 - e);
+  return true;
+}
+
 // Current value of a kernel-choice option (pa_option in pa.h); 0 = the
 // default choice.
 int option_value(int option);

@@ -32,7 +32,7 @@ def test_headers_declare_the_boundary():
     inc = os.path.join(ROOT, "include")
     assert declared_functions(os.path.join(inc, "pa.h")) == sorted([
         "pa_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_copy_blocks", "pa_decode", "pa_decode_fp8",
-        "pa_reshape_and_decode", "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes",
+        "pa_reshape_and_decode", "pa_reshape_and_decode_fp8", "pa_multi_query", "pa_multi_query_fp8", "pa_multi_query_split_workspace_bytes",
         "pa_multi_query_split", "pa_multi_query_split_partition_size", "pa_decode_prefix_workspace_bytes",
         "pa_decode_prefix",
         "pa_decode_split_workspace_bytes", "pa_decode_split", "pa_merge_partitions", "pa_status_string",

@@ -45,7 +45,7 @@ def _specials(dtype, shape, rng):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Hkv,d", [(8, 128), (2, 64)])
-@pytest.mark.parametrize("scales", [(1.0, 1.0), (1 / 64, 1 / 8), (0.3, 3.0)])
+@pytest.mark.parametrize("scales", [(1.0, 1.0), (1 / 64, 1 / 8), (0.3, 3.0), (2.0 ** 20, 2.0 ** -20)])
 def test_reshape_fp8_bit_exact(pa, dtype, Hkv, d, scales):
     rng = np.random.default_rng(21)
     nb, T = 40, 37
@@ -115,5 +115,92 @@ def test_fp8_step_full_size(pa):
     kc_after, vc_after = gk.cpu().numpy(), gv.cpu().numpy()
     ref, ref_lse = oracle.paged_decode_fp8(inp.query, kc_after, vc_after, inp.block_tables, inp.context_lens,
                                            cfg.scale, cfg.k_scale, cfg.v_scale)
+    assert max_err(out, ref) <= TOL["bf16"]
+    assert max_err(lse, ref_lse) <= LSE_TOL["bf16"]
+
+
+def _fp8_fused(pa, q, new_k, new_v, slots, gk, gv, bt, cl, cfg):
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    pa.pa_reshape_and_decode_fp8(out, q, to_dev(new_k), to_dev(new_v), to_dev(slots), gk, gv, bt, cl, cfg.scale,
+                                 cfg.k_scale, cfg.v_scale, lse_out=lse)
+    return out, lse
+
+
+@pytest.mark.parametrize("scales", [(1 / 64, 1 / 32), (0.3 / 64, 1 / 48)], ids=["pow2", "other"])
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 32, 8), (64, 8, 2), (128, 16, 1)])
+def test_fp8_one_launch_step_slots_and_shapes(pa, d, Hq, Hkv, scales):
+    """pa_reshape_and_decode_fp8 on ragged contexts (empty, one token, block
+    boundaries) with every slot case: position n-1's own slot, padding, a free
+    block (the row is written, attention keeps the cached codes), past the
+    pool. Rows written to free blocks carry NaN, infinities, overflow and
+    subnormal values. Power-of-two scales take the reciprocal path of the
+    write, others the division. Caches bit-exact against the oracle's quantizing write,
+    outputs bit-identical to the two-launch step and within tolerance of the
+    oracle."""
+    lens = np.array([1, 15, 16, 17, 33, 100, 257, 31, 0, 48, 129, 64], np.int32)
+    cfg = W.small_case("fp8fused", len(lens), Hq, Hkv, d, "bf16", ("uniform", 1, 2), seed=53, num_blocks=240,
+                       kv_dtype="fp8", k_scale=scales[0], v_scale=scales[1])
+    inp = W.make_inputs(cfg, context_lens=np.maximum(lens, 1))
+    inp.context_lens = lens
+    rows = cfg.num_blocks * 16
+    free = np.setdiff1d(np.arange(cfg.num_blocks), inp.referenced_blocks)
+    rng = np.random.default_rng(8)
+    new_k, new_v = inp.new_key.copy(), inp.new_value.copy()
+    slots = inp.slot_mapping.copy()
+    kb, vb = W.caches_before_write(inp)
+    keep = {1: -1, 3: int(free[0]) * 16 + 9, 8: int(free[1]) * 16 + 2, 10: rows, 11: 2 ** 40}
+    for i, s in keep.items():
+        if lens[i] > 0:
+            # Position n-1 keeps the codes of its token already in the cache.
+            kb.reshape(rows, Hkv, d)[inp.slot_mapping[i]] = oracle.quantize(inp.new_key[i], cfg.k_scale)
+            vb.reshape(rows, Hkv, d)[inp.slot_mapping[i]] = oracle.quantize(inp.new_value[i], cfg.v_scale)
+        new_k[i] = _specials("bf16", (Hkv, d), rng)
+        new_v[i] = _specials("bf16", (Hkv, d), rng)
+        slots[i] = s
+    gk, gv = _dev_u8(kb), _dev_u8(vb)
+    q, bt, cl = to_dev(inp.query), to_dev(inp.block_tables), to_dev(lens)
+    out, lse = _fp8_fused(pa, q, new_k, new_v, slots, gk, gv, bt, cl, cfg)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.reshape_and_cache_fp8(new_k, new_v, kb, vb, slots, cfg.k_scale, cfg.v_scale)
+    np.testing.assert_array_equal(gk.cpu().numpy(), ref_k)
+    np.testing.assert_array_equal(gv.cpu().numpy(), ref_v)
+    # Two launches on the same inputs: identical bits.
+    gk2, gv2 = _dev_u8(kb), _dev_u8(vb)
+    pa.pa_reshape_and_cache_fp8(to_dev(new_k), to_dev(new_v), gk2, gv2, to_dev(slots), cfg.k_scale, cfg.v_scale)
+    out2 = torch.empty_like(q)
+    lse2 = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    pa.pa_decode_fp8(out2, q, gk2, gv2, bt, cl, cfg.scale, cfg.k_scale, cfg.v_scale, lse_out=lse2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), bits(out2))
+    np.testing.assert_array_equal(bits(lse), bits(lse2))
+    ref, ref_lse = oracle.paged_decode_fp8(inp.query, ref_k, ref_v, inp.block_tables, lens, cfg.scale, cfg.k_scale,
+                                           cfg.v_scale)
+    z = lens == 0
+    o, l = f64(out), f64(lse)
+    assert (o[z] == 0).all() and np.isneginf(l[z]).all()
+    assert np.abs(o[~z] - ref[~z]).max() <= TOL["bf16"]
+    assert np.abs(l[~z] - ref_lse[~z]).max() <= LSE_TOL["bf16"]
+
+
+def test_fp8_one_launch_step_full_size(pa):
+    """The FP8 batch-256 workload as one launch: the written codes bit-exact,
+    every output row and log-sum-exp against the oracle."""
+    cfg = W.CONFIG_BY_NAME["llama3_8b_b256_fp8"]
+    inp = W.make_inputs(cfg, mode="perf")
+    kc_h, vc_h = W.caches_before_write(inp)
+    gk, gv = _dev_u8(kc_h), _dev_u8(vc_h)
+    q = to_dev(inp.query)
+    out, lse = _fp8_fused(pa, q, inp.new_key, inp.new_value, inp.slot_mapping, gk, gv, to_dev(inp.block_tables),
+                          to_dev(inp.context_lens), cfg)
+    torch.cuda.synchronize()
+    rows = cfg.num_blocks * 16
+    sl = torch.from_numpy(inp.slot_mapping).cuda()
+    np.testing.assert_array_equal(gk.view(rows, cfg.num_kv_heads, cfg.head_size)[sl].cpu().numpy(),
+                                  oracle.quantize(inp.new_key, cfg.k_scale))
+    np.testing.assert_array_equal(gv.view(rows, cfg.num_kv_heads, cfg.head_size)[sl].cpu().numpy(),
+                                  oracle.quantize(inp.new_value, cfg.v_scale))
+    ref, ref_lse = oracle.paged_decode_fp8(inp.query, gk.cpu().numpy(), gv.cpu().numpy(), inp.block_tables,
+                                           inp.context_lens, cfg.scale, cfg.k_scale, cfg.v_scale)
     assert max_err(out, ref) <= TOL["bf16"]
     assert max_err(lse, ref_lse) <= LSE_TOL["bf16"]
