@@ -570,7 +570,9 @@ def main():
     if one_launch:
         one += " with the new-token write"
     split_label = "paged_decode_split_kernel + merge_pieces_kernel"
-    if args.decode == "split" and pa.pa_decode_split_part_tokens(S, Hq, cfg.num_kv_heads, inp.max_context_len, P):
+    if args.decode == "split" and pa.pa_decode_split_part_tokens(
+            S, Hq, cfg.num_kv_heads, inp.max_context_len, P,
+            pa.PA_DTYPE_BF16 if cfg.dtype == "bf16" else pa.PA_DTYPE_F32):
         split_label = "paged_multi_query_kernel (context partitions) + merge_parts_kernel"
     kernel_label = {"fused": one, "split": split_label,
                     "prefix": "paged_multi_query_kernel (shared prefix) + " + one}[args.decode]

@@ -425,9 +425,9 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * on the same stream merges the slots of every (sequence, head) that hold a
  * partition into out. The header is not written.
  *
- * Pieces (groups above 16; groups of at most 4 when num_seqs * H_kv is below
- * the number of resident tile workgroups, i.e. a few long contexts; or
- * PA_OPT_SPLIT_CUT = 2): the kv heads are taken
+ * Pieces (groups above 16; with float32 caches, groups of at most 4 when
+ * num_seqs * H_kv is below the number of resident tile workgroups, i.e. a few
+ * long contexts; or PA_OPT_SPLIT_CUT = 2): the kv heads are taken
  * in groups of up to 8 (one persistent workgroup has one wave per kv head of
  * its group, all walking the same blocks). Per head group, the blocks of all
  * sequences are laid end to end (sequence i has nb_i = ceil(n_i / block_size)
@@ -500,10 +500,11 @@ int pa_decode_split_noalloc(void* out, const void* query, const void* key_cache,
  * arguments on the current device: the partition length P' (a multiple of
  * partition_size) of the partition cut, 0 for the pieces cut, -1 for invalid
  * arguments, with the options PA_OPT_SPLIT_CUT and PA_OPT_SPLIT_PART_FACTOR
- * as they stand. Queries the device's CU count, launches nothing.
+ * as they stand. dtype: the caches' element type. Queries the device's CU
+ * count, launches nothing.
  */
 int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                    int32_t max_context_len, int32_t partition_size);
+                                    int32_t max_context_len, int32_t partition_size, int32_t dtype);
 
 /*
  * pa_merge_partitions - exact log-sum-exp merge of partial attention results.

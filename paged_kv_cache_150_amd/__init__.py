@@ -95,7 +95,7 @@ def load_library() -> ctypes.CDLL:
     lib.pa_set_option.restype = c_int
     lib.pa_get_option.argtypes = [c_int]
     lib.pa_get_option.restype = c_int
-    lib.pa_decode_split_part_tokens.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
+    lib.pa_decode_split_part_tokens.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]
     lib.pa_decode_split_part_tokens.restype = c_i32
     lib.pa_multi_query_fp8.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                        c_i64, c_i32, c_f, c_f, c_f, c_i32, c_p, c_p]
@@ -410,10 +410,10 @@ def pa_multi_query_split(out: torch.Tensor, query: torch.Tensor, key_cache: torc
 
 
 def pa_decode_split_part_tokens(num_seqs: int, num_heads: int, num_kv_heads: int, max_context_len: int,
-                                partition_size: int) -> int:
+                                partition_size: int, dtype: int = PA_DTYPE_BF16) -> int:
     """Partition length of pa_decode_split's partition cut for these arguments, or 0 for its pieces cut."""
     r = load_library().pa_decode_split_part_tokens(num_seqs, num_heads, num_kv_heads, max_context_len,
-                                                   partition_size)
+                                                   partition_size, dtype)
     if r < 0:
         raise ValueError("invalid split arguments")
     return int(r)

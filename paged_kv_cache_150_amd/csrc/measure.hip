@@ -73,7 +73,7 @@ __device__ __forceinline__ uint32_t fold_chunk(const Chunk<T, D, 16, CB, F8>& f)
 // per sequence) with the arithmetic taken out: the same workgroup per
 // (sequence, kv head) in the same dispatch order, chunk c of CB blocks to wave
 // c % W, one chunk of look-ahead in registers, the same non-temporal loads
-// (load_chunk).
+// (load_chunk, K row by row through LDS for 16-bit caches).
 template <typename T, int D, int CB, bool F8, int W>
 __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void stream_kv_kernel(StreamKvArgs a) {
   using S = DecodeShape<T, D, 16, CB, F8>;
@@ -102,32 +102,39 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void stream_kv_kernel(St
   const int last_rows = n - blk_last * kBlockTokens;
   const int mine = wave < nchunk ? (nchunk - wave + W - 1) / W : 0;
   auto blk_of = [&](int i) { return (wave + i * W) * CB; };
+  // 16-bit caches: row-wise K through each wave's LDS area, as the decode does.
+  constexpr bool kRowK = S::kRowKCapable;
+  __shared__ u32x4_t s_stage[W][kRowK ? CB * kBlockTokens * S::kRowPieces : 1];
   uint32_t acc = 0;
   Chunk<T, D, 16, CB, F8> fa, fb;
+  auto fold = [&](Chunk<T, D, 16, CB, F8>& f) {
+    if constexpr (kRowK) k_rows_to_mfma<T, D, 16, CB, F8>(f, s_stage[wave], lane);
+    return fold_chunk<T, D, CB, F8>(f);
+  };
   if (mine > 0) {
-    load_chunk<T, D, 16, CB, F8, true>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
+    load_chunk<T, D, 16, CB, F8, true, kRowK>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
                                  head_off, lane, last_rows);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
-      load_chunk<T, D, 16, CB, F8, true>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, 16, CB, F8, true, kRowK>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
                                    blk_stride, head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
-      acc ^= fold_chunk<T, D, CB, F8>(fa);
+      acc ^= fold(fa);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk<T, D, 16, CB, F8, true>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, 16, CB, F8, true, kRowK>(fa, kc, vc, bt_row, blk_of(i + 2), blk_last, a.num_blocks, tok_stride,
                                    blk_stride, head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
-      acc ^= fold_chunk<T, D, CB, F8>(fb);
+      acc ^= fold(fb);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < mine) {
-      load_chunk<T, D, 16, CB, F8, true>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
+      load_chunk<T, D, 16, CB, F8, true, kRowK>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,
                                    blk_stride, head_off, lane, last_rows);
       __builtin_amdgcn_sched_barrier(0);
-      acc ^= fold_chunk<T, D, CB, F8>(fa);
-      acc ^= fold_chunk<T, D, CB, F8>(fb);
+      acc ^= fold(fa);
+      acc ^= fold(fb);
     } else {
-      acc ^= fold_chunk<T, D, CB, F8>(fa);
+      acc ^= fold(fa);
     }
   }
   if (acc == kSinkMagic) a.sink[0] = acc;

@@ -312,12 +312,13 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
 // The new token's bf16 K and V pieces of one lane (kraw: two 16-byte loads per
 // 16-code K piece; vraw: the V piece) to E4M3 codes in the layout the FP8
 // chunk loads use (kn: 16 codes per K piece, vn: 4 codes per dword).
-template <bool POW2, int KS, int VD>
+// KQ: the K pieces to quantize (all KS, or just the first with row-wise K).
+template <bool POW2, int KQ, int KS, int VD>
 __device__ __forceinline__ void quantize_rows(u32x4_t (&kn)[KS], uint32_t (&vn)[VD], const u32x4_t (&kraw)[2 * KS],
                                               const uint32_t (&vraw)[2 * VD], float k_scale, float k_inv,
                                               float v_scale, float v_inv) {
 #pragma unroll
-  for (int sg = 0; sg < KS; ++sg) {
+  for (int sg = 0; sg < KQ; ++sg) {
     const u32x4_t lo = kraw[2 * sg], hi = kraw[2 * sg + 1];
     kn[sg] = u32x4_t{quantize_bf16x4_e4m3<POW2>(lo[0], lo[1], k_scale, k_inv),
                      quantize_bf16x4_e4m3<POW2>(lo[2], lo[3], k_scale, k_inv),
@@ -365,6 +366,8 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   using S = DecodeShape<T, D, 16, CB, F8>;
   constexpr int kCols = 16 * NT;
   constexpr int kRow = D + 4;  // LDS row stride in floats: 16-byte rows, the 16 columns on distinct banks
+  // s_acc also holds each wave's K staging area (k_rows_to_mfma) during the
+  // chunk loop; a barrier separates the two uses.
   __shared__ __attribute__((aligned(16))) float s_acc[kMqWaves][kCols][kRow];
   __shared__ float s_m[kMqWaves][kCols];
   __shared__ float s_l[kMqWaves][kCols];
@@ -375,6 +378,13 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = a.group;
+  // 16-column tiles of 16-bit caches load K row by row (k_rows_to_mfma); the
+  // 32-column ones keep the direct operand loads (the staging pushes them
+  // past the register budget).
+  constexpr bool kRowK = S::kRowKCapable && NT == 1;
+  constexpr int kStagePieces = CB * kBlockTokens * S::kRowPieces;  // 16-byte pieces per wave
+  static_assert(!kRowK || sizeof(s_acc) >= sizeof(u32x4_t) * kStagePieces * kMqWaves, "K staging fits s_acc");
+  u32x4_t* k_stage = reinterpret_cast<u32x4_t*>(&s_acc[0][0][0]) + wave * kStagePieces;
 
   int slot, kvh;
   if (a.query_start_loc != nullptr && a.part_blocks == 0 && a.prefix_keys == 0)
@@ -535,6 +545,7 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
       if constexpr (F8) {
         // Elements 64 sg + 16 (lane / 16) .. +15 (K) and (lane % 16) * D/16
         // .. +D/16 - 1 (V): the elements of the codes this lane holds.
+        static_assert(!kRowK, "FP8 tiles load K in the operand layout");
 #pragma unroll
         for (int sg = 0; sg < S::kKSeg; ++sg) {
           const gchar_t* kp = ksrc + 2 * (sg * 64 + (lane >> 4) * 16);
@@ -542,6 +553,10 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
           kraw[2 * sg + 1] = gload16(kp + 16);
         }
         load_dwords<2 * S::kVDw>(vraw, vsrc + 2 * (lane & 15) * S::kVec);
+      } else if constexpr (kRowK) {
+        // The piece of row new_r0 this lane holds in the row-wise K layout.
+        kn[0] = gload16(ksrc + ((lane - new_r0) & (S::kRowPieces - 1)) * 16);
+        load_dwords<S::kVDw>(vn, vsrc + (lane & 15) * (S::kVDw * 4));
       } else {
 #pragma unroll
         for (int sg = 0; sg < S::kKSeg; ++sg) kn[sg] = gload16(ksrc + sg * 64 + (lane >> 4) * 16);
@@ -555,23 +570,32 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   auto quantize_new = [&]() __attribute__((always_inline)) {
     if constexpr (kFusedWrite && F8) {
       if (own_new) {
+        constexpr int kKQ = kRowK ? 1 : S::kKSeg;
         if (a.scales_pow2)
-          quantize_rows<true>(kn, vn, kraw, vraw, a.k_scale, a.k_inv, a.v_scale_write, a.v_inv);
+          quantize_rows<true, kKQ>(kn, vn, kraw, vraw, a.k_scale, a.k_inv, a.v_scale_write, a.v_inv);
         else
-          quantize_rows<false>(kn, vn, kraw, vraw, a.k_scale, a.k_inv, a.v_scale_write, a.v_inv);
+          quantize_rows<false, kKQ>(kn, vn, kraw, vraw, a.k_scale, a.k_inv, a.v_scale_write, a.v_inv);
       }
     }
   };
   // K row new_r0 of block new_ib lives in lanes with lane % 16 == new_r0; V row
   // new_r0 in lanes with lane / 16 == new_r0 / 4, register row new_r0 % 4.
+  // With row-wise K (16-bit caches) row new_r0 sits in load new_r0 /
+  // kRowsPerLoad, lanes with lane / kRowPieces == new_r0 % kRowsPerLoad.
   auto patch_new = [&](Chunk<T, D, 16, CB, F8>& f) {
-    const bool krow = (lane & 15) == new_r0;
+    const bool krow = kRowK ? lane / S::kRowPieces == new_r0 % S::kRowsPerLoad : (lane & 15) == new_r0;
     const bool vrow = (lane >> 4) == new_r0 / 4;
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       if (i != new_ib) continue;
 #pragma unroll
-      for (int sg = 0; sg < S::kKSeg; ++sg) f.k[i][sg] = krow ? kn[sg] : f.k[i][sg];
+      for (int sg = 0; sg < S::kKSeg; ++sg) {
+        if constexpr (kRowK) {
+          if (sg == new_r0 / S::kRowsPerLoad) f.k[i][sg] = krow ? kn[0] : f.k[i][sg];
+        } else {
+          f.k[i][sg] = krow ? kn[sg] : f.k[i][sg];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (r != new_r0 % 4) continue;
@@ -616,10 +640,11 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     constexpr bool kAllMasked = decltype(all_masked_tag)::value;
     Chunk<T, D, 16, CB, F8> fa, fb;
     auto load = [&](Chunk<T, D, 16, CB, F8>& f, int i) {
-      load_chunk<T, D, 16, CB, F8, kStream>(f, kc, vc, bt_row, blk_of(i), blk_last, a.num_blocks, tok_stride,
-                                            blk_stride, head_off, lane, last_rows);
+      load_chunk<T, D, 16, CB, F8, kStream, kRowK>(f, kc, vc, bt_row, blk_of(i), blk_last, a.num_blocks,
+                                                   tok_stride, blk_stride, head_off, lane, last_rows);
     };
-    auto compute = [&](const Chunk<T, D, 16, CB, F8>& f, int i, auto mask_tag) {
+    auto compute = [&](Chunk<T, D, 16, CB, F8>& f, int i, auto mask_tag) {
+      if constexpr (kRowK) k_rows_to_mfma<T, D, 16, CB, F8>(f, k_stage, lane);
       mq_chunk<T, D, CB, NT, F8, decltype(mask_tag)::value || kAllMasked>(st, f, q, a.scale_log2, tok_of(i), lim,
                                                                           key_end, lane);
     };
@@ -666,7 +691,11 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     const int64_t dst_off = (new_slot / kBlockTokens) * blk_stride + (new_slot % kBlockTokens) * tok_stride + head_off;
     gwchar_t* kdst = reinterpret_cast<gwchar_t*>(reinterpret_cast<uintptr_t>(kc + dst_off));
     gwchar_t* vdst = reinterpret_cast<gwchar_t*>(reinterpret_cast<uintptr_t>(vc + dst_off));
-    if ((lane & 15) == 0) {
+    if constexpr (kRowK) {
+      if (lane < S::kRowPieces)
+        *reinterpret_cast<__attribute__((address_space(1))) u32x4_t*>(
+            kdst + ((lane - new_r0) & (S::kRowPieces - 1)) * 16) = kn[0];
+    } else if ((lane & 15) == 0) {
 #pragma unroll
       for (int sg = 0; sg < S::kKSeg; ++sg)
         *reinterpret_cast<__attribute__((address_space(1))) u32x4_t*>(kdst + sg * 64 + (lane >> 4) * 16) = kn[sg];
@@ -678,6 +707,8 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     }
   }
 
+  // Every wave is done with its K staging area before s_acc takes the partials.
+  if constexpr (kRowK) __syncthreads();
   // Wave partials to LDS: per column the running max and normaliser, and the
   // lane's D/4 output elements.
   const int j = lane >> 4;

@@ -1,8 +1,10 @@
 // K/V tile loads and the MFMA score tile shared by the paged-attention
 // kernels (gfx950 only). Layout of one tile (16 tokens of one block, one kv
 // head): for the score MFMA, lane l holds K row (l % 16), 16-byte pieces at
-// byte offset s*64 + (l/16)*16; for the value side, lane l holds rows
-// 4*(l/16) .. 4*(l/16)+3, elements (l%16)*D/16 .. (l%16+1)*D/16 - 1 of each.
+// byte offset s*64 + (l/16)*16 (16-bit caches load K row by row and reach
+// this layout through LDS: k_rows_to_mfma); for the value side, lane l holds
+// rows 4*(l/16) .. 4*(l/16)+3, elements (l%16)*D/16 .. (l%16+1)*D/16 - 1 of
+// each.
 #pragma once
 
 #include "pa_device.h"
@@ -18,6 +20,13 @@ struct DecodeShape {
   static constexpr int kQSeg = F8 ? 2 * kKSeg : kKSeg;  // 16-byte query pieces per lane (MFMA k-steps)
   static constexpr int kVec = D / 16;                // V elements per lane per token
   static constexpr int kVDw = kVec * kElemBytes / 4; // ... as dwords
+  // 16-bit caches can load K row by row (each load instruction covers whole
+  // token rows) and pass it through LDS into the MFMA operand layout; see
+  // load_chunk (ROWK) and k_rows_to_mfma. (FP8 caches measured slower that
+  // way: 100.2 vs 94.0 us for the batch-256 step.)
+  static constexpr bool kRowKCapable = !F8 && sizeof(T) == 2;
+  static constexpr int kRowPieces = D * kElemBytes / 16;  // 16-byte pieces per K row
+  static constexpr int kRowsPerLoad = kWave / kRowPieces;  // K rows per load instruction
   static_assert(kKSeg >= 1 && kVDw >= 1, "shape");
   static_assert(G >= 1 && G <= 16, "group");
   static_assert(!F8 || sizeof(T) == 2, "FP8 caches take bf16 queries");
@@ -36,7 +45,8 @@ struct Chunk {
 // lanes for later rows read the last valid row again (same lines, no extra
 // memory traffic); those rows are masked out by the caller (16-bit and FP8
 // caches). STREAM: non-temporal loads (data no other workgroup reads again).
-template <typename T, int D, int G, int CB, bool F8 = false, bool STREAM = false>
+// ROWK (16-bit caches): K loaded row by row, for k_rows_to_mfma.
+template <typename T, int D, int G, int CB, bool F8 = false, bool STREAM = false, bool ROWK = false>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
                                            const int32_t* bt_row, int blk0, int blk_last,
                                            int64_t num_blocks, uint32_t tok_stride_bytes,
@@ -61,7 +71,26 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
     const int64_t base = static_cast<int64_t>(phys) * blk_stride_bytes + head_off_bytes;
     const gchar_t* kb = uniform_ptr(kc + base);
     const gchar_t* vb = uniform_ptr(vc + base);
-    if constexpr (S::kElemBytes <= 2) {
+    static_assert(!ROWK || S::kRowKCapable, "row-wise K needs 16-bit caches");
+    if constexpr (ROWK) {
+      // K: load s covers rows kRowsPerLoad * s + lane / kRowPieces; lane l
+      // takes piece (l - row) mod kRowPieces of its row, so that the pieces
+      // land rotated by the row in LDS (k_rows_to_mfma) and the MFMA-layout
+      // reads hit distinct banks.
+#pragma unroll
+      for (int s = 0; s < S::kKSeg; ++s) {
+        const int row = S::kRowsPerLoad * s + lane / S::kRowPieces;
+        const int rr = last ? min(row, lr) : row;
+        const int piece = (lane - row) & (S::kRowPieces - 1);
+        f.k[i][s] = gload16s<STREAM>(kb + rr * tok_stride_bytes + piece * 16);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // V: rows 4j + r, piece tok.
+        const int row = last ? min(4 * j + r, lr) : 4 * j + r;
+        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
+      }
+    } else if constexpr (S::kElemBytes <= 2) {
       const uint32_t ko = last ? koff_last : koff;
 #pragma unroll
       for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16s<STREAM>(kb + s * 64 + ko);
@@ -81,6 +110,30 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
         load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + r * tok_stride_bytes + voff);
     }
   }
+}
+
+// K rows of a chunk loaded row by row (16-bit caches) into the MFMA operand
+// layout (lane l: row l % 16, piece 4 s + l / 16 at k-step s), through this
+// wave's LDS area `kt` (CB blocks of 16 x kRowPieces 16-byte pieces). Each lane
+// stores its pieces at consecutive addresses; piece p of row t sits at
+// position (p + t) mod kRowPieces of the row, so the 16 lanes reading one
+// k-step's piece of rows 0..15 use distinct banks. Only this wave touches
+// `kt`, and a wave's LDS operations complete in order, so no barrier is needed.
+template <typename T, int D, int G, int CB, bool F8>
+__device__ __forceinline__ void k_rows_to_mfma(Chunk<T, D, G, CB, F8>& f, u32x4_t* kt, int lane) {
+  using S = DecodeShape<T, D, G, CB, F8>;
+  constexpr int kBlockPieces = kBlockTokens * S::kRowPieces;
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int s = 0; s < S::kKSeg; ++s) kt[i * kBlockPieces + s * kWave + lane] = f.k[i][s];
+  const int t = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < CB; ++i)
+#pragma unroll
+    for (int s = 0; s < S::kKSeg; ++s)
+      f.k[i][s] = kt[i * kBlockPieces + t * S::kRowPieces + ((4 * s + j + t) & (S::kRowPieces - 1))];
 }
 
 // Scores of one chunk: s[i][r] = scale*log2(e) * <q, K> for token 4*(lane/16)+r

@@ -772,17 +772,19 @@ int launch_merge_parts(void* out, float* lse_out, const float* o_parts, const fl
 // workgroup per (sequence, partition, kv head), from the hardware
 // dispatcher) when its 16-column tiles hold the group; pieces on the
 // persistent split kernel, whose workgroups read whole token rows (one wave
-// per kv head), for groups above 16 and for groups of at most 4 when the
-// batch has fewer (sequence, kv head) pairs than resident tile workgroups (2
-// per CU): long contexts of a few sequences, where the pieces measured faster.
-// (Larger groups keep the tiles: the piece kernel's per-lane accumulators
-// spill registers from a group of 8 up.) PA_OPT_SPLIT_CUT forces a cut.
-bool split_by_tiles(int group, int num_seqs, int num_kv_heads) {
+// per kv head), for groups above 16 and, with float32 caches, for groups of
+// at most 4 when the batch has fewer (sequence, kv head) pairs than resident
+// tile workgroups (2 per CU): long contexts of a few sequences. With 16-bit
+// caches the tile kernel's row-wise K loads made the partitions faster there
+// too (batch of 8, contexts 16k-32k: 134.3 vs 141.4 us). (Larger groups keep
+// the tiles: the piece kernel's per-lane accumulators spill registers from a
+// group of 8 up.) PA_OPT_SPLIT_CUT forces a cut.
+bool split_by_tiles(int group, int num_seqs, int num_kv_heads, int dtype) {
   if (group > 16) return false;
   const int v = option_value(PA_OPT_SPLIT_CUT);
   if (v == 1) return true;
   if (v == 2) return false;
-  if (group > 4) return true;
+  if (group > 4 || dtype == PA_DTYPE_BF16) return true;
   return static_cast<int64_t>(num_seqs) * num_kv_heads >= 2 * static_cast<int64_t>(device_cus());
 }
 
@@ -849,10 +851,11 @@ extern "C" int pa_decode(void* out, const void* query, const void* key_cache, co
 }
 
 extern "C" int32_t pa_decode_split_part_tokens(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                               int32_t max_context_len, int32_t partition_size) {
+                                               int32_t max_context_len, int32_t partition_size, int32_t dtype) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return -1;
   if (max_context_len < 0 || partition_size <= 0 || partition_size % kBlockTokens != 0) return -1;
-  if (!split_by_tiles(num_heads / num_kv_heads, num_seqs, num_kv_heads)) return 0;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16) return -1;
+  if (!split_by_tiles(num_heads / num_kv_heads, num_seqs, num_kv_heads, dtype)) return 0;
   return split_part_tokens(num_seqs, num_kv_heads, max_context_len, partition_size);
 }
 
@@ -972,7 +975,7 @@ int decode_split_launch(void* out, const void* query, const void* key_cache, con
   args.part_tokens = partition_size;
   args.slots = static_cast<int32_t>(L.slots);
   args.scale_log2 = scale * kLog2e;
-  if (split_by_tiles(args.group, num_seqs, num_kv_heads)) {
+  if (split_by_tiles(args.group, num_seqs, num_kv_heads, dtype)) {
     // Partitions of pt = k * P tokens; positions past ceil(max_context_len / P) * P
     // are ignored, as with the pieces cut.
     const hipStream_t s = static_cast<hipStream_t>(stream);

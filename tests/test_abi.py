@@ -203,31 +203,35 @@ def test_multi_query_host_validation(lib):
 
 def test_split_cut_choice(lib):
     """pa_decode_split cuts into partitions of k * P tokens (tile kernel) when
-    its 16-column tiles hold the group and the batch has at least as many
+    its 16-column tiles hold the group: always with bf16 caches; with float32
+    caches when the group is above 4 or the batch has at least as many
     (sequence, kv head) pairs as resident tile workgroups, else into pieces;
     the overrides win where they apply. Host-only: with no device the CU count
     defaults to 256 (512 resident tile workgroups)."""
     f = lib.pa_decode_split_part_tokens
     PART_FACTOR, CUT = 3, 2
+    BF16, F32 = 1, 0
     lib.pa_set_option(PART_FACTOR, 1)
-    assert f(64, 32, 8, 2048, 512) == 512                 # 512 pairs: partitions
-    assert f(8, 32, 8, 32768, 512) == 0                   # 64 pairs, group 4: pieces
-    assert f(8, 64, 8, 32768, 512) == 512                 # 64 pairs, group 8: partitions
-    assert f(256, 64, 2, 4096, 512) == 0                  # group of 32: pieces
+    assert f(64, 32, 8, 2048, 512, F32) == 512            # 512 pairs: partitions
+    assert f(8, 32, 8, 32768, 512, F32) == 0              # 64 pairs, group 4, float32: pieces
+    assert f(8, 32, 8, 32768, 512, BF16) == 512           # ... bf16: partitions
+    assert f(8, 64, 8, 32768, 512, F32) == 512            # 64 pairs, group 8: partitions
+    assert f(256, 64, 2, 4096, 512, BF16) == 0            # group of 32: pieces
     lib.pa_set_option(PART_FACTOR, 3)
-    assert f(64, 32, 8, 32768, 512) == 1536
-    assert f(64, 32, 8, 1000, 512) == 1024                # k capped at ceil(1000 / 512)
-    assert f(64, 32, 8, 300, 512) == 512
-    for bad in [(8, 30, 8, 4096, 512), (8, 32, 0, 4096, 512), (8, 32, 8, -1, 512), (8, 32, 8, 4096, 24),
-                (-1, 32, 8, 4096, 512)]:
+    assert f(64, 32, 8, 32768, 512, BF16) == 1536
+    assert f(64, 32, 8, 1000, 512, BF16) == 1024          # k capped at ceil(1000 / 512)
+    assert f(64, 32, 8, 300, 512, BF16) == 512
+    for bad in [(8, 30, 8, 4096, 512, BF16), (8, 32, 0, 4096, 512, BF16), (8, 32, 8, -1, 512, BF16),
+                (8, 32, 8, 4096, 24, BF16), (-1, 32, 8, 4096, 512, BF16), (8, 32, 8, 4096, 512, 5)]:
         assert f(*bad) == -1
     lib.pa_set_option(PART_FACTOR, 0)
-    assert f(64, 32, 8, 2048, 512) == 512                 # 64 * 4 * 8 / 1536 rounds down to k = 1
-    assert f(256, 32, 8, 4096, 512) == 4096               # k = 10, capped at 8 partitions
+    assert f(64, 32, 8, 2048, 512, BF16) == 512           # 64 * 4 * 8 / 1536 rounds down to k = 1
+    assert f(256, 32, 8, 4096, 512, BF16) == 4096         # k = 10, capped at 8 partitions
+    assert f(8, 32, 8, 32768, 512, BF16) == 1024          # k = 8 * 64 * 8 // 1536 = 2
     lib.pa_set_option(CUT, 2)
-    assert f(64, 32, 8, 2048, 512) == 0
+    assert f(64, 32, 8, 2048, 512, BF16) == 0
     lib.pa_set_option(CUT, 1)
-    assert f(8, 32, 8, 32768, 512) == 1024 and f(256, 64, 2, 4096, 512) == 0   # k = 8 * 64 * 8 // 1536
+    assert f(8, 32, 8, 32768, 512, F32) == 1024 and f(256, 64, 2, 4096, 512, BF16) == 0
     lib.pa_set_option(CUT, 0)
 
 

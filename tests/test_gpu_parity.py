@@ -70,7 +70,8 @@ def test_workload_reshape_then_decode(pa, cfg):
 def check_split_pieces(pa, cfg, inp, kc, vc, ws, P, max_pairs=24):
     """The workspace partials of pa_decode_split against the oracle: pieces of
     the persistent split kernel, or P-token partitions of the tile kernel."""
-    pt = pa.pa_decode_split_part_tokens(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, inp.max_context_len, P)
+    pt = pa.pa_decode_split_part_tokens(cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, inp.max_context_len, P,
+                                        pa.PA_DTYPE_BF16 if cfg.dtype == "bf16" else pa.PA_DTYPE_F32)
     if pt:
         return check_split_partitions(pa, cfg, inp, kc, vc, ws, P, pt, max_pairs)
     return check_pieces_cut(pa, cfg, inp, kc, vc, ws, P, max_pairs)
