@@ -33,7 +33,8 @@
  *        key, value        [num_tokens, num_kv_heads, head_size]
  *        slot_mapping      int64 [num_tokens]
  *  - Supported shapes: block_size == 16; head_size in {64, 128};
- *    num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16.
+ *    num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16;
+ *    num_kv_heads * head_size * 4 < 2^24 (a token row under 16 MiB).
  *  - Host-side checks (shapes, enums, null or misaligned pointers, workspace
  *    size) return a non-zero pa_status before any GPU work is queued. Device
  *    CONTENTS are the caller's contract: block ids in [0, num_blocks),

@@ -188,6 +188,7 @@ extern "C" int pa_stream_kv(const void* key_cache, const void* value_cache, cons
   if (((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) & 15u) != 0)
     return PA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_kv_heads) * head_size * 4 >= (int64_t{1} << 24)) return PA_ERR_UNSUPPORTED;
   const int64_t grid = (static_cast<int64_t>(num_seqs) + 7) / 8 * 8 * num_kv_heads;
   if (grid > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
   // Waves per workgroup as the decode picks them.

@@ -881,6 +881,8 @@ int check_multi(const void* out, const void* query, const void* key_cache, const
   if (!aligned16_mq(out) || !aligned16_mq(query) || !aligned16_mq(key_cache) || !aligned16_mq(value_cache))
     return PA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_blocks_per_seq) * kBlockTokens > INT32_MAX) return PA_ERR_INVALID_ARG;
+  // A token row (all kv heads) must stay under 2^24 bytes (24-bit row offsets).
+  if (static_cast<int64_t>(num_kv_heads) * head_size * 4 >= (int64_t{1} << 24)) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 

@@ -76,19 +76,23 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
       // K: load s covers rows kRowsPerLoad * s + lane / kRowPieces; lane l
       // takes piece (l - row) mod kRowPieces of its row, so that the pieces
       // land rotated by the row in LDS (k_rows_to_mfma) and the MFMA-layout
-      // reads hit distinct banks.
+      // reads hit distinct banks. Rows past the last valid one of the
+      // context's last block read that row again (the wave-uniform limit
+      // `lim` is 15 elsewhere). Offsets stay unsigned 32-bit so that the loads
+      // take the scalar-base + lane-offset form, and row * stride is a 24-bit
+      // multiply (row <= 15; the callers keep a token row under 2^24 bytes).
+      const uint32_t lim = static_cast<uint32_t>(last ? lr : kBlockTokens - 1);
 #pragma unroll
       for (int s = 0; s < S::kKSeg; ++s) {
-        const int row = S::kRowsPerLoad * s + lane / S::kRowPieces;
-        const int rr = last ? min(row, lr) : row;
-        const int piece = (lane - row) & (S::kRowPieces - 1);
-        f.k[i][s] = gload16s<STREAM>(kb + rr * tok_stride_bytes + piece * 16);
+        const uint32_t row = static_cast<uint32_t>(S::kRowsPerLoad * s + lane / S::kRowPieces);
+        const uint32_t piece = static_cast<uint32_t>(lane - static_cast<int>(row)) & (S::kRowPieces - 1);
+        f.k[i][s] = gload16s<STREAM>(kb + (__umul24(min(row, lim), tok_stride_bytes) + piece * 16u));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // V: rows 4j + r, piece tok.
-        const int row = last ? min(4 * j + r, lr) : 4 * j + r;
-        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
+        const uint32_t row = min(static_cast<uint32_t>(4 * j + r), lim);
+        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + (__umul24(row, tok_stride_bytes) + vcol));
       }
     } else if constexpr (S::kElemBytes <= 2) {
       const uint32_t ko = last ? koff_last : koff;
