@@ -96,8 +96,9 @@ def build_sanitized(verbose: bool = False) -> str:
         return obj
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(one, SOURCES))
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan",
-           "-o", SAN_LIB + ".tmp", *objs]
+    # The runtime is not linked in: its symbols resolve at load time from the
+    # preloaded shared ASan runtime (which carries the UBSan handlers too).
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", SAN_LIB + ".tmp", *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
