@@ -180,7 +180,13 @@ def bench_multi_query(args):
     cfg = W.MQ_CONFIG_BY_NAME[name]
     base = cfg.base
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
-    mq = W.make_multi_inputs(cfg, mode="perf")
+    mq_drawn = W.make_multi_inputs(cfg, mode="perf")
+    mq = mq_drawn
+    if args.order == "longest":
+        # The batch listed longest context first (a serving engine orders its
+        # batch freely): the tile slots, and so the dispatch, follow it. The
+        # batch as drawn is timed as well (natural_order).
+        mq = W.reorder_multi_inputs(mq_drawn, np.argsort(-mq_drawn.paged.context_lens, kind="stable"))
     inp = mq.paged
     dev = torch.device("cuda:0")
 
@@ -191,26 +197,33 @@ def bench_multi_query(args):
         return torch.from_numpy(a).to(dev)
 
     pools = [(up(inp.key_cache), up(inp.value_cache)) for _ in range(2)]
-    q, bt, cl, loc = up(mq.query), up(inp.block_tables), up(inp.context_lens), up(mq.query_start_loc)
-    new_k, new_v, slots = up(mq.new_key), up(mq.new_value), up(mq.slot_mapping)
-    out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-
-    reshape_p = [pa.prepared(pa.pa_reshape_and_cache, new_k, new_v, *pools[k], slots, stream=stream)
-                 for k in range(2)]
     split = args.decode == "split"
+    max_ctx = int(inp.context_lens.max(initial=0))
+    P = None
     if split:
         # Every context cut into P-token partitions, then the per-row merge.
-        max_ctx = int(inp.context_lens.max(initial=0))
         P = (args.partition_size or pa.pa_multi_query_split_partition_size(
             base.num_seqs, mq.num_tokens, base.num_heads, base.num_kv_heads, base.head_size, max_ctx) or 1024)
         ws = torch.empty(pa.pa_multi_query_split_workspace_bytes(mq.num_tokens, base.num_heads, base.head_size,
                                                                  max_ctx, P), dtype=torch.uint8, device=dev)
-        attend_p = [pa.prepared(pa.pa_multi_query_split, out, q, *pools[k], bt, cl, loc, base.scale, max_ctx, P, ws,
-                                stream=stream) for k in range(2)]
-    else:
-        attend_p = [pa.prepared(pa.pa_multi_query, out, q, *pools[k], bt, cl, loc, base.scale, stream=stream)
-                    for k in range(2)]
+
+    def calls(m):
+        """The step's two launches on batch m, for either pool copy."""
+        q, bt, cl, loc = up(m.query), up(m.paged.block_tables), up(m.paged.context_lens), up(m.query_start_loc)
+        new_k, new_v, slots = up(m.new_key), up(m.new_value), up(m.slot_mapping)
+        out = torch.empty_like(q)
+        reshape = [pa.prepared(pa.pa_reshape_and_cache, new_k, new_v, *pools[k], slots, stream=stream)
+                   for k in range(2)]
+        if split:
+            attend = [pa.prepared(pa.pa_multi_query_split, out, q, *pools[k], bt, cl, loc, base.scale, max_ctx, P,
+                                  ws, stream=stream) for k in range(2)]
+        else:
+            attend = [pa.prepared(pa.pa_multi_query, out, q, *pools[k], bt, cl, loc, base.scale, stream=stream)
+                      for k in range(2)]
+        return reshape, attend
+
+    reshape_p, attend_p = calls(mq)
 
     print(f"[bench] warmup {args.warmup}, timed {args.steps} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -238,6 +251,20 @@ def bench_multi_query(args):
     torch.cuda.synchronize()
     att = [a.elapsed_time(b) for a, b in ev]
     att_avg = statistics.fmean(att)
+    natural_ms = None
+    if mq is not mq_drawn:
+        nat_reshape, nat_attend = calls(mq_drawn)
+        for i in range(args.warmup):
+            nat_reshape[i & 1]()
+            nat_attend[i & 1]()
+        hold_gpu(stream)
+        t_begin.record(stream)
+        for i in range(args.steps):
+            nat_reshape[i & 1]()
+            nat_attend[i & 1]()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        natural_ms = t_begin.elapsed_time(t_end) / args.steps
     kv_bytes = W.algorithmic_kv_bytes(base, inp.context_lens)
     flops = W.multi_query_flops(mq)
     t_hbm = kv_bytes / (HBM_PEAK_GBS * 1e9)
@@ -267,13 +294,18 @@ def bench_multi_query(args):
                    "head_size": base.head_size, "block_size": base.block_size, "num_blocks": base.num_blocks,
                    "mean_context": float(inp.context_lens.mean()),
                    "step": "pa_reshape_and_cache + " + ("pa_multi_query_split" if split else "pa_multi_query"),
-                   "partition_size": P if split else None, "options": forced or None},
+                   "partition_size": P if split else None, "options": forced or None,
+                   "batch_order": "longest context first" if args.order == "longest" else "as drawn"},
         "pct_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes, "attention_ms_avg": round(att_avg, 5),
         "attention_ms_median": round(statistics.median(att), 5),
         "roofline": roof,
     }
+    if natural_ms is not None:
+        nat_gbs = kv_bytes / (natural_ms * 1e-3) / 1e9
+        rec["natural_order"] = {"ms_per_step": round(natural_ms, 5), "value": round(nat_gbs, 1),
+                                "pct_hbm_peak": round(100 * nat_gbs / HBM_PEAK_GBS, 2)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline_multi(mq, args.cpu_seconds)

@@ -102,6 +102,24 @@ def test_one_token_each_matches_decode_oracle(pa):
     assert np.abs(f64(lse) - ref_lse).max() <= LSE_TOL["bf16"]
 
 
+def test_batch_order_does_not_change_rows(pa):
+    """The same step with its sequences listed in another order (the bench
+    lists them longest context first): every sequence's rows are bit-identical,
+    for both tile widths and both workgroup sizes of the 16-column tiles."""
+    mq = _case(128, 32, 8, "bf16", QLENS, NLENS, seed=37)
+    order = np.random.default_rng(6).permutation(len(QLENS))
+    r = W.reorder_multi_inputs(mq, order)
+    rows = np.concatenate([np.arange(mq.query_start_loc[i], mq.query_start_loc[i + 1]) for i in order])
+    for columns in (16, 32):
+        for waves in (4, 8):
+            pa.pa_set_option(pa.PA_OPT_TILE_COLUMNS, columns)
+            pa.pa_set_option(pa.PA_OPT_TILE_WAVES, waves)
+            a, la = _run(pa, mq)
+            b, lb = _run(pa, r)
+            np.testing.assert_array_equal(bits(a)[rows], bits(b))
+            np.testing.assert_array_equal(bits(la)[rows], bits(lb))
+
+
 def test_block_placement_does_not_change_bits(pa):
     mq = _case(128, 32, 8, "bf16", QLENS, NLENS, seed=34)
     a, la = _run(pa, mq)

@@ -134,3 +134,28 @@ def test_contiguous_placement_keeps_every_context():
         b = oracle.paged_decode(inp.query, inp.key_cache[ids], inp.value_cache[ids], tables, inp.context_lens,
                                 cfg.scale, cfg.dtype)[0]
         np.testing.assert_array_equal(a, b)
+
+
+def test_reorder_multi_inputs_moves_whole_sequences():
+    """Reordering a multi-query step moves each sequence's table, length,
+    query rows, slots and new K/V rows together: the oracle's rows of the
+    reordered step are the original rows, permuted, bit for bit."""
+    import oracle
+    base = W.small_case("reorder", 6, 8, 2, 64, "bf16", ("uniform", 1, 2), seed=3, num_blocks=64)
+    cfg = W.MultiQueryConfig("reorder", base, ("fixed", 1))
+    mq = W.make_multi_inputs(cfg, context_lens=np.array([5, 40, 17, 1, 33, 9], np.int32),
+                             query_lens=np.array([2, 1, 3, 1, 0, 4], np.int32))
+    order = np.argsort(-mq.paged.context_lens, kind="stable")
+    r = W.reorder_multi_inputs(mq, order)
+    assert list(r.paged.context_lens) == sorted(mq.paged.context_lens, reverse=True)
+    assert r.query_start_loc[0] == 0 and r.query_start_loc[-1] == mq.num_tokens
+    rows = np.concatenate([np.arange(mq.query_start_loc[i], mq.query_start_loc[i + 1]) for i in order])
+    np.testing.assert_array_equal(r.slot_mapping, mq.slot_mapping[rows])
+    np.testing.assert_array_equal(r.new_key, mq.new_key[rows])
+    p = mq.paged
+    a, la = oracle.paged_multi_query(mq.query, p.key_cache, p.value_cache, p.block_tables, p.context_lens,
+                                     mq.query_start_loc, p.cfg.scale, p.cfg.dtype)
+    b, lb = oracle.paged_multi_query(r.query, p.key_cache, p.value_cache, r.paged.block_tables,
+                                     r.paged.context_lens, r.query_start_loc, p.cfg.scale, p.cfg.dtype)
+    np.testing.assert_array_equal(a[rows], b)
+    np.testing.assert_array_equal(la[rows], lb)

@@ -388,6 +388,26 @@ def contiguous_placement(inp: PagedInputs):
     return ids, tables, slots
 
 
+def reorder_multi_inputs(mq: "MultiQueryInputs", order: np.ndarray) -> "MultiQueryInputs":
+    """The same multi-query step with its sequences listed in ``order``
+    (sequence k of the result is sequence order[k] of ``mq``): tables, lengths,
+    and each sequence's query rows, slots and new K/V rows move together; the
+    caches are unchanged."""
+    order = np.asarray(order, dtype=np.int64)
+    loc = mq.query_start_loc
+    rows = np.concatenate([np.arange(loc[i], loc[i + 1]) for i in order]).astype(np.int64) \
+        if order.size else np.zeros(0, np.int64)
+    qlens = mq.query_lens[order].astype(np.int32)
+    new_loc = np.zeros(order.size + 1, np.int32)
+    new_loc[1:] = np.cumsum(qlens)
+    p = mq.paged
+    paged = dataclasses.replace(p, context_lens=p.context_lens[order].copy(),
+                                block_tables=p.block_tables[order].copy())
+    return dataclasses.replace(mq, paged=paged, query_lens=qlens, query_start_loc=new_loc,
+                               query=mq.query[rows].copy(), slot_mapping=mq.slot_mapping[rows].copy(),
+                               new_key=mq.new_key[rows].copy(), new_value=mq.new_value[rows].copy())
+
+
 def algorithmic_kv_bytes(cfg: PagedConfig, context_lens: np.ndarray) -> int:
     """K and V bytes one decode call must read: sum_i n_i * 2 * H_kv * d_h * b."""
     return int(np.asarray(context_lens, dtype=np.int64).sum()) * 2 * cfg.num_kv_heads * cfg.head_size * cfg.kv_elem_bytes
