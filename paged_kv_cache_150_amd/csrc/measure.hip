@@ -88,6 +88,10 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void stream_kv_kernel(St
     seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
   }
   const int max_tokens = a.max_blocks * kBlockTokens;
+  // As the decode: the first chunk's table entries with the length (16-bit caches).
+  int32_t first_ids[CB] = {};
+  if constexpr (!F8) first_chunk_ids<CB>(first_ids, a.block_tables + static_cast<int64_t>(seq) * a.max_blocks,
+                                         wave * CB, a.max_blocks);
   int n = a.context_lens[seq];
   n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
   const uint32_t tok_stride = static_cast<uint32_t>(a.num_kv_heads) * D * S::kElemBytes;
@@ -112,8 +116,8 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void stream_kv_kernel(St
     return fold_chunk<T, D, CB, F8>(f);
   };
   if (mine > 0) {
-    load_chunk<T, D, 16, CB, F8, true, kRowK>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride, blk_stride,
-                                 head_off, lane, last_rows);
+    load_chunk<T, D, 16, CB, F8, true, kRowK>(fa, kc, vc, bt_row, blk_of(0), blk_last, a.num_blocks, tok_stride,
+                                              blk_stride, head_off, lane, last_rows, first_ids, !F8);
     int i = 0;
     for (; i + 2 < mine; i += 2) {
       load_chunk<T, D, 16, CB, F8, true, kRowK>(fb, kc, vc, bt_row, blk_of(i + 1), blk_last, a.num_blocks, tok_stride,

@@ -398,6 +398,10 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // keys below lim[p]; min_lim is the smallest limit of the tile's columns.
   int seq, q0, tok0, ntok, key_end, min_lim, blk_begin = 0, part = -1;
   int lim[NT];
+  // One-pass decode with 16-bit caches: the first chunk's table entries are
+  // requested with the context length (FP8 caches measured slower with it).
+  int32_t first_ids[CB] = {};
+  bool have_first = false;
   if (a.prefix_keys > 0) {
     // Shared-prefix pass: tile `slot` of the queries, all over row 0's prefix.
     seq = 0;
@@ -437,6 +441,11 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
           seq = static_cast<int>(o < static_cast<uint32_t>(a.num_seqs) ? o : a.num_seqs - 1);
         }
         blk_begin = a.skip_blocks;
+        if constexpr (!F8) {
+          first_chunk_ids<CB>(first_ids, a.block_tables + static_cast<int64_t>(seq) * a.max_blocks,
+                              blk_begin + wave * CB, a.max_blocks);
+          have_first = true;
+        }
       }
       q0 = seq;
       q1 = seq + 1;
@@ -641,7 +650,8 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     Chunk<T, D, 16, CB, F8> fa, fb;
     auto load = [&](Chunk<T, D, 16, CB, F8>& f, int i) {
       load_chunk<T, D, 16, CB, F8, kStream, kRowK>(f, kc, vc, bt_row, blk_of(i), blk_last, a.num_blocks,
-                                                   tok_stride, blk_stride, head_off, lane, last_rows);
+                                                   tok_stride, blk_stride, head_off, lane, last_rows, first_ids,
+                                                   i == 0 && have_first);
     };
     auto compute = [&](Chunk<T, D, 16, CB, F8>& f, int i, auto mask_tag) {
       if constexpr (kRowK) k_rows_to_mfma<T, D, 16, CB, F8>(f, k_stage, lane);

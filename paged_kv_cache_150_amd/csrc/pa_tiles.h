@@ -45,13 +45,15 @@ struct Chunk {
 // lanes for later rows read the last valid row again (same lines, no extra
 // memory traffic); those rows are masked out by the caller (16-bit and FP8
 // caches). STREAM: non-temporal loads (data no other workgroup reads again).
-// ROWK (16-bit caches): K loaded row by row, for k_rows_to_mfma.
+// ROWK (16-bit caches): K loaded row by row, for k_rows_to_mfma. use_ids:
+// ids[i] is the table entry of block blk0 + i, read in advance (used where the
+// block is not clamped to blk_last).
 template <typename T, int D, int G, int CB, bool F8 = false, bool STREAM = false, bool ROWK = false>
 __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
                                            const int32_t* bt_row, int blk0, int blk_last,
                                            int64_t num_blocks, uint32_t tok_stride_bytes,
                                            int64_t blk_stride_bytes, int64_t head_off_bytes,
-                                           int lane, int last_rows = kBlockTokens) {
+                                           int lane, int last_rows, const int32_t (&ids)[CB], bool use_ids) {
   using S = DecodeShape<T, D, G, CB, F8>;
   const int tok = lane & 15;
   const int j = lane >> 4;
@@ -66,7 +68,8 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
     const bool last = b == blk_last;
     // Out-of-range ids (negative included) are clamped so a bad table never
     // leads to an out-of-bounds access.
-    uint64_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bt_row[b]));
+    const int32_t id = (use_ids && blk0 + i <= blk_last) ? ids[i] : bt_row[b];
+    uint64_t phys = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(id));
     phys = phys < static_cast<uint64_t>(num_blocks) ? phys : static_cast<uint64_t>(num_blocks - 1);
     const int64_t base = static_cast<int64_t>(phys) * blk_stride_bytes + head_off_bytes;
     const gchar_t* kb = uniform_ptr(kc + base);
@@ -114,6 +117,26 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
         load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + r * tok_stride_bytes + voff);
     }
   }
+}
+
+template <typename T, int D, int G, int CB, bool F8 = false, bool STREAM = false, bool ROWK = false>
+__device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char* kc, const char* vc,
+                                           const int32_t* bt_row, int blk0, int blk_last,
+                                           int64_t num_blocks, uint32_t tok_stride_bytes,
+                                           int64_t blk_stride_bytes, int64_t head_off_bytes,
+                                           int lane, int last_rows = kBlockTokens) {
+  const int32_t none[CB] = {};
+  load_chunk<T, D, G, CB, F8, STREAM, ROWK>(f, kc, vc, bt_row, blk0, blk_last, num_blocks, tok_stride_bytes,
+                                            blk_stride_bytes, head_off_bytes, lane, last_rows, none, false);
+}
+
+// Table entries of a wave's first chunk (blocks blk0 .. blk0 + CB - 1, kept
+// inside the row), requested before the context length is known: the first
+// K/V loads then wait for one scalar round trip fewer.
+template <int CB>
+__device__ __forceinline__ void first_chunk_ids(int32_t (&ids)[CB], const int32_t* bt_row, int blk0, int max_blocks) {
+#pragma unroll
+  for (int i = 0; i < CB; ++i) ids[i] = bt_row[min(blk0 + i, max_blocks - 1)];
 }
 
 // K rows of a chunk loaded row by row (16-bit caches) into the MFMA operand
