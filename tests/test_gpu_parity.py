@@ -192,15 +192,7 @@ def test_shape_sweep(pa, dtype, d_h, Hq, Hkv):
         assert max_err(l, ref_lse) <= LSE_TOL[dtype]
 
 
-@pytest.mark.parametrize("factor", ["auto", "1", "3"])
-@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (24, 12)])
-def test_split_pieces_long_contexts(pa, decode_kernel, Hq, Hkv, factor):
-    """Long contexts cut in many pieces or partitions; for the partition cut,
-    partitions of P tokens and of k * P (the library's choice, or forced)."""
-    if factor != "auto":
-        if decode_kernel != "tiles_partitions":
-            pytest.skip("the factor applies to the partition cut only")
-        pa.pa_set_option(pa.PA_OPT_SPLIT_PART_FACTOR, int(factor))
+def _split_long_contexts(pa, Hq, Hkv):
     cfg = W.small_case("pieces", 5, Hq, Hkv, 128, "bf16", ("uniform", 900, 3000), seed=31, num_blocks=1200,
                        partition_size=64)
     inp = W.make_inputs(cfg)
@@ -212,6 +204,22 @@ def test_split_pieces_long_contexts(pa, decode_kernel, Hq, Hkv, factor):
                                            inp.context_lens, cfg.scale, cfg.dtype)
         assert max_err(out, ref) <= TOL["bf16"] and max_err(lse, ref_lse) <= LSE_TOL["bf16"]
         assert check_split_pieces(pa, cfg, inp, inp.key_cache, inp.value_cache, ws, P, max_pairs=8) >= 1
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (24, 12)])
+def test_split_pieces_long_contexts(pa, decode_kernel, Hq, Hkv):
+    """Long contexts cut in many pieces or partitions (partitions of k * P
+    tokens, k the library's choice)."""
+    _split_long_contexts(pa, Hq, Hkv)
+
+
+@pytest.mark.parametrize("factor", [1, 3])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (24, 12)])
+def test_split_partition_factor_forced(pa, Hq, Hkv, factor):
+    """The partition cut with its factor forced: partitions of P and 3 * P tokens."""
+    pa.pa_set_option(pa.PA_OPT_SPLIT_CUT, 1)
+    pa.pa_set_option(pa.PA_OPT_SPLIT_PART_FACTOR, factor)
+    _split_long_contexts(pa, Hq, Hkv)
 
 
 # --------------------------------------------------------------- closed forms, bit-exact
