@@ -245,18 +245,20 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
     // two blocks per MFMA, or 4 keys of the odd block out. FP8 V codes are
     // first converted to bf16 (exact), giving the same per-lane rows.
     constexpr int kBW = D / 32;  // bf16 dwords of a lane's piece of one row
-    uint32_t vb[CB][4][kBW];
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int w = 0; w < kBW; ++w) {
-          if constexpr (F8)
-            vb[i][r][w] = fp8x2_to_bf16x2(vz[i][r][w / 2], (w & 1) != 0);
-          else
-            vb[i][r][w] = vz[i][r][w];
-        }
+    // Element t of rows ra and rb of block i as a bf16 pair (row ra low). FP8
+    // codes are first byte-permuted into (ra, rb) pairs, then converted: one
+    // permute serves two elements.
+    auto vpair = [&](int i, int ra, int rb, auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      if constexpr (F8) {
+        const uint32_t p = __builtin_amdgcn_perm(vz[i][rb][t / 4], vz[i][ra][t / 4],
+                                                 (t % 4) < 2 ? 0x05010400u : 0x07030602u);
+        return fp8x2_to_bf16x2(p, (t & 1) != 0);
+      } else {
+        static_assert(kBW == S::kVDw, "bf16 piece");
+        return pick_bf16<t>(&vz[i][ra][0], &vz[i][rb][0]);
+      }
+    };
 #pragma unroll
     for (int i = 0; i < CB; i += 2) {
       if (i + 1 < CB) {
@@ -268,8 +270,7 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
         }
         static_for<kTiles>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          const u32x4_t av = {pick_bf16<t>(vb[i][0], vb[i][1]), pick_bf16<t>(vb[i][2], vb[i][3]),
-                              pick_bf16<t>(vb[i + 1][0], vb[i + 1][1]), pick_bf16<t>(vb[i + 1][2], vb[i + 1][3])};
+          const u32x4_t av = {vpair(i, 0, 1, tc), vpair(i, 2, 3, tc), vpair(i + 1, 0, 1, tc), vpair(i + 1, 2, 3, tc)};
 #pragma unroll
           for (int p = 0; p < NT; ++p)
             st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
@@ -284,7 +285,7 @@ __device__ __forceinline__ void mq_chunk(MqState<T, D, CB, NT>& st, const Chunk<
         }
         static_for<kTiles>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          const u32x2_t av = {pick_bf16<t>(vb[i][0], vb[i][1]), pick_bf16<t>(vb[i][2], vb[i][3])};
+          const u32x2_t av = {vpair(i, 0, 1, tc), vpair(i, 2, 3, tc)};
 #pragma unroll
           for (int p = 0; p < NT; ++p)
             st.acc[p][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, av),

@@ -101,11 +101,13 @@ __device__ __forceinline__ void load_chunk(Chunk<T, D, G, CB, F8>& f, const char
       const uint32_t ko = last ? koff_last : koff;
 #pragma unroll
       for (int s = 0; s < S::kKSeg; ++s) f.k[i][s] = gload16s<STREAM>(kb + s * 64 + ko);
+      // V: rows 4j + r, piece tok, clamped to the wave-uniform limit; unsigned
+      // 32-bit offsets with a 24-bit row multiply, as in the row-wise K loads.
+      const uint32_t lim = static_cast<uint32_t>(last ? lr : kBlockTokens - 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // V: rows 4j + r, piece tok.
-        const int row = last ? min(4 * j + r, lr) : 4 * j + r;
-        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + row * tok_stride_bytes + vcol);
+        const uint32_t row = min(static_cast<uint32_t>(4 * j + r), lim);
+        load_dwords<S::kVDw, STREAM>(f.v[i][r], vb + (__umul24(row, tok_stride_bytes) + vcol));
       }
     } else {
       // fp32 caches (the small workloads) read whole blocks: the per-row
