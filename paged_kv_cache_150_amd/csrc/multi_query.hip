@@ -410,18 +410,24 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     tok0 = slot * a.tile_tokens;
     if (tok0 >= a.num_tokens) return;
     ntok = min(a.tile_tokens, a.num_tokens - tok0);
-    key_end = 0;
-    min_lim = a.prefix_keys;
-    for (int t = 0; t < ntok; ++t) {
-      const int k = min(clamp_len(a.context_lens[tok0 + t]), a.prefix_keys);
-      key_end = max(key_end, k);
-      min_lim = min(min_lim, k);
-    }
+    // Each lane reads its columns' lengths (one round trip); the tile's key
+    // range and smallest limit are reductions over the 16 columns of a row.
+    int hi = 0, lo = a.prefix_keys;
 #pragma unroll
     for (int p = 0; p < NT; ++p) {
       const int c = 16 * p + (lane & 15);
-      lim[p] = c < ntok * g ? min(clamp_len(a.context_lens[tok0 + c / g]), a.prefix_keys) : 0;
+      const bool valid = c < ntok * g;
+      lim[p] = valid ? min(clamp_len(a.context_lens[tok0 + c / g]), a.prefix_keys) : 0;
+      hi = max(hi, lim[p]);
+      lo = valid ? min(lo, lim[p]) : lo;
     }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {
+      hi = max(hi, __shfl_xor(hi, m, kWave));
+      lo = min(lo, __shfl_xor(lo, m, kWave));
+    }
+    key_end = __builtin_amdgcn_readfirstlane(hi);
+    min_lim = __builtin_amdgcn_readfirstlane(lo);
   } else {
     int q1, r;
     if (a.query_start_loc == nullptr) {
@@ -773,39 +779,49 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   }
   __syncthreads();
 
-  // Each column's row, two elements per thread: out = (sum_w weight_w acc_w) / L
-  // times v_scale (0 for a column with no visible key).
-  for (int idx = 2 * threadIdx.x; idx < ncols * D; idx += 2 * kMqWaves * kWave) {
-    const int c = idx / D;
-    const int d = idx - c * D;
-    const int64_t row = out_row(c);
-    float o0 = 0.f, o1 = 0.f;
-    const float L = s_L[c];
+  // Each column's row: kTpc threads per column, each a contiguous run of kPer
+  // elements (vector LDS reads and stores; the column's row, weights and
+  // normaliser read once). out = (sum_w weight_w acc_w) / L times v_scale (0
+  // for a column with no visible key).
+  constexpr int kTpc = kMqWaves * kWave / kCols;
+  constexpr int kPer = D / kTpc;
+  static_assert(kPer >= 2 && kPer % 2 == 0 && kPer * kTpc == D, "epilogue split");
+  const int oc = threadIdx.x / kTpc;
+  if (oc < ncols) {
+    const int d0 = (threadIdx.x % kTpc) * kPer;
+    const int64_t row = out_row(oc);
+    float o[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) o[e] = 0.f;
+    const float L = s_L[oc];
     if (L != 0.f) {
 #pragma unroll
       for (int v = 0; v < kMqWaves; ++v) {
-        const float wv = s_w[v][c];
-        o0 = fmaf(wv, s_acc[v][c][d], o0);
-        o1 = fmaf(wv, s_acc[v][c][d + 1], o1);
+        const float wv = s_w[v][oc];
+        const float* src = &s_acc[v][oc][d0];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) o[e] = fmaf(wv, src[e], o[e]);
       }
       if (a.prefix_o != nullptr) {
-        const float wp = s_w[kMqWaves][c];
+        const float wp = s_w[kMqWaves][oc];
         if (wp != 0.f) {
-          o0 = fmaf(wp, a.prefix_o[row * D + d], o0);
-          o1 = fmaf(wp, a.prefix_o[row * D + d + 1], o1);
+          const float* src = a.prefix_o + row * D + d0;
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) o[e] = fmaf(wp, src[e], o[e]);
         }
       }
-      o0 = o0 / L * a.v_scale;
-      o1 = o1 / L * a.v_scale;
+      // Divided, not multiplied by 1/L: a one-key context returns its V row
+      // exactly.
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) o[e] = o[e] / L * a.v_scale;
     }
     if (a.part_o != nullptr) {
       const int64_t orow = part >= 0 ? row * a.parts_stride + part : row;
-      a.part_o[orow * D + d] = o0;
-      a.part_o[orow * D + d + 1] = o1;
-      if (d == 0) a.part_lse[orow] = s_lse[c];
+      store_run<float, kPer>(a.part_o + orow * D + d0, o);
+      if (d0 == 0) a.part_lse[orow] = s_lse[oc];
     } else {
-      store_pair<T>(static_cast<T*>(a.out) + row * D + d, o0, o1);
-      if (a.lse_out != nullptr && d == 0) a.lse_out[row] = s_lse[c];
+      store_run<T, kPer>(static_cast<T*>(a.out) + row * D + d0, o);
+      if (a.lse_out != nullptr && d0 == 0) a.lse_out[row] = s_lse[oc];
     }
   }
 }

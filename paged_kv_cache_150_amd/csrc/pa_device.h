@@ -200,6 +200,34 @@ __device__ __forceinline__ void store_pair<bf16_t>(bf16_t* p, float x, float y) 
   *reinterpret_cast<uint32_t*>(p) = static_cast<uint32_t>(f32_to_bf16(x)) | (static_cast<uint32_t>(f32_to_bf16(y)) << 16);
 }
 
+// N consecutive elements from floats (bf16: rounded to nearest even), as
+// 16-byte stores where the run allows (p aligned to the run's size, up to 16
+// bytes).
+template <typename T, int N>
+__device__ __forceinline__ void store_run(T* p, const float (&x)[N]) {
+  constexpr int kWords = N * static_cast<int>(sizeof(T)) / 4;
+  uint32_t w[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) {
+    if constexpr (sizeof(T) == 4)
+      w[i] = __builtin_bit_cast(uint32_t, x[i]);
+    else
+      w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+  }
+  uint32_t* q = reinterpret_cast<uint32_t*>(p);
+  if constexpr (kWords % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < kWords; i += 4)
+      *reinterpret_cast<u32x4_t*>(q + i) = u32x4_t{w[i], w[i + 1], w[i + 2], w[i + 3]};
+  } else if constexpr (kWords % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < kWords; i += 2) *reinterpret_cast<u32x2_t*>(q + i) = u32x2_t{w[i], w[i + 1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) q[i] = w[i];
+  }
+}
+
 // Load `NDW` dwords (4, 8, 16 or 32 bytes) that are 16-byte (or 8- or
 // 4-byte) aligned; STREAM as for gload16s.
 template <int NDW, bool STREAM = false>
