@@ -621,6 +621,33 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
     }
   };
 
+  // Output row of column c; the epilogue's split of a tile's outputs over the
+  // threads (kTpc threads per column, kPer consecutive elements each).
+  auto out_row = [&](int c) {
+    const int tok = c / g;
+    return (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
+  };
+  constexpr int kTpc = kMqWaves * kWave / kCols;
+  constexpr int kPer = D / kTpc;
+  static_assert(kPer >= 2 && kPer % 2 == 0 && kPer * kTpc == D, "epilogue split");
+  // Suffix pass of the shared-prefix decode (16-column tiles of 16-bit
+  // caches): the prefix part of this thread's outputs, and of its column's
+  // weight, is read now, so that the epilogue does not wait for it.
+  constexpr bool kPrefetchPrefix = NT == 1 && sizeof(T) == 2;
+  float pre_o[kPrefetchPrefix ? kPer : 1];
+  float pre_lse = -__builtin_inff();
+  if constexpr (kPrefetchPrefix) {
+    if (a.prefix_o != nullptr) {
+      if (static_cast<int>(threadIdx.x) < ncols) pre_lse = a.prefix_lse[out_row(threadIdx.x)];
+      const int c = threadIdx.x / kTpc;
+      if (c < ncols) {
+        const float* src = a.prefix_o + out_row(c) * D + (threadIdx.x % kTpc) * kPer;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) pre_o[e] = src[e];
+      }
+    }
+  }
+
   u32x4_t q[NT][S::kQSeg];
   load_query_cols<T, D, CB, NT, F8>(a.query, q0 + tok0, a.num_heads, kvh * g, g, ncols, lane, q);
 
@@ -752,16 +779,12 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // Merge weights per column, once: wave w's part weighs 2^(m_w - M), and
   // the normaliser is L = sum_w 2^(m_w - M) l_w. A prefix-pass result joins
   // as one more part: l = 1, acc = its output, m = its log-sum-exp in base 2.
-  auto out_row = [&](int c) {
-    const int tok = c / g;
-    return (static_cast<int64_t>(q0) + tok0 + tok) * a.num_heads + kvh * g + (c - tok * g);
-  };
   for (int c = threadIdx.x; c < ncols; c += kMqWaves * kWave) {
-    const int64_t row = out_row(c);
     float M = -__builtin_inff();
 #pragma unroll
     for (int v = 0; v < kMqWaves; ++v) M = fmaxf(M, s_m[v][c]);
-    const float pm = a.prefix_o != nullptr ? a.prefix_lse[row] * kLog2e : -__builtin_inff();
+    float pm = -__builtin_inff();
+    if (a.prefix_o != nullptr) pm = (kPrefetchPrefix ? pre_lse : a.prefix_lse[out_row(c)]) * kLog2e;
     M = fmaxf(M, pm);
     float L = 0.f;
     float w[kMqWaves + 1];
@@ -783,9 +806,6 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
   // elements (vector LDS reads and stores; the column's row, weights and
   // normaliser read once). out = (sum_w weight_w acc_w) / L times v_scale (0
   // for a column with no visible key).
-  constexpr int kTpc = kMqWaves * kWave / kCols;
-  constexpr int kPer = D / kTpc;
-  static_assert(kPer >= 2 && kPer % 2 == 0 && kPer * kTpc == D, "epilogue split");
   const int oc = threadIdx.x / kTpc;
   if (oc < ncols) {
     const int d0 = (threadIdx.x % kTpc) * kPer;
@@ -807,7 +827,7 @@ __global__ __launch_bounds__(W * kWave, W == 4 ? 2 : 1) void paged_multi_query_k
         if (wp != 0.f) {
           const float* src = a.prefix_o + row * D + d0;
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) o[e] = fmaf(wp, src[e], o[e]);
+          for (int e = 0; e < kPer; ++e) o[e] = fmaf(wp, kPrefetchPrefix ? pre_o[e] : src[e], o[e]);
         }
       }
       // Divided, not multiplied by 1/L: a one-key context returns its V row
