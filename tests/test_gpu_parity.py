@@ -353,6 +353,30 @@ def test_seq_order_is_only_a_schedule(pa):
         np.testing.assert_array_equal(bits(la), bits(l))
 
 
+def test_seq_order_entries_out_of_range_are_clamped(pa):
+    """seq_order entries outside [0, num_seqs) are clamped to the last
+    sequence (the header's contract): the listed sequences get their
+    natural-order bits, the last one is written twice with the same bits, and
+    the sequence no entry names keeps the caller's sentinel."""
+    cfg = W.small_case("order_clamp", 24, 32, 8, 128, "bf16", ("uniform", 1, 300), seed=47, num_blocks=600)
+    d = Dev(W.make_inputs(cfg))
+    S = cfg.num_seqs
+    want, want_lse = d.decode(pa, lse=True)
+    order = np.arange(S, dtype=np.int32)
+    order[S - 2], order[0], order[5] = -7, S + 5, 0  # sequence 5 is named by no entry
+    order[S - 1] = 2**31 - 1
+    out = torch.full_like(d.q, float("nan"))
+    lse = torch.full(d.q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    pa.pa_decode(out, d.q, d.kc, d.vc, d.bt, d.cl, cfg.scale, lse_out=lse, seq_order=to_dev(order))
+    torch.cuda.synchronize()
+    named = np.ones(S, bool)
+    named[[5, S - 2]] = False  # S - 2 is listed only through clamped entries, which name S - 1
+    np.testing.assert_array_equal(bits(out)[named], bits(want)[named])
+    np.testing.assert_array_equal(bits(lse)[named], bits(want_lse)[named])
+    for i in (5, S - 2):
+        assert np.isnan(f64(out)[i]).all() and np.isnan(f64(lse)[i]).all()
+
+
 def test_many_jobs_per_workgroup(pa):
     """Far more (sequence, kv head) jobs than resident workgroups: many rounds
     of tile workgroups, short and empty jobs included, and the schedule
