@@ -103,6 +103,57 @@ def test_decode_split_graph(pa, cut):
     _replay_against_eager(q, _queries(q.shape, q.dtype, REPLAYS, 2), graph, [out, lse], eager)
 
 
+def test_decode_prefix_graph(pa):
+    """The shared-prefix decode (its two launches and the workspace between
+    them) under capture, against eager calls on fresh workspaces."""
+    cfg = W.small_case("graph_prefix", 40, 64, 8, 128, "bf16", ("prefix", 96, 1, 300), seed=64, num_blocks=900)
+    inp = W.make_inputs(cfg)
+    kc, vc = to_dev(inp.key_cache), to_dev(inp.value_cache)
+    bt, cl = to_dev(inp.block_tables), to_dev(inp.context_lens)
+    q = to_dev(inp.query)
+    P = inp.shared_prefix_blocks
+    ws = torch.empty(pa.pa_decode_prefix_workspace_bytes(cfg.num_seqs, cfg.num_heads, cfg.head_size),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    graph = _capture(lambda: pa.pa_decode_prefix(out, q, kc, vc, bt, cl, cfg.scale, P, ws, lse_out=lse))
+
+    def eager(qr):
+        oe, le = torch.empty_like(q), torch.empty_like(lse)
+        pa.pa_decode_prefix(oe, qr, kc, vc, bt, cl, cfg.scale, P, torch.empty_like(ws), lse_out=le)
+        torch.cuda.synchronize()
+        return oe, le
+
+    _replay_against_eager(q, _queries(q.shape, q.dtype, REPLAYS, 4), graph, [out, lse], eager)
+
+
+def test_reshape_and_decode_fp8_graph(pa):
+    """The one-launch FP8 step (quantizing write and decode) under capture:
+    every replay writes the same codes and gives the eager bits."""
+    cfg = W.small_case("graph_fp8", 48, 32, 8, 128, "bf16", ("uniform", 1, 700), seed=65, num_blocks=2400,
+                       kv_dtype="fp8", k_scale=1 / 64, v_scale=1 / 32)
+    inp = W.make_inputs(cfg)
+    kc0, vc0 = W.caches_before_write(inp)
+    kc, vc = to_dev(kc0), to_dev(vc0)
+    nk, nv, sm = to_dev(inp.new_key), to_dev(inp.new_value), to_dev(inp.slot_mapping)
+    bt, cl = to_dev(inp.block_tables), to_dev(inp.context_lens)
+    q = to_dev(inp.query)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    graph = _capture(lambda: pa.pa_reshape_and_decode_fp8(out, q, nk, nv, sm, kc, vc, bt, cl, cfg.scale,
+                                                          cfg.k_scale, cfg.v_scale, lse_out=lse))
+
+    def eager(qr):
+        kce, vce = to_dev(kc0), to_dev(vc0)
+        oe, le = torch.empty_like(q), torch.empty_like(lse)
+        pa.pa_reshape_and_decode_fp8(oe, qr, nk, nv, sm, kce, vce, bt, cl, cfg.scale, cfg.k_scale, cfg.v_scale,
+                                     lse_out=le)
+        torch.cuda.synchronize()
+        return oe, le, kce, vce
+
+    _replay_against_eager(q, _queries(q.shape, q.dtype, REPLAYS, 5), graph, [out, lse, kc, vc], eager)
+
+
 @pytest.mark.parametrize("split", [False, True])
 def test_multi_query_graph(pa, split):
     base = W.small_case("graph_mq", 10, 32, 8, 128, "bf16", ("uniform", 1, 2), seed=63, num_blocks=400)
