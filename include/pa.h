@@ -204,7 +204,11 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapp
  *                     NULL (natural order) result. Entries outside
  *                     [0, num_seqs) are clamped.
  *   n = 0             gives out = 0 and lse = -inf.
- *   Table entries at index >= ceil(n / block_size) are never read.
+ *   Table entries at index >= ceil(n / block_size) never affect the result
+ *                     and no cache block they name is read, but the first 16
+ *                     entries of a row may be read before n is known (the
+ *                     row holds max_blocks_per_seq entries, so this stays
+ *                     inside the table).
  * Returns PA_OK or an error status.
  */
 int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
