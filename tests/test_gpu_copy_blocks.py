@@ -29,7 +29,7 @@ def _pairs(rng, nb, n, junk=0):
     return pairs
 
 
-@pytest.mark.parametrize("dtype,Hkv,d", [("bf16", 8, 128), ("f32", 2, 64), ("bf16", 1, 64)])
+@pytest.mark.parametrize("dtype,Hkv,d", [("bf16", 8, 128), ("f32", 2, 64), ("bf16", 1, 64), ("bf16", 16, 128), ("f32", 8, 128)])
 def test_copy_blocks_bit_exact(pa, dtype, Hkv, d):
     rng = np.random.default_rng(11)
     nb = 300
